@@ -1,0 +1,67 @@
+"""The hybrid layer: SWA, DSWA and gated-delta-rule branches combined by
+per-head sigmoid gates.
+
+Source: Kairos paper (arXiv 2606.16533, HTML v3), Sec. 2.2 and Fig. 5 (the
+three temporal pathways: SWA for local, DSWA for mid-range, GLA implemented
+as GatedDeltaNet for global memory), Sec. 2.2.1 (Eq. 1-6), Sec. 2.2.2 (Eq.
+7-8) and "Long-Horizon Generation" (recurrent state passing).
+
+Readings:
+
+* The paper stacks the pathways as separate blocks; the layer here runs them
+  as parallel branches on one shared q, k, v and mixes them per head:
+  ``y = sigmoid(z_swa) o_swa + sigmoid(z_dswa) o_dswa + sigmoid(z_gdn) o_gdn``
+  with z of shape [3, H] and no normalisation of the gates.
+* With FP8 windows the SWA/DSWA branches use the dequantised q_hat, k_hat
+  (per-64-token-block absmax e4m3); the GDN branch uses the unquantised q, k.
+* A streamed rollout (frames fed call by call, state carried) is defined to
+  equal one call over the whole sequence; the oracle is that single call.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .gdn import gdn_recurrent
+from .window import windowed_attention_rows
+from .fp8 import fp8_quantize_blocks
+
+
+def sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _window_inputs(q, k, window_qk):
+    if window_qk == "fp8":
+        _, _, qh = fp8_quantize_blocks(q)
+        _, _, kh = fp8_quantize_blocks(k)
+        return qh, kh
+    return q, k
+
+
+def hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, rows, frame_offset=0,
+              state_in=None, window_qk="bf16", o_gdn=None):
+    """Layer output for the query tokens ``rows`` (all heads) and final state.
+
+    The GDN branch needs every token before the last requested row; it is
+    computed over the full sequence (or taken from ``o_gdn`` when given).
+    Returns ``(y_rows [B, n, H, d], S_T or None)``.
+    """
+    S = None
+    if o_gdn is None:
+        o_gdn, S = gdn_recurrent(q, k, v, alpha, beta, state_in)
+    qw, kw = _window_inputs(q, k, window_qk)
+    o_swa = windowed_attention_rows(qw, kw, v, rows, L, w, 1, frame_offset)
+    o_dswa = windowed_attention_rows(qw, kw, v, rows, L, w, dil, frame_offset)
+    g = sigmoid(gates)                                        # [3, H]
+    y = g[0][None, None, :, None] * o_swa + g[1][None, None, :, None] * o_dswa \
+        + g[2][None, None, :, None] * np.asarray(o_gdn, np.float64)[:, rows]
+    return y, S
+
+
+def hlta(q, k, v, alpha, beta, gates, L, w, dil, frame_offset=0, state_in=None,
+         window_qk="bf16"):
+    """Layer output for every token ``[B, T, H, d]`` and the final GDN state."""
+    T = np.asarray(q).shape[1]
+    return hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, np.arange(T), frame_offset,
+                     state_in, window_qk)

@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs shaped like the video-token workloads of the hybrid
+linear temporal attention layer.
+
+This module holds input generation only: random draws, the L2 normalisation
+of keys that the inputs are specified to arrive with, bf16 rounding, and the
+named workload shapes.  It contains none of the method's arithmetic and is
+shared by the oracle side (tests, CPU baseline) and the GPU side (tests,
+bench) alike.
+
+Recipe (per workload index i): NumPy PCG64 seeded with ``1000 + i``; a
+SeedSequence is spawned into six child streams used in the fixed order
+q, k, v, alpha-source, beta-source, gates.  Draws are fp32 in C order
+``[B, T, H, d]``; k is L2-normalised per (token, head) in fp64 and then
+rounded; bf16 workloads round q, k, v to bf16 (round to nearest even).
+alpha and beta stay fp32, shape ``[B, T, H]``; gate logits are fp32 ``[3, H]``
+in the order (swa, dswa, gdn).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "workload", "make_inputs", "make_custom",
+    "to_bf16_bits", "bf16_bits_to_f32", "round_bf16",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and distribution recipe of one synthetic workload."""
+    name: str
+    B: int
+    T: int
+    H: int
+    d: int
+    io: str                      # "f32" or "bf16"
+    alpha_kind: str              # "uniform" (U(0.9,0.999)) or "softplus" (exp(-softplus(N(-4,1))))
+    beta_kind: str               # "uniform" (U(0.05,1)) or "sigmoid" (sigmoid(N(0,1)))
+    L: int = 0                   # tokens per frame (0: no frames, GDN only)
+    window: int = 0
+    dilation: int = 1
+    window_qk: str = "bf16"      # "bf16" or "fp8"
+    stream_frames: int = 0       # >0: rolled out one frame per call with a KV ring
+    ring_frames: int = 0
+    seed: int = 1000
+
+    @property
+    def frames(self) -> int:
+        return self.T // self.L if self.L else 0
+
+
+# The five workloads, sizes as named by the task's configurations.
+WORKLOADS = [
+    Workload("gdn_f32_B1H2T64d32", 1, 64, 2, 32, "f32", "uniform", "uniform", seed=1000),
+    Workload("gdn_bf16_B2H16T4096d128", 2, 4096, 16, 128, "bf16", "softplus", "sigmoid", seed=1001),
+    Workload("hlta_bf16_B1H24F21L1560", 1, 21 * 1560, 24, 128, "bf16", "softplus", "sigmoid",
+             L=1560, window=1560, dilation=4, seed=1002),
+    Workload("hlta_stream_B1H24F61L1560", 1, 61 * 1560, 24, 128, "bf16", "softplus", "sigmoid",
+             L=1560, window=1560, dilation=4, stream_frames=61, ring_frames=4, seed=1003),
+    Workload("hlta_fp8_B4H24F16L3600", 4, 16 * 3600, 24, 128, "bf16", "softplus", "sigmoid",
+             L=3600, window=3600, dilation=4, window_qk="fp8", seed=1004),
+]
+
+
+def workload(i: int) -> Workload:
+    return WORKLOADS[i]
+
+
+# --------------------------------------------------------------------------- bf16
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even.  Inputs are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(to_bf16_bits(x))
+
+
+# --------------------------------------------------------------------------- draws
+
+def _l2_normalise_rows(k: np.ndarray, block: int = 1 << 20) -> np.ndarray:
+    """Normalise the last axis to unit L2 norm in fp64, in slices to bound memory."""
+    flat = k.reshape(-1, k.shape[-1])
+    out = np.empty_like(flat)
+    for s in range(0, flat.shape[0], block):
+        x = flat[s:s + block].astype(np.float64)
+        n = np.sqrt(np.sum(x * x, axis=1, keepdims=True))
+        out[s:s + block] = (x / n).astype(np.float32)
+    return out.reshape(k.shape)
+
+
+def _draw(rngs, B, T, H, d, alpha_kind, beta_kind):
+    rq, rk, rv, ra, rb, rg = rngs
+    q = rq.standard_normal((B, T, H, d), dtype=np.float32)
+    k = _l2_normalise_rows(rk.standard_normal((B, T, H, d), dtype=np.float32))
+    v = rv.standard_normal((B, T, H, d), dtype=np.float32)
+    if alpha_kind == "uniform":
+        alpha = ra.uniform(0.9, 0.999, size=(B, T, H)).astype(np.float32)
+    elif alpha_kind == "softplus":
+        x = ra.standard_normal((B, T, H), dtype=np.float32).astype(np.float64) - 4.0
+        alpha = (1.0 / (1.0 + np.exp(x))).astype(np.float32)      # exp(-softplus(x))
+    else:
+        raise ValueError(alpha_kind)
+    if beta_kind == "uniform":
+        beta = rb.uniform(0.05, 1.0, size=(B, T, H)).astype(np.float32)
+    elif beta_kind == "sigmoid":
+        x = rb.standard_normal((B, T, H), dtype=np.float32).astype(np.float64)
+        beta = (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+    else:
+        raise ValueError(beta_kind)
+    gates = rg.standard_normal((3, H), dtype=np.float32)
+    return q, k, v, alpha, beta, gates
+
+
+def make_custom(B: int, T: int, H: int, d: int, io: str = "bf16", seed: int = 0,
+                alpha_kind: str = "softplus", beta_kind: str = "sigmoid") -> dict:
+    """Inputs of arbitrary shape with a workload's distributions.
+
+    Returns a dict of fp32 arrays (q, k, v hold exactly representable bf16
+    values when ``io == "bf16"``) plus ``q_bits``/``k_bits``/``v_bits`` uint16
+    bf16 patterns for bf16 io.
+    """
+    rngs = [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(6)]
+    q, k, v, alpha, beta, gates = _draw(rngs, B, T, H, d, alpha_kind, beta_kind)
+    out = dict(alpha=alpha, beta=beta, gates=gates)
+    if io == "bf16":
+        for name, x in (("q", q), ("k", k), ("v", v)):
+            bits = to_bf16_bits(x)
+            out[name + "_bits"] = bits
+            out[name] = bf16_bits_to_f32(bits)
+    elif io == "f32":
+        out.update(q=q, k=k, v=v)
+    else:
+        raise ValueError(io)
+    return out
+
+
+def make_inputs(w: Workload | int, T: Optional[int] = None) -> dict:
+    """Inputs of a named workload (optionally truncated to the first T tokens,
+    which keeps every draw of the full workload's prefix only when T equals
+    the full length; truncated draws are a different, smaller sample)."""
+    if isinstance(w, int):
+        w = WORKLOADS[w]
+    return make_custom(w.B, T if T is not None else w.T, w.H, w.d, w.io, w.seed,
+                       w.alpha_kind, w.beta_kind)
