@@ -1,0 +1,167 @@
+/*
+ * kairos.h -- C ABI of the MI355X (gfx950) hybrid linear temporal attention
+ * forward: the gated delta rule global memory, causal sliding-window and
+ * dilated sliding-window softmax attention, per-head sigmoid branch gates,
+ * a streaming state carry with a key/value ring, and FP8 E4M3 windowed Q/K.
+ *
+ * Source of the operations: "Kairos: A Regret-Aware Native World-Action
+ * Model Stack for Physical AI" (arXiv 2606.16533, HTML v3):
+ *   Sec. 2.2.1, Eq. 1-6 and step 4    gated delta rule, read-out o_t = S_t q_t
+ *   Sec. 2.2.2, Eq. 7                 sliding-window attention, w = L x window_size
+ *   Sec. 2.2.2, Eq. 8                 dilated SWA on the frame-rearranged sequence
+ *   Sec. 2.2.2, "Long-Horizon Generation"  recurrent state passing, constant memory per step
+ * and the project page "Kairos: A Native World Model Stack for Physical AI"
+ * (TL;DR, Q3: FP8 attention quantisation, tiled GatedDeltaNet).
+ *
+ * Conventions shared by every entry point
+ * --------------------------------------
+ * Layouts (C order, no padding):
+ *   q, k, v, out       [B][T][H][d]      (bf16, or fp32 for the fp32 GDN path)
+ *   alpha, beta        [B][T][H]         fp32, the gate values themselves
+ *   state_in/out       [B][H][dv][dk]    fp32 (the memory S in R^{dv x dk})
+ *   gate_logits        [3][H]            fp32, rows (swa, dswa, gdn); sigmoid applied inside
+ *   k_ring, v_ring     [B][R][L][H][d]   bf16, slot s holds absolute frame f with f mod R == s
+ *   fp8 codes          [B][T][H][d]      uint8 OCP E4M3; scales [B][H][ceil(T/64)] fp32
+ * The gated delta rule is the canonical form
+ *   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t,
+ * keys arrive L2-normalised (nothing renormalises them).  Windows are causal:
+ * query i sees keys i-w < j <= i (SWA); DSWA groups frames by absolute frame
+ * index mod dilation and applies the same window to positions inside a group.
+ * The softmax scale is 1/sqrt(d).
+ *
+ * Ownership and streams: the caller owns every buffer (device memory unless
+ * stated).  Entry points allocate nothing: scratch space comes from the
+ * caller's workspace, sized by the *_workspace_size calls.  Work is enqueued
+ * on `stream` (a hipStream_t; NULL is the null stream) and the call returns
+ * without synchronising; nothing is copied between host and device.  The
+ * current HIP device is used.  Calls keep no global state, so they are
+ * reentrant; calls that share output buffers on one stream are ordered by it.
+ *
+ * Errors: all arguments are validated on the host before anything is
+ * enqueued.  An invalid call returns a negative kairos_status and has no side
+ * effects.  A failed launch returns KAIROS_ERR_HIP; faults inside kernels
+ * surface at the caller's next synchronisation.
+ */
+#ifndef KAIROS_H
+#define KAIROS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KAIROS_OK = 0,
+  KAIROS_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  KAIROS_ERR_SHAPE = -2,       /* a size is out of range or inconsistent          */
+  KAIROS_ERR_DTYPE = -3,       /* unsupported element type                        */
+  KAIROS_ERR_ALIGN = -4,       /* a buffer is not 16-byte aligned                 */
+  KAIROS_ERR_ALIAS = -5,       /* an output overlaps an input it may not overlap  */
+  KAIROS_ERR_UNSUPPORTED = -6, /* valid in principle, not implemented             */
+  KAIROS_ERR_WORKSPACE = -7,   /* workspace missing or too small                  */
+  KAIROS_ERR_HIP = -8          /* a HIP launch or query failed                    */
+} kairos_status;
+
+typedef enum { KAIROS_F32 = 0, KAIROS_BF16 = 1, KAIROS_FP8_E4M3 = 2 } kairos_dtype;
+
+/* Gated delta rule problem.  dk == dv == d with d in {32, 64, 128};
+ * chunk must be 64 (the chunkwise evaluation's block length; any chunk size
+ * gives the same result up to rounding).  io: KAIROS_F32 (q, k, v, out fp32,
+ * token-by-token fp32 evaluation) or KAIROS_BF16 (q, k, v, out bf16, chunkwise
+ * evaluation on bf16 matrix cores, fp32 state; d in {64, 128}).
+ * B >= 1, H >= 1, T >= 0 (T == 0 copies state_in to state_out). */
+typedef struct {
+  int32_t B, T, H, dk, dv;
+  int32_t chunk;
+  int32_t io;                  /* kairos_dtype */
+} kairos_gdn_desc;
+
+/* Hybrid layer problem.  g describes q, k, v, alpha, beta, state (io must be
+ * KAIROS_BF16, d == 128).  The sequence is T tokens of frames of L tokens
+ * (the last frame may be partial when ring_frames == 0).  window w >= 1 in
+ * tokens; dilation >= 1.  frame_offset is the absolute index of the call's
+ * first frame.  window_qk: KAIROS_BF16, or KAIROS_FP8_E4M3 to quantise the
+ * windowed branches' q and k per 64-token block (not with a ring).
+ * ring_frames R: 0 for a self-contained call (no keys before token 0);
+ * otherwise the call continues a rollout: frames frame_offset-R ..
+ * frame_offset-1 (those >= 0) are read from the ring, T must be a multiple of
+ * L, and R must be >= kairos_hlta_ring_frames_required(). */
+typedef struct {
+  kairos_gdn_desc g;
+  int32_t L;
+  int32_t window;
+  int32_t dilation;
+  int32_t window_qk;           /* kairos_dtype */
+  int64_t frame_offset;
+  int32_t ring_frames;
+  int32_t reserved;            /* must be 0 */
+} kairos_hlta_desc;
+
+/* Human-readable name of a status code (static storage). */
+const char* kairos_status_string(int status);
+
+/* ABI version: 100 * major + minor. */
+int kairos_version(void);
+
+/* Workspace bytes needed by kairos_gdn_fwd / kairos_hlta_fwd for this problem
+ * (written to *bytes; 0 is a valid answer).  Validates the descriptor only. */
+int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes);
+int kairos_hlta_workspace_size(const kairos_hlta_desc* desc, size_t* bytes);
+
+/* Ring frames a streamed call needs: dilation * ceil((window - 1) / L)
+ * (frames whose keys a query can still see), written to *frames. */
+int kairos_hlta_ring_frames_required(const kairos_hlta_desc* desc, int32_t* frames);
+
+/* Gated delta rule forward (Sec. 2.2.1, Eq. 1-6 canonical form, step 4).
+ *   q, k, v      [B][T][H][d]  io type; k L2-normalised per (token, head)
+ *   alpha, beta  [B][T][H]     fp32, alpha in (0, 1], beta in [0, 1]
+ *   state_in     [B][H][d][d]  fp32 initial memory; NULL means zero
+ *   out          [B][T][H][d]  io type, o_t = S_t q_t; must not overlap inputs
+ *   state_out    [B][H][d][d]  fp32 final memory; NULL discards it; may equal
+ *                state_in (in-place carry) but may not partially overlap it
+ *   workspace    >= kairos_gdn_workspace_size bytes (may be NULL when 0) */
+int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* state_in,
+                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* One windowed softmax branch on its own (Sec. 2.2.2): SWA when dilation == 1,
+ * DSWA otherwise (Eq. 8 as a frame-residue index map; nothing is rearranged
+ * in memory).  Uses desc->L, window, frame_offset, ring_frames, window_qk and
+ * g.{B,T,H,dk}; `dilation` overrides desc->dilation.  With window_qk ==
+ * KAIROS_FP8_E4M3, q and k are the E4M3 codes and q_scales / k_scales the
+ * per-64-token-block scales written by kairos_fp8_quantize; otherwise q, k are
+ * bf16 and the scale pointers must be NULL.  out [B][T][H][d] bf16.  The ring
+ * is read, never written. */
+int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void* q, const void* k,
+                      const void* v, const float* q_scales, const float* k_scales,
+                      const void* k_ring, const void* v_ring, void* out, void* stream);
+
+/* Hybrid layer forward: y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn
+ * per head (Sec. 2.2, Fig. 5 pathways, run as parallel gated branches).
+ *   gate_logits  [3][H] fp32 (device memory)
+ *   k_ring, v_ring  [B][R][L][H][d] bf16, required iff ring_frames > 0; read
+ *                for the frames before the call, then updated in stream order
+ *                with the call's last min(R, F) frames
+ *   out          [B][T][H][d] bf16; state_out as in kairos_gdn_fwd
+ *   workspace    >= kairos_hlta_workspace_size bytes */
+int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, const float* gate_logits,
+                    const float* state_in, void* k_ring, void* v_ring, void* out,
+                    float* state_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block):
+ * s = amax / 448 (fp32; 1 when amax == 0), code = E4M3(x / s) with an IEEE
+ * fp32 division, round to nearest even, saturating at 448 (OCP E4M3: bias 7,
+ * subnormals, no infinities).  codes [B][T][H][d] uint8, scales
+ * [B][H][ceil(T/64)] fp32.  d in {32, 64, 128}. */
+int kairos_fp8_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
+                        int32_t H, int32_t d, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KAIROS_H */

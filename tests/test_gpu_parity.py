@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds that still span
+several tiles, chunks and ragged tails.
+
+Tolerances (relative to the reference tensor's magnitude, see conftest):
+fp32 path rel_max <= 1e-4; bf16 / fp8 paths rel_max <= 2e-2 and
+rel_mean <= 5e-3, on outputs and on the final state.  FP8 results are
+compared with the oracle that applies the same quantisation; quantiser codes
+and scales are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import video_world_model_chunkwise_amd as K
+from tests.conftest import rel_errors
+from tests.gpu_util import dev_bf16, dev_f32, host, inputs_to_dev
+from workloads import make_custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_MAX, TOL_MEAN = 2e-2, 5e-3
+
+
+def _assert_close(got, ref, what, tmax=TOL_MAX, tmean=TOL_MEAN):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    rmax, rmean = rel_errors(got, ref)
+    print(f"{what}: rel_max={rmax:.3e} rel_mean={rmean:.3e}", flush=True)
+    assert rmax <= tmax and rmean <= tmean, f"{what}: rel_max {rmax:.3e} rel_mean {rmean:.3e}"
+
+
+# ------------------------------------------------------------------ gated delta rule
+
+def test_gdn_f32_workload0():
+    inp = make_inputs(0)
+    d = inputs_to_dev(inp, "f32")
+    out, S = K.kairos_gdn_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
+    _assert_close(host(out), o_ref, "o", 1e-4, 1e-4)
+    _assert_close(host(S), S_ref, "S", 1e-4, 1e-4)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_gdn_f32_with_state(d):
+    inp = make_custom(2, 77, 3, d, "f32", seed=11, alpha_kind="uniform", beta_kind="uniform")
+    S0 = np.random.default_rng(3).standard_normal((2, 3, d, d)).astype(np.float32)
+    dv = inputs_to_dev(inp, "f32")
+    out, S = K.kairos_gdn_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dev_f32(S0))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0)
+    _assert_close(host(out), o_ref, "o", 1e-4, 1e-4)
+    _assert_close(host(S), S_ref, "S", 1e-4, 1e-4)
+
+
+@pytest.mark.parametrize("B,T,H,d", [(1, 200, 2, 128), (2, 130, 3, 64), (1, 64, 1, 128),
+                                     (1, 1, 2, 128), (1, 65, 16, 128), (3, 300, 8, 128)])
+def test_gdn_bf16_chunked(B, T, H, d):
+    inp = make_custom(B, T, H, d, "bf16", seed=100 + T + H)
+    S0 = (np.random.default_rng(T).standard_normal((B, H, d, d)) * 0.5).astype(np.float32)
+    dv = inputs_to_dev(inp)
+    out, S = K.kairos_gdn_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dev_f32(S0))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0)
+    _assert_close(host(out), o_ref, f"o B{B} T{T} H{H} d{d}")
+    _assert_close(host(S), S_ref, f"S B{B} T{T} H{H} d{d}")
+
+
+def test_gdn_bf16_zero_length_copies_state():
+    S0 = np.random.default_rng(5).standard_normal((1, 2, 128, 128)).astype(np.float32)
+    e = torch.empty((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.empty((1, 0, 2), dtype=torch.float32, device="cuda:0")
+    out, S = K.kairos_gdn_fwd(e, e, e, g, g, dev_f32(S0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(S), S0)
+
+
+def test_gdn_bf16_retrieval_pin():
+    """alpha = beta = 1 with orthonormal keys and q = k: o_t = v_t (bf16 path)."""
+    rng = np.random.default_rng(9)
+    d, T = 128, 128
+    Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    kk = Qm.T.astype(np.float32)[None, :, None, :]
+    from workloads import to_bf16_bits, bf16_bits_to_f32
+    kb = to_bf16_bits(kk)
+    vb = to_bf16_bits(rng.standard_normal((1, T, 1, d)).astype(np.float32))
+    ones = dev_f32(np.ones((1, T, 1), np.float32))
+    out, S = K.kairos_gdn_fwd(dev_bf16(kb), dev_bf16(kb), dev_bf16(vb), ones, ones)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.gdn_recurrent(bf16_bits_to_f32(kb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
+                                    np.ones((1, T, 1)), np.ones((1, T, 1)))
+    _assert_close(host(out), o_ref, "retrieval o")
+
+
+# ------------------------------------------------------------------ fp8 quantiser
+
+@pytest.mark.parametrize("T", [1, 64, 150, 1000])
+def test_fp8_quantize_bit_exact(T):
+    inp = make_custom(2, T, 3, 128, "bf16", seed=T)
+    x = inp["q"] * np.float32(7.0)
+    from workloads import to_bf16_bits, bf16_bits_to_f32
+    xb = to_bf16_bits(x)
+    xb[0, :min(T, 64), 1] = 0                       # an all-zero block
+    codes, scales = K.kairos_fp8_quantize(dev_bf16(xb))
+    torch.cuda.synchronize()
+    c_ref, s_ref, _ = oracle.fp8_quantize_blocks(bf16_bits_to_f32(xb))
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
+# ------------------------------------------------------------------ windowed branches
+
+WIN_CASES = [
+    # B, F, L, H, w, dil, frame_offset  (T = F*L, last frame full)
+    (1, 7, 100, 2, 150, 3, 0),
+    (1, 5, 200, 2, 200, 2, 1),
+    (2, 6, 64, 1, 64, 4, 0),
+    (1, 9, 130, 1, 300, 4, 3),
+    (1, 3, 300, 1, 1000, 1, 0),
+]
+
+
+@pytest.mark.parametrize("B,F,L,H,w,dil,fo", WIN_CASES)
+def test_window_single_branch(B, F, L, H, w, dil, fo):
+    T = F * L
+    inp = make_custom(B, T, H, 128, "bf16", seed=F * L + w)
+    dv = inputs_to_dev(inp)
+    for dl in (1, dil):
+        out = K.kairos_window_fwd(dv["q"], dv["k"], dv["v"], L, w, dl, frame_offset=fo)
+        torch.cuda.synchronize()
+        ref = oracle.windowed_attention(inp["q"], inp["k"], inp["v"], L, w, dl, fo)
+        _assert_close(host(out), ref, f"window dil={dl}")
+
+
+def test_window_partial_last_frame():
+    B, H, L, w, dil = 1, 2, 100, 120, 2
+    T = 4 * L + 37
+    inp = make_custom(B, T, H, 128, "bf16", seed=77)
+    dv = inputs_to_dev(inp)
+    for dl in (1, dil):
+        out = K.kairos_window_fwd(dv["q"], dv["k"], dv["v"], L, w, dl)
+        torch.cuda.synchronize()
+        _assert_close(host(out), oracle.windowed_attention(inp["q"], inp["k"], inp["v"], L, w, dl),
+                      f"partial frame dil={dl}")
+
+
+@pytest.mark.parametrize("B,F,L,H,w,dil,fo", WIN_CASES[:3])
+def test_hlta_small(B, F, L, H, w, dil, fo):
+    T = F * L
+    inp = make_custom(B, T, H, 128, "bf16", seed=7 + F * L)
+    dv = inputs_to_dev(inp)
+    y, S = K.kairos_hlta_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dv["gates"],
+                             L, w, dil, frame_offset=fo)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, frame_offset=fo)
+    _assert_close(host(y), y_ref, "y")
+    _assert_close(host(S), S_ref, "S")
+
+
+def test_hlta_fp8_small():
+    B, F, L, H, w, dil = 2, 6, 150, 2, 200, 4
+    T = F * L
+    inp = make_custom(B, T, H, 128, "bf16", seed=321)
+    dv = inputs_to_dev(inp)
+    y, S = K.kairos_hlta_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dv["gates"],
+                             L, w, dil, window_qk=K.FP8_E4M3)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, window_qk="fp8")
+    _assert_close(host(y), y_ref, "y fp8")
+    _assert_close(host(S), S_ref, "S fp8")
+
+
+def test_streaming_equals_full_run():
+    """Recurrent state passing: frames fed one call at a time with the GDN state
+    carried and a key/value ring equal one full-length oracle run."""
+    B, F, L, H, w, dil = 1, 9, 96, 2, 150, 2
+    T = F * L
+    inp = make_custom(B, T, H, 128, "bf16", seed=55)
+    dv = inputs_to_dev(inp)
+    R = K.kairos_hlta_ring_frames_required(K.hlta_desc(B, L, H, 128, L, w, dil))
+    k_ring = torch.zeros((B, R, L, H, 128), dtype=torch.bfloat16, device="cuda:0")
+    v_ring = torch.zeros_like(k_ring)
+    state = torch.zeros((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
+    ys = []
+    for f in range(F):
+        sl = slice(f * L, (f + 1) * L)
+        y, _ = K.kairos_hlta_fwd(dv["q"][:, sl].contiguous(), dv["k"][:, sl].contiguous(),
+                                 dv["v"][:, sl].contiguous(), dv["alpha"][:, sl].contiguous(),
+                                 dv["beta"][:, sl].contiguous(), dv["gates"], L, w, dil,
+                                 frame_offset=f, state_in=state, state_out=state, ring_frames=R,
+                                 k_ring=k_ring, v_ring=v_ring)
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil)
+    _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
+    _assert_close(host(state), S_ref, "stream S")

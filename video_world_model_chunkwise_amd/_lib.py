@@ -1,0 +1,262 @@
+"""ctypes binding of libkairos.so (the C ABI of include/kairos.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libkairos.so")
+
+# every symbol include/kairos.h declares
+symbols = (
+    "kairos_status_string", "kairos_version", "kairos_gdn_workspace_size",
+    "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
+    "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize",
+)
+
+
+class KairosError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("T", c_int32), ("H", c_int32), ("dk", c_int32), ("dv", c_int32),
+                ("chunk", c_int32), ("io", c_int32)]
+
+
+class HltaDesc(ctypes.Structure):
+    _fields_ = [("g", GdnDesc), ("L", c_int32), ("window", c_int32), ("dilation", c_int32),
+                ("window_qk", c_int32), ("frame_offset", c_int64), ("ring_frames", c_int32),
+                ("reserved", c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is missing: build it with "
+                              "`python -m video_world_model_chunkwise_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        L.kairos_status_string.restype = c_char_p
+        L.kairos_status_string.argtypes = [c_int]
+        L.kairos_version.restype = c_int
+        L.kairos_version.argtypes = []
+        L.kairos_gdn_workspace_size.argtypes = [POINTER(GdnDesc), POINTER(c_size_t)]
+        L.kairos_hlta_workspace_size.argtypes = [POINTER(HltaDesc), POINTER(c_size_t)]
+        L.kairos_hlta_ring_frames_required.argtypes = [POINTER(HltaDesc), POINTER(c_int32)]
+        L.kairos_gdn_fwd.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]
+        L.kairos_window_fwd.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 9
+        L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p]
+        L.kairos_fp8_quantize.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                          c_int32, c_void_p]
+        for name in symbols:
+            getattr(L, name).restype = c_int if name != "kairos_status_string" else c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kairos_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return lib().kairos_version()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KairosError(status, where)
+
+
+def gdn_desc(B, T, H, d, io=BF16, chunk=64) -> GdnDesc:
+    return GdnDesc(B, T, H, d, d, chunk, io)
+
+
+def hlta_desc(B, T, H, d, L, window, dilation, frame_offset=0, ring_frames=0,
+              window_qk=BF16, io=BF16) -> HltaDesc:
+    return HltaDesc(gdn_desc(B, T, H, d, io), L, window, dilation, window_qk, frame_offset,
+                    ring_frames, 0)
+
+
+# ------------------------------------------------------------------ torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return c_void_p(stream)
+    return c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def kairos_gdn_workspace_size(desc: GdnDesc) -> int:
+    n = c_size_t(0)
+    _check(lib().kairos_gdn_workspace_size(byref(desc), byref(n)), "kairos_gdn_workspace_size")
+    return n.value
+
+
+def kairos_hlta_workspace_size(desc: HltaDesc) -> int:
+    n = c_size_t(0)
+    _check(lib().kairos_hlta_workspace_size(byref(desc), byref(n)), "kairos_hlta_workspace_size")
+    return n.value
+
+
+def kairos_hlta_ring_frames_required(desc: HltaDesc) -> int:
+    n = c_int32(0)
+    _check(lib().kairos_hlta_ring_frames_required(byref(desc), byref(n)),
+           "kairos_hlta_ring_frames_required")
+    return n.value
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def kairos_gdn_fwd(q, k, v, alpha, beta, state_in=None, out=None, state_out=None,
+                   keep_state=True, stream=None, workspace=None):
+    """Gated delta rule forward.  q, k, v: [B, T, H, d] (bf16 or fp32, same
+    dtype); alpha, beta: [B, T, H] fp32; state_in: [B, H, d, d] fp32 or None.
+    Returns (out, state_out); state_out is None when keep_state is False."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    dev = q.device
+    io = F32 if q.dtype == torch.float32 else BF16
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, (B, T, H, d), dev)
+    _need(alpha, "alpha", torch.float32, (B, T, H), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (B, H, d, d), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, (B, T, H, d), dev)
+    if state_out is None and keep_state:
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (B, H, d, d), dev)
+    desc = gdn_desc(B, T, H, d, io)
+    nws = kairos_gdn_workspace_size(desc)
+    ws = workspace if workspace is not None else _workspace(nws, dev)
+    st = lib().kairos_gdn_fwd(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                              _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ws), nws,
+                              _stream(stream))
+    _check(st, "kairos_gdn_fwd")
+    return out, state_out
+
+
+def kairos_fp8_quantize(x, codes=None, scales=None, stream=None):
+    """Per-(b, h, 64-token block) E4M3 quantisation of x [B, T, H, d] bf16.
+    Returns (codes uint8 [B, T, H, d], scales fp32 [B, H, ceil(T/64)])."""
+    torch = _torch()
+    B, T, H, d = x.shape
+    _need(x, "x", torch.bfloat16, (B, T, H, d), x.device)
+    if codes is None:
+        codes = torch.empty((B, T, H, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, (T + 63) // 64), dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8, (B, T, H, d), x.device)
+    _need(scales, "scales", torch.float32, (B, H, (T + 63) // 64), x.device)
+    st = lib().kairos_fp8_quantize(_ptr(x), _ptr(codes), _ptr(scales), B, T, H, d, _stream(stream))
+    _check(st, "kairos_fp8_quantize")
+    return codes, scales
+
+
+def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=0,
+                      k_ring=None, v_ring=None, q_scales=None, k_scales=None, out=None,
+                      stream=None):
+    """One windowed branch (SWA if dilation == 1, else DSWA).  q, k bf16, or
+    uint8 E4M3 codes with q_scales/k_scales; v bf16 [B, T, H, 128]."""
+    torch = _torch()
+    B, T, H, d = v.shape
+    dev = v.device
+    fp8 = q.dtype == torch.uint8
+    qk_dtype = torch.uint8 if fp8 else torch.bfloat16
+    _need(q, "q", qk_dtype, (B, T, H, d), dev)
+    _need(k, "k", qk_dtype, (B, T, H, d), dev)
+    _need(v, "v", torch.bfloat16, (B, T, H, d), dev)
+    if fp8:
+        nb = (T + 63) // 64
+        _need(q_scales, "q_scales", torch.float32, (B, H, nb), dev)
+        _need(k_scales, "k_scales", torch.float32, (B, H, nb), dev)
+    if ring_frames:
+        _need(k_ring, "k_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+        _need(v_ring, "v_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
+    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames,
+                     FP8_E4M3 if fp8 else BF16)
+    st = lib().kairos_window_fwd(byref(desc), dilation, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scales),
+                                 _ptr(k_scales), _ptr(k_ring), _ptr(v_ring), _ptr(out),
+                                 _stream(stream))
+    _check(st, "kairos_window_fwd")
+    return out
+
+
+def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, frame_offset=0,
+                    state_in=None, ring_frames=0, k_ring=None, v_ring=None, window_qk=BF16,
+                    out=None, state_out=None, keep_state=True, workspace=None, stream=None):
+    """Hybrid layer forward.  q, k, v: [B, T, H, 128] bf16; alpha, beta
+    [B, T, H] fp32; gate_logits [3, H] fp32.  Returns (out, state_out)."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, (B, T, H, d), dev)
+    _need(alpha, "alpha", torch.float32, (B, T, H), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    _need(gate_logits, "gate_logits", torch.float32, (3, H), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (B, H, d, d), dev)
+    if ring_frames:
+        _need(k_ring, "k_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+        _need(v_ring, "v_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
+    if state_out is None and keep_state:
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, window_qk)
+    nws = kairos_hlta_workspace_size(desc)
+    ws = workspace if workspace is not None else _workspace(nws, dev)
+    if ws is not None and ws.numel() < nws:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nws}")
+    st = lib().kairos_hlta_fwd(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(gate_logits), _ptr(state_in), _ptr(k_ring), _ptr(v_ring),
+                               _ptr(out), _ptr(state_out), _ptr(ws), nws, _stream(stream))
+    _check(st, "kairos_hlta_fwd")
+    return out, state_out

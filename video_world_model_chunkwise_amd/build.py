@@ -1,0 +1,69 @@
+"""Build the gfx950 shared library ``libkairos.so`` in-tree with hipcc.
+
+Usage: ``python -m video_world_model_chunkwise_amd.build`` (always rebuilds).
+Sources: ``csrc/*.hip`` (kernels and the C ABI of ``include/kairos.h``).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkairos.so")
+ARCH = "gfx950"
+
+SOURCES = ["gdn.hip", "window_attn.hip", "fp8_ring.hip", "kairos_abi.hip"]
+
+CFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # no packed-fp32 instructions anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + INCLUDE, "-I" + CSRC,
+]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    with tempfile.TemporaryDirectory(prefix="kairos_build_") as tmp:
+        objs = []
+        jobs = []
+        with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+            for src in SOURCES:
+                obj = os.path.join(tmp, src.replace(".hip", ".o"))
+                objs.append(obj)
+                cmd = [hipcc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+                jobs.append(ex.submit(_run, cmd))
+            for j in jobs:
+                out = j.result()
+                if verbose and out.strip():
+                    print(out)
+        tmp_lib = LIB + ".tmp"
+        _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib])
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

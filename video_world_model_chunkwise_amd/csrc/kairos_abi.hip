@@ -1,0 +1,318 @@
+// Host side of the C ABI declared in include/kairos.h: argument validation
+// (complete before anything is enqueued), workspace layout, and the launch
+// sequence of each entry point on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kairos.h"
+#include "common.hpp"
+
+#include "launch.hpp"
+
+using namespace kairos;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // bound on any tensor's element count
+constexpr size_t kWsAlign = 256;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+int check_gdn_desc(const kairos_gdn_desc* d) {
+  if (!d) return KAIROS_ERR_NULL;
+  if (d->B < 1 || d->H < 1 || d->T < 0) return KAIROS_ERR_SHAPE;
+  if (d->dk != d->dv) return KAIROS_ERR_SHAPE;
+  if (d->dk != 32 && d->dk != 64 && d->dk != 128) return KAIROS_ERR_SHAPE;
+  if (d->chunk != 64) return KAIROS_ERR_SHAPE;
+  if (d->io != KAIROS_F32 && d->io != KAIROS_BF16) return KAIROS_ERR_DTYPE;
+  if (d->io == KAIROS_BF16 && d->dk == 32) return KAIROS_ERR_UNSUPPORTED;
+  const int64_t n = (int64_t)d->B * d->T * d->H * d->dk;
+  if (n > kMaxElems) return KAIROS_ERR_SHAPE;
+  return KAIROS_OK;
+}
+
+int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
+  if (!d) return KAIROS_ERR_NULL;
+  int st = check_gdn_desc(&d->g);
+  if (st != KAIROS_OK) return st;
+  if (d->g.io != KAIROS_BF16) return KAIROS_ERR_DTYPE;
+  if (d->g.dk != 128) return KAIROS_ERR_UNSUPPORTED;
+  if (d->L < 1 || d->window < 1 || d->dilation < 1 || d->frame_offset < 0 || d->ring_frames < 0 ||
+      d->reserved != 0)
+    return KAIROS_ERR_SHAPE;
+  if (d->window_qk != KAIROS_BF16 && d->window_qk != KAIROS_FP8_E4M3) return KAIROS_ERR_DTYPE;
+  if (d->window_qk == KAIROS_FP8_E4M3 && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
+  // group positions (frame / dil) * L + L and token indices must fit in int32
+  const int64_t frames = (d->g.T + d->L - 1) / d->L;
+  if ((d->frame_offset + frames + 1) * (int64_t)d->L >= ((int64_t)1 << 30)) return KAIROS_ERR_SHAPE;
+  if ((int64_t)d->window >= ((int64_t)1 << 30)) return KAIROS_ERR_SHAPE;
+  if (d->ring_frames > 0) {
+    if (d->g.T % d->L != 0) return KAIROS_ERR_SHAPE;
+    const int64_t need = (int64_t)d->dilation * ((d->window - 1 + d->L - 1) / d->L);
+    if (d->ring_frames < need) return KAIROS_ERR_SHAPE;
+  }
+  (void)layer;
+  return KAIROS_OK;
+}
+
+struct HltaWs {
+  size_t o_gdn, q8, k8, qs, ks, total;
+};
+
+HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
+  HltaWs w{};
+  const size_t n = (size_t)d->g.B * d->g.T * d->g.H * d->g.dk;
+  const size_t nblk = (size_t)(d->g.T + 63) / 64;
+  size_t off = 0;
+  w.o_gdn = off;
+  off += align_up(n * 2);
+  if (d->window_qk == KAIROS_FP8_E4M3) {
+    w.q8 = off;
+    off += align_up(n);
+    w.k8 = off;
+    off += align_up(n);
+    w.qs = off;
+    off += align_up((size_t)d->g.B * d->g.H * nblk * 4);
+    w.ks = off;
+    off += align_up((size_t)d->g.B * d->g.H * nblk * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+int check_gdn_ptrs(const kairos_gdn_desc* d, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* state_in, const void* out,
+                   const float* state_out) {
+  if (d->T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return KAIROS_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state_in) ||
+      !aligned16(state_out))
+    return KAIROS_ERR_ALIGN;
+  if (((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u)) return KAIROS_ERR_ALIGN;
+  const size_t esz = d->io == KAIROS_F32 ? 4 : 2;
+  const size_t nx = (size_t)d->B * d->T * d->H * d->dk * esz;
+  const size_t ng = (size_t)d->B * d->T * d->H * 4;
+  const size_t ns = (size_t)d->B * d->H * d->dk * d->dv * 4;
+  if (overlaps(out, nx, q, nx) || overlaps(out, nx, k, nx) || overlaps(out, nx, v, nx) ||
+      overlaps(out, nx, alpha, ng) || overlaps(out, nx, beta, ng) || overlaps(out, nx, state_in, ns) ||
+      overlaps(out, nx, state_out, ns))
+    return KAIROS_ERR_ALIAS;
+  if (state_out && state_out != state_in &&
+      (overlaps(state_out, ns, state_in, ns) || overlaps(state_out, ns, q, nx) ||
+       overlaps(state_out, ns, k, nx) || overlaps(state_out, ns, v, nx) ||
+       overlaps(state_out, ns, alpha, ng) || overlaps(state_out, ns, beta, ng)))
+    return KAIROS_ERR_ALIAS;
+  return KAIROS_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KAIROS_OK : KAIROS_ERR_HIP; }
+
+void fill_win_args(WinArgs& a, const kairos_hlta_desc* d) {
+  memset(&a, 0, sizeof(a));
+  a.B = d->g.B;
+  a.T = d->g.T;
+  a.H = d->g.H;
+  a.L = d->L;
+  a.F = (d->g.T + d->L - 1) / d->L;
+  a.w = d->window;
+  a.dil = d->dilation;
+  a.R = d->ring_frames;
+  a.nblk = (d->g.T + 63) / 64;
+  a.frame_offset = (long)d->frame_offset;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kairos_status_string(int status) {
+  switch (status) {
+    case KAIROS_OK: return "ok";
+    case KAIROS_ERR_NULL: return "null pointer";
+    case KAIROS_ERR_SHAPE: return "invalid shape";
+    case KAIROS_ERR_DTYPE: return "unsupported dtype";
+    case KAIROS_ERR_ALIGN: return "misaligned buffer";
+    case KAIROS_ERR_ALIAS: return "overlapping buffers";
+    case KAIROS_ERR_UNSUPPORTED: return "unsupported combination";
+    case KAIROS_ERR_WORKSPACE: return "workspace missing or too small";
+    case KAIROS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int kairos_version(void) { return 100; }
+
+int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
+  if (!bytes) return KAIROS_ERR_NULL;
+  const int st = check_gdn_desc(desc);
+  if (st != KAIROS_OK) return st;
+  *bytes = 0;
+  return KAIROS_OK;
+}
+
+int kairos_hlta_workspace_size(const kairos_hlta_desc* desc, size_t* bytes) {
+  if (!bytes) return KAIROS_ERR_NULL;
+  const int st = check_hlta_desc(desc, true);
+  if (st != KAIROS_OK) return st;
+  *bytes = hlta_ws_layout(desc).total;
+  return KAIROS_OK;
+}
+
+int kairos_hlta_ring_frames_required(const kairos_hlta_desc* desc, int32_t* frames) {
+  if (!desc || !frames) return KAIROS_ERR_NULL;
+  if (desc->L < 1 || desc->window < 1 || desc->dilation < 1) return KAIROS_ERR_SHAPE;
+  *frames = (int32_t)((int64_t)desc->dilation * ((desc->window - 1 + desc->L - 1) / desc->L));
+  return KAIROS_OK;
+}
+
+int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* state_in, void* out,
+                   float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gdn_desc(desc);
+  if (st != KAIROS_OK) return st;
+  st = check_gdn_ptrs(desc, q, k, v, alpha, beta, state_in, out, state_out);
+  if (st != KAIROS_OK) return st;
+  (void)workspace;
+  (void)workspace_bytes;
+  hipStream_t s = (hipStream_t)stream;
+  if (desc->io == KAIROS_F32)
+    return hip_status(launch_gdn_f32((const float*)q, (const float*)k, (const float*)v, alpha, beta,
+                                     state_in, (float*)out, state_out, desc->B, desc->T, desc->H,
+                                     desc->dk, s));
+  return hip_status(launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                     alpha, beta, state_in, (uint16_t*)out, state_out, desc->B,
+                                     desc->T, desc->H, desc->dk, 0, s));
+}
+
+int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void* q, const void* k,
+                      const void* v, const float* q_scales, const float* k_scales,
+                      const void* k_ring, const void* v_ring, void* out, void* stream) {
+  int st = check_hlta_desc(desc, false);
+  if (st != KAIROS_OK) return st;
+  if (dilation < 1) return KAIROS_ERR_SHAPE;
+  if (desc->ring_frames > 0) {
+    const int64_t need = (int64_t)dilation * ((desc->window - 1 + desc->L - 1) / desc->L);
+    if (desc->ring_frames < need) return KAIROS_ERR_SHAPE;
+  }
+  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  if (desc->g.T == 0) return KAIROS_OK;
+  if (!q || !k || !v || !out) return KAIROS_ERR_NULL;
+  if (fp8 && (!q_scales || !k_scales)) return KAIROS_ERR_NULL;
+  if (!fp8 && (q_scales || k_scales)) return KAIROS_ERR_UNSUPPORTED;
+  if (desc->ring_frames > 0 && (!k_ring || !v_ring)) return KAIROS_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(k_ring) ||
+      !aligned16(v_ring))
+    return KAIROS_ERR_ALIGN;
+  const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
+  const size_t nqk = fp8 ? n : 2 * n;
+  const size_t nring = (size_t)desc->g.B * desc->ring_frames * desc->L * desc->g.H * desc->g.dk * 2;
+  if (overlaps(out, 2 * n, q, nqk) || overlaps(out, 2 * n, k, nqk) || overlaps(out, 2 * n, v, 2 * n) ||
+      overlaps(out, 2 * n, k_ring, nring) || overlaps(out, 2 * n, v_ring, nring))
+    return KAIROS_ERR_ALIAS;
+  WinArgs a;
+  fill_win_args(a, desc);
+  a.dil = dilation;
+  a.q = q;
+  a.k = k;
+  a.v = (const uint16_t*)v;
+  a.q_scales = q_scales;
+  a.k_scales = k_scales;
+  a.k_ring = (const uint16_t*)k_ring;
+  a.v_ring = (const uint16_t*)v_ring;
+  a.out = (uint16_t*)out;
+  return hip_status(launch_window(a, fp8, false, (hipStream_t)stream));
+}
+
+int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, const float* gate_logits,
+                    const float* state_in, void* k_ring, void* v_ring, void* out, float* state_out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_hlta_desc(desc, true);
+  if (st != KAIROS_OK) return st;
+  st = check_gdn_ptrs(&desc->g, q, k, v, alpha, beta, state_in, out, state_out);
+  if (st != KAIROS_OK) return st;
+  if (!gate_logits) return KAIROS_ERR_NULL;
+  if (desc->ring_frames > 0 && (!k_ring || !v_ring)) return KAIROS_ERR_NULL;
+  if (!aligned16(k_ring) || !aligned16(v_ring)) return KAIROS_ERR_ALIGN;
+  const HltaWs ws = hlta_ws_layout(desc);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return KAIROS_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return KAIROS_ERR_ALIGN;
+  const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
+  const size_t nring = (size_t)desc->g.B * desc->ring_frames * desc->L * desc->g.H * desc->g.dk * 2;
+  if (overlaps(k_ring, nring, v_ring, nring) || overlaps(k_ring, nring, out, 2 * n) ||
+      overlaps(v_ring, nring, out, 2 * n) || overlaps(k_ring, nring, k, 2 * n) ||
+      overlaps(v_ring, nring, v, 2 * n) || overlaps(workspace, ws.total, out, 2 * n) ||
+      overlaps(workspace, ws.total, q, 2 * n) || overlaps(workspace, ws.total, k, 2 * n) ||
+      overlaps(workspace, ws.total, v, 2 * n))
+    return KAIROS_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  const int B = desc->g.B, T = desc->g.T, H = desc->g.H, D = desc->g.dk;
+  uint8_t* wsb = (uint8_t*)workspace;
+  uint16_t* o_gdn = (uint16_t*)(wsb + ws.o_gdn);
+  hipError_t e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha,
+                                  beta, state_in, o_gdn, state_out, B, T, H, D, 0, s);
+  if (e != hipSuccess) return KAIROS_ERR_HIP;
+  if (T == 0) return KAIROS_OK;
+  WinArgs a;
+  fill_win_args(a, desc);
+  a.v = (const uint16_t*)v;
+  a.k_ring = (const uint16_t*)k_ring;
+  a.v_ring = (const uint16_t*)v_ring;
+  a.o_gdn = o_gdn;
+  a.gates = gate_logits;
+  a.out = (uint16_t*)out;
+  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  if (fp8) {
+    uint8_t* q8 = wsb + ws.q8;
+    uint8_t* k8 = wsb + ws.k8;
+    float* qs = (float*)(wsb + ws.qs);
+    float* ks = (float*)(wsb + ws.ks);
+    e = launch_fp8_quant((const uint16_t*)q, q8, qs, B, T, H, D, s);
+    if (e != hipSuccess) return KAIROS_ERR_HIP;
+    e = launch_fp8_quant((const uint16_t*)k, k8, ks, B, T, H, D, s);
+    if (e != hipSuccess) return KAIROS_ERR_HIP;
+    a.q = q8;
+    a.k = k8;
+    a.q_scales = qs;
+    a.k_scales = ks;
+  } else {
+    a.q = q;
+    a.k = k;
+  }
+  e = launch_window(a, fp8, true, s);
+  if (e != hipSuccess) return KAIROS_ERR_HIP;
+  if (desc->ring_frames > 0) {
+    e = launch_ring_update((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)k_ring,
+                           (uint16_t*)v_ring, B, T / desc->L, desc->L, H, D,
+                           (long)desc->frame_offset, desc->ring_frames, s);
+    if (e != hipSuccess) return KAIROS_ERR_HIP;
+  }
+  return KAIROS_OK;
+}
+
+int kairos_fp8_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
+                        int32_t H, int32_t d, void* stream) {
+  if (B < 1 || H < 1 || T < 0) return KAIROS_ERR_SHAPE;
+  if (d != 32 && d != 64 && d != 128) return KAIROS_ERR_SHAPE;
+  if ((int64_t)B * T * H * d > kMaxElems) return KAIROS_ERR_SHAPE;
+  if (T == 0) return KAIROS_OK;
+  if (!x_bf16 || !codes || !scales) return KAIROS_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(codes) || ((uintptr_t)scales & 3u)) return KAIROS_ERR_ALIGN;
+  const size_t n = (size_t)B * T * H * d;
+  const size_t ns = (size_t)B * H * ((T + 63) / 64) * 4;
+  if (overlaps(codes, n, x_bf16, 2 * n) || overlaps(scales, ns, x_bf16, 2 * n) ||
+      overlaps(scales, ns, codes, n))
+    return KAIROS_ERR_ALIAS;
+  return hip_status(launch_fp8_quant((const uint16_t*)x_bf16, codes, scales, B, T, H, d,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Host-callable launchers of the gfx950 kernels (one per kernel family).
+// Every launcher only enqueues work on `stream` and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kairos {
+
+// Arguments of the windowed-attention kernel (SWA / DSWA / hybrid epilogue).
+struct WinArgs {
+  const void* q;            // bf16 [B][T][H][128] or E4M3 codes
+  const void* k;            // same type as q
+  const uint16_t* v;        // bf16 [B][T][H][128]
+  const float* q_scales;    // [B][H][nblk] (FP8 only)
+  const float* k_scales;
+  const uint16_t* k_ring;   // [B][R][L][H][128] bf16 or null
+  const uint16_t* v_ring;
+  const uint16_t* o_gdn;    // bf16 [B][T][H][128] (hybrid only)
+  const float* gates;       // logits [3][H] (hybrid only)
+  uint16_t* out;            // bf16 [B][T][H][128]
+  int B, T, H, L, F, QT;    // F frames in the call (last may be partial), QT query tiles per frame
+  int w, dil, R, nblk;
+  long frame_offset;
+};
+
+hipError_t launch_gdn_f32(const float* q, const float* k, const float* v, const float* alpha,
+                          const float* beta, const float* state_in, float* out, float* state_out,
+                          int B, int T, int H, int D, hipStream_t stream);
+// nw: waves per workgroup (rows of S per workgroup = 16 nw); <= 0 picks by problem size
+hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const float* alpha, const float* beta, const float* state_in,
+                            uint16_t* out, float* state_out, int B, int T, int H, int D, int nw,
+                            hipStream_t stream);
+int gdn_chunk_waves(int B, int H, int D);
+hipError_t launch_fp8_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
+                            int D, hipStream_t stream);
+hipError_t launch_ring_update(const uint16_t* k, const uint16_t* v, uint16_t* k_ring,
+                              uint16_t* v_ring, int B, int F, int L, int H, int D, long frame_offset,
+                              int R, hipStream_t stream);
+hipError_t launch_window(const WinArgs& args, bool fp8, bool hybrid, hipStream_t stream);
+
+}  // namespace kairos
