@@ -121,7 +121,9 @@ int kairos_hlta_ring_frames_required(const kairos_hlta_desc* desc, int32_t* fram
  *   out          [B][T][H][d]  io type, o_t = S_t q_t; must not overlap inputs
  *   state_out    [B][H][d][d]  fp32 final memory; NULL discards it; may equal
  *                state_in (in-place carry) but may not partially overlap it
- *   workspace    >= kairos_gdn_workspace_size bytes (may be NULL when 0) */
+ *   workspace    >= kairos_gdn_workspace_size bytes, 256-byte aligned (may be
+ *                NULL when 0): the bf16 path keeps each chunk's T = (I + A)^{-1}
+ *                and decays there (B*H*ceil(T/64)*(64*64*2 + 64*4) bytes) */
 int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, const float* state_in,
                    void* out, float* state_out, void* workspace, size_t workspace_bytes,
@@ -151,6 +153,20 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
                     const float* alpha, const float* beta, const float* gate_logits,
                     const float* state_in, void* k_ring, void* v_ring, void* out,
                     float* state_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The windowed stage of kairos_hlta_fwd on its own: both windowed branches
+ * and the gated combination with an already computed GDN branch output.
+ *   q, k       bf16 [B][T][H][128], or E4M3 codes with q_scales / k_scales
+ *              (window_qk == KAIROS_FP8_E4M3, as written by kairos_fp8_quantize)
+ *   v          bf16 [B][T][H][128];  o_gdn bf16 [B][T][H][128]
+ *   gate_logits [3][H] fp32;  k_ring / v_ring as in kairos_hlta_fwd (read only)
+ *   out        bf16 [B][T][H][128], y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn
+ * kairos_hlta_fwd = [kairos_fp8_quantize x2] + kairos_gdn_fwd + this call
+ * [+ the ring update]; the stages are exposed for timing and composition. */
+int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const void* k,
+                           const void* v, const float* q_scales, const float* k_scales,
+                           const void* o_gdn, const float* gate_logits, const void* k_ring,
+                           const void* v_ring, void* out, void* stream);
 
 /* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block):
  * s = amax / 448 (fp32; 1 when amax == 0), code = E4M3(x / s) with an IEEE

@@ -14,7 +14,7 @@ lib_path = os.path.join(_HERE, "libkairos.so")
 symbols = (
     "kairos_status_string", "kairos_version", "kairos_gdn_workspace_size",
     "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
-    "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize",
+    "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
 )
 
 
@@ -56,6 +56,7 @@ def lib():
         L.kairos_gdn_fwd.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]
         L.kairos_window_fwd.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 9
         L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p]
+        L.kairos_hlta_window_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11
         L.kairos_fp8_quantize.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                           c_int32, c_void_p]
         for name in symbols:
@@ -260,3 +261,37 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
                                _ptr(out), _ptr(state_out), _ptr(ws), nws, _stream(stream))
     _check(st, "kairos_hlta_fwd")
     return out, state_out
+
+
+def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, frame_offset=0,
+                           ring_frames=0, k_ring=None, v_ring=None, q_scales=None, k_scales=None,
+                           out=None, stream=None):
+    """Windowed stage of the hybrid layer: SWA + DSWA + gated combination with
+    o_gdn.  q, k bf16 or uint8 E4M3 codes (with scales); v, o_gdn bf16."""
+    torch = _torch()
+    B, T, H, d = v.shape
+    dev = v.device
+    fp8 = q.dtype == torch.uint8
+    qk_dtype = torch.uint8 if fp8 else torch.bfloat16
+    _need(q, "q", qk_dtype, (B, T, H, d), dev)
+    _need(k, "k", qk_dtype, (B, T, H, d), dev)
+    _need(v, "v", torch.bfloat16, (B, T, H, d), dev)
+    _need(o_gdn, "o_gdn", torch.bfloat16, (B, T, H, d), dev)
+    _need(gate_logits, "gate_logits", torch.float32, (3, H), dev)
+    if fp8:
+        nb = (T + 63) // 64
+        _need(q_scales, "q_scales", torch.float32, (B, H, nb), dev)
+        _need(k_scales, "k_scales", torch.float32, (B, H, nb), dev)
+    if ring_frames:
+        _need(k_ring, "k_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+        _need(v_ring, "v_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
+    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames,
+                     FP8_E4M3 if fp8 else BF16)
+    st = lib().kairos_hlta_window_fwd(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scales),
+                                      _ptr(k_scales), _ptr(o_gdn), _ptr(gate_logits), _ptr(k_ring),
+                                      _ptr(v_ring), _ptr(out), _stream(stream))
+    _check(st, "kairos_hlta_window_fwd")
+    return out

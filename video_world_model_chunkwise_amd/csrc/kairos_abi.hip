@@ -65,14 +65,20 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
 }
 
 struct HltaWs {
-  size_t o_gdn, q8, k8, qs, ks, total;
+  size_t gdn, o_gdn, q8, k8, qs, ks, total;
 };
+
+size_t gdn_ws_bytes(const kairos_gdn_desc* d) {
+  return d->io == KAIROS_BF16 ? gdn_chunk_workspace(d->B, d->T, d->H) : 0;
+}
 
 HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
   HltaWs w{};
   const size_t n = (size_t)d->g.B * d->g.T * d->g.H * d->g.dk;
   const size_t nblk = (size_t)(d->g.T + 63) / 64;
   size_t off = 0;
+  w.gdn = off;
+  off += align_up(gdn_ws_bytes(&d->g));
   w.o_gdn = off;
   off += align_up(n * 2);
   if (d->window_qk == KAIROS_FP8_E4M3) {
@@ -154,7 +160,7 @@ int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
   if (!bytes) return KAIROS_ERR_NULL;
   const int st = check_gdn_desc(desc);
   if (st != KAIROS_OK) return st;
-  *bytes = 0;
+  *bytes = gdn_ws_bytes(desc);
   return KAIROS_OK;
 }
 
@@ -180,8 +186,14 @@ int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, co
   if (st != KAIROS_OK) return st;
   st = check_gdn_ptrs(desc, q, k, v, alpha, beta, state_in, out, state_out);
   if (st != KAIROS_OK) return st;
-  (void)workspace;
-  (void)workspace_bytes;
+  const size_t need = gdn_ws_bytes(desc);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KAIROS_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return KAIROS_ERR_ALIGN;
+  const size_t nx = (size_t)desc->B * desc->T * desc->H * desc->dk * (desc->io == KAIROS_F32 ? 4 : 2);
+  if (overlaps(workspace, need, out, nx) || overlaps(workspace, need, q, nx) ||
+      overlaps(workspace, need, k, nx) || overlaps(workspace, need, v, nx) ||
+      overlaps(workspace, need, state_out, (size_t)desc->B * desc->H * desc->dk * desc->dv * 4))
+    return KAIROS_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   if (desc->io == KAIROS_F32)
     return hip_status(launch_gdn_f32((const float*)q, (const float*)k, (const float*)v, alpha, beta,
@@ -189,7 +201,7 @@ int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, co
                                      desc->dk, s));
   return hip_status(launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                      alpha, beta, state_in, (uint16_t*)out, state_out, desc->B,
-                                     desc->T, desc->H, desc->dk, 0, s));
+                                     desc->T, desc->H, desc->dk, 0, workspace, s));
 }
 
 int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void* q, const void* k,
@@ -231,6 +243,43 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
   return hip_status(launch_window(a, fp8, false, (hipStream_t)stream));
 }
 
+int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const void* k,
+                           const void* v, const float* q_scales, const float* k_scales,
+                           const void* o_gdn, const float* gate_logits, const void* k_ring,
+                           const void* v_ring, void* out, void* stream) {
+  int st = check_hlta_desc(desc, true);
+  if (st != KAIROS_OK) return st;
+  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  if (desc->g.T == 0) return KAIROS_OK;
+  if (!q || !k || !v || !o_gdn || !gate_logits || !out) return KAIROS_ERR_NULL;
+  if (fp8 && (!q_scales || !k_scales)) return KAIROS_ERR_NULL;
+  if (!fp8 && (q_scales || k_scales)) return KAIROS_ERR_UNSUPPORTED;
+  if (desc->ring_frames > 0 && (!k_ring || !v_ring)) return KAIROS_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_gdn) || !aligned16(out) ||
+      !aligned16(k_ring) || !aligned16(v_ring))
+    return KAIROS_ERR_ALIGN;
+  const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
+  const size_t nqk = fp8 ? n : 2 * n;
+  const size_t nring = (size_t)desc->g.B * desc->ring_frames * desc->L * desc->g.H * desc->g.dk * 2;
+  if (overlaps(out, 2 * n, q, nqk) || overlaps(out, 2 * n, k, nqk) || overlaps(out, 2 * n, v, 2 * n) ||
+      overlaps(out, 2 * n, o_gdn, 2 * n) || overlaps(out, 2 * n, k_ring, nring) ||
+      overlaps(out, 2 * n, v_ring, nring))
+    return KAIROS_ERR_ALIAS;
+  WinArgs a;
+  fill_win_args(a, desc);
+  a.q = q;
+  a.k = k;
+  a.v = (const uint16_t*)v;
+  a.q_scales = q_scales;
+  a.k_scales = k_scales;
+  a.k_ring = (const uint16_t*)k_ring;
+  a.v_ring = (const uint16_t*)v_ring;
+  a.o_gdn = (const uint16_t*)o_gdn;
+  a.gates = gate_logits;
+  a.out = (uint16_t*)out;
+  return hip_status(launch_window(a, fp8, true, (hipStream_t)stream));
+}
+
 int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, const float* gate_logits,
                     const float* state_in, void* k_ring, void* v_ring, void* out, float* state_out,
@@ -258,7 +307,7 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   uint8_t* wsb = (uint8_t*)workspace;
   uint16_t* o_gdn = (uint16_t*)(wsb + ws.o_gdn);
   hipError_t e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha,
-                                  beta, state_in, o_gdn, state_out, B, T, H, D, 0, s);
+                                  beta, state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, s);
   if (e != hipSuccess) return KAIROS_ERR_HIP;
   if (T == 0) return KAIROS_OK;
   WinArgs a;

@@ -26,12 +26,16 @@ struct WinArgs {
 hipError_t launch_gdn_f32(const float* q, const float* k, const float* v, const float* alpha,
                           const float* beta, const float* state_in, float* out, float* state_out,
                           int B, int T, int H, int D, hipStream_t stream);
-// nw: waves per workgroup (rows of S per workgroup = 16 nw); <= 0 picks by problem size
+// Chunkwise bf16 gated delta rule: a parallel per-chunk prep kernel (decays,
+// T = (I + A)^{-1}) into `workspace` (gdn_chunk_workspace bytes), then the
+// sequential scan.  nw: waves per scan workgroup (16 nw rows of S per
+// workgroup); <= 0 picks by problem size.
 hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* alpha, const float* beta, const float* state_in,
                             uint16_t* out, float* state_out, int B, int T, int H, int D, int nw,
-                            hipStream_t stream);
+                            void* workspace, hipStream_t stream);
 int gdn_chunk_waves(int B, int H, int D);
+size_t gdn_chunk_workspace(int B, int T, int H);
 hipError_t launch_fp8_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
                             int D, hipStream_t stream);
 hipError_t launch_ring_update(const uint16_t* k, const uint16_t* v, uint16_t* k_ring,

@@ -24,6 +24,17 @@
 // O^T += V^T P^T with P taken straight from the score registers.  With FP8
 // Q/K the score product uses the 32x32x64 E4M3 instruction and the per-64-
 // token-block scales multiply the fp32 scores; P V stays bf16.
+//
+// Key order inside a 32-key tile: the score tile's row r maps to key
+// pi(r) = 16 j + 8 g + 4 h + i for r = 16 j + 8 h + 4 g + i (bits g and h
+// swapped).  With that order the 8 score registers a lane feeds into one
+// P V product step are 8 consecutive keys, so each V^T operand is a single
+// 16-byte LDS read.
+//
+// The running maximum is only raised when a block's maximum exceeds it by
+// more than 8 (log2 units): probabilities then stay <= 2^8, which is exact
+// to rescale away at the end, and the O rescale is skipped in almost every
+// block.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,7 +45,8 @@ constexpr int BQ = 128;          // queries per workgroup
 constexpr int BK = 64;           // keys per block
 constexpr int KST = WD + 8;      // Ks row stride (bf16 elements)
 constexpr int K8ST = WD + 16;    // K8s row stride (bytes)
-constexpr int VST = BK + 4;      // Vt row stride (bf16 elements)
+constexpr int VST = BK + 8;      // Vt row stride (bf16 elements)
+constexpr float RESCALE_SLACK = 8.f;
 
 template <bool FP8>
 struct WinSmem {
@@ -44,97 +56,163 @@ struct WinSmem {
   float sk[2][BK];
 };
 
-// Source pointer of the row (key at group position p) for batch b, head h.
+// Position -> source row map of one branch for one workgroup.
 struct KeyMap {
-  int L, dil, res, R, T;
-  long frame_offset;
-  __device__ __forceinline__ long token_or_ring(int p, bool& ring) const {
-    const int n = p / L;
-    const int m = p - n * L;
-    const long f = (long)n * dil + res;             // absolute frame
-    if (f >= frame_offset) {
-      ring = false;
-      return (f - frame_offset) * L + m;             // token index in the call
+  int L, dil, res, R, frame_offset;
+};
+
+// Element offset of row m of the frame at sub-frame index n of the group:
+// a frame of the call, or (frames before the call) a ring slot.
+__device__ __forceinline__ const uint8_t* frame_base(const KeyMap& km, const uint8_t* x,
+                                                     const uint8_t* ring, int esz, int b, int h,
+                                                     int T, int H, int n) {
+  const int f = n * km.dil + km.res;                       // absolute frame
+  if (f >= km.frame_offset)
+    return x + (((size_t)b * T + (size_t)(f - km.frame_offset) * km.L) * H + h) * (size_t)WD * esz;
+  return ring + (((size_t)b * km.R + f % km.R) * km.L * (size_t)H + h) * (size_t)WD * esz;
+}
+
+// Source rows of the 64 keys of a block starting at group position pb.  For
+// L >= 64 a block spans at most two frames: positions with offset m < L come
+// from frame n0, the rest from frame n0 + 1.  Positions past p_hi are clamped
+// to p_hi (they are masked out of the softmax; clamping keeps loads in bounds
+// and the loaded values finite).
+template <bool SHORTL>
+struct BlockSrc {
+  const uint8_t* base0;
+  const uint8_t* base1;
+  int m0, L, p_hi, pb;
+  size_t rstride;             // bytes between consecutive rows of a frame
+  const KeyMap* km;
+  const uint8_t* x;
+  const uint8_t* ring;
+  int esz, b, h, T, H;
+  int tok0, tok1;             // token index (in the call) of row 0 of frames n0, n0 + 1
+  // token of the key at block offset off; only for blocks without ring rows
+  __device__ __forceinline__ int token(int off) const {
+    const int p = min(pb + off, p_hi);
+    if (!SHORTL) {
+      const int m = m0 + (p - pb);
+      const bool second = m >= L;
+      return (second ? tok1 : tok0) + (second ? m - L : m);
     }
-    ring = true;
-    return (long)(f % R) * L + m;                    // row index in the ring
+    const int n = p / L, m = p - n * L;
+    return (n * km->dil + km->res - km->frame_offset) * L + m;
+  }
+  __device__ __forceinline__ const uint8_t* row(int off) const {
+    const int p = min(pb + off, p_hi);
+    if (!SHORTL) {
+      const int m = m0 + (p - pb);
+      const bool second = m >= L;
+      const uint8_t* base = second ? base1 : base0;
+      return base + (size_t)(unsigned)(second ? m - L : m) * rstride;
+    }
+    // frames shorter than a block: walk the frames
+    const int n = p / L, m = p - n * L;
+    return frame_base(*km, x, ring, esz, b, h, T, H, n) + (size_t)m * rstride;
   }
 };
 
+template <bool SHORTL>
+__device__ __forceinline__ BlockSrc<SHORTL> block_src(const KeyMap& km, const void* x, const void* ring,
+                                                      int esz, int b, int h, int T, int H, int pb,
+                                                      int p_hi) {
+  BlockSrc<SHORTL> s;
+  const int n0 = pb / km.L;
+  s.m0 = pb - n0 * km.L;
+  s.L = km.L;
+  s.p_hi = p_hi;
+  s.pb = pb;
+  s.rstride = (size_t)H * WD * esz;
+  s.km = &km;
+  s.x = reinterpret_cast<const uint8_t*>(x);
+  s.ring = reinterpret_cast<const uint8_t*>(ring);
+  s.esz = esz;
+  s.b = b;
+  s.h = h;
+  s.T = T;
+  s.H = H;
+  s.base0 = frame_base(km, s.x, s.ring, esz, b, h, T, H, n0);
+  // the second frame is only dereferenced for positions <= p_hi, which exist
+  const int n1 = min(n0 + 1, p_hi / km.L);
+  s.base1 = frame_base(km, s.x, s.ring, esz, b, h, T, H, n1);
+  s.tok0 = (n0 * km.dil + km.res - km.frame_offset) * km.L;
+  s.tok1 = (n1 * km.dil + km.res - km.frame_offset) * km.L;
+  return s;
+}
+
+// Global loads of one 64-key block into registers.
+//  V: thread -> keys 8*(tid%8) .. +7, features 4*(tid/8) .. +3 (8 loads of 8 bytes)
+//  bf16 K: thread -> keys 4*(tid/16) .. +3, features 8*(tid%16) .. +7 (4 loads of 16 bytes)
+//  E4M3 K: thread -> key tid/4, bytes 32*(tid%4) .. +31 (2 loads of 16 bytes) + its block scale
 template <bool FP8>
+struct BlockRegs {
+  uint2 v[8];
+  uint4 k[FP8 ? 2 : 4];
+  float sk;
+};
+
+template <bool FP8, bool SHORTL>
 __device__ __forceinline__ void win_load_block(const WinArgs& a, const KeyMap& km, int b, int h,
-                                               int pb, int p_hi, uint4 (&kr)[4], uint4 (&vr)[4],
-                                               float& skr) {
+                                               int pb, int p_hi, BlockRegs<FP8>& r) {
   const int tid = threadIdx.x;
-  const size_t tok_stride = (size_t)a.H * WD;
-  // V (and bf16 K): 4 consecutive keys x 8 features per thread
-  const int kq = tid / 16, dg = tid % 16;
+  {
+    const auto vs = block_src<SHORTL>(km, a.v, a.v_ring, 2, b, h, a.T, a.H, pb, p_hi);
+    const int kq8 = tid % 8, dq = tid / 8;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = pb + 4 * kq + j;
-    vr[j] = make_uint4(0, 0, 0, 0);
-    if (!FP8) kr[j] = make_uint4(0, 0, 0, 0);
-    if (p <= p_hi) {
-      bool ring;
-      const long row = km.token_or_ring(p, ring);
-      const size_t off = ring ? (((size_t)b * a.R * a.L + row) * a.H + h) * WD + 8 * dg
-                              : ((size_t)b * a.T + row) * tok_stride + (size_t)h * WD + 8 * dg;
-      const uint16_t* vsrc = ring ? a.v_ring : a.v;
-      vr[j] = *reinterpret_cast<const uint4*>(vsrc + off);
-      if (!FP8) {
-        const uint16_t* ksrc = ring ? a.k_ring : reinterpret_cast<const uint16_t*>(a.k);
-        kr[j] = *reinterpret_cast<const uint4*>(ksrc + off);
-      }
-    }
+    for (int j = 0; j < 8; ++j)
+      r.v[j] = *reinterpret_cast<const uint2*>(vs.row(8 * kq8 + j) + 8 * dq);
   }
-  if (FP8) {
-    // K codes: key tid / 4, 32 bytes at feature 32 * (tid % 4); FP8 calls have no ring
+  if (!FP8) {
+    const auto ks = block_src<SHORTL>(km, a.k, a.k_ring, 2, b, h, a.T, a.H, pb, p_hi);
+    const int kq = tid / 16, dg = tid % 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.k[j] = *reinterpret_cast<const uint4*>(ks.row(4 * kq + j) + 16 * dg);
+  } else {
+    // E4M3 codes; FP8 calls have no ring, so rows are tokens of the call
+    const auto ks = block_src<SHORTL>(km, a.k, nullptr, 1, b, h, a.T, a.H, pb, p_hi);
     const int key = tid / 4, part = tid % 4;
-    const int p = pb + key;
-    kr[0] = kr[1] = make_uint4(0, 0, 0, 0);
-    skr = 0.f;
-    if (p <= p_hi) {
-      bool ring;
-      const long row = km.token_or_ring(p, ring);
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k) +
-                           ((size_t)b * a.T + row) * tok_stride + (size_t)h * WD + 32 * part;
-      kr[0] = *reinterpret_cast<const uint4*>(src);
-      kr[1] = *reinterpret_cast<const uint4*>(src + 16);
-      if (part == 0) skr = a.k_scales[((size_t)b * a.H + h) * a.nblk + row / 64];
-    }
+    const uint8_t* src = ks.row(key);
+    r.k[0] = *reinterpret_cast<const uint4*>(src + 32 * part);
+    r.k[1] = *reinterpret_cast<const uint4*>(src + 32 * part + 16);
+    r.sk = a.k_scales[((size_t)b * a.H + h) * a.nblk + ks.token(key) / 64];
   }
 }
 
 __device__ __forceinline__ uint32_t lo16w(uint32_t x) { return x & 0xFFFFu; }
 __device__ __forceinline__ uint32_t hi16w(uint32_t x) { return x >> 16; }
+// (low half of a, low half of b) and (high half of a, high half of b)
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 template <bool FP8>
-__device__ __forceinline__ void win_store_block(WinSmem<FP8>& sm, int buf, const uint4 (&kr)[4],
-                                                const uint4 (&vr)[4], float skr) {
+__device__ __forceinline__ void win_store_block(WinSmem<FP8>& sm, int buf, const BlockRegs<FP8>& r) {
   const int tid = threadIdx.x;
-  const int kq = tid / 16, dg = tid % 16;
   if (!FP8) {
+    const int kq = tid / 16, dg = tid % 16;
     uint16_t* Ks = reinterpret_cast<uint16_t*>(sm.kbuf[buf]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(Ks + (4 * kq + j) * KST + 8 * dg) = kr[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(Ks + (4 * kq + j) * KST + 8 * dg) = r.k[j];
   } else {
     const int key = tid / 4, part = tid % 4;
     uint8_t* K8 = sm.kbuf[buf];
-    *reinterpret_cast<uint4*>(K8 + key * K8ST + 32 * part) = kr[0];
-    *reinterpret_cast<uint4*>(K8 + key * K8ST + 32 * part + 16) = kr[1];
-    if (part == 0) sm.sk[buf][key] = skr;
+    *reinterpret_cast<uint4*>(K8 + key * K8ST + 32 * part) = r.k[0];
+    *reinterpret_cast<uint4*>(K8 + key * K8ST + 32 * part + 16) = r.k[1];
+    if (part == 0) sm.sk[buf][key] = r.sk;
   }
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
+  // V^T: feature row 4 dq + e gets keys 8 kq8 .. +7 (one 16-byte write per feature)
+  const int kq8 = tid % 8, dq = tid / 8;
+  uint4 w[4];
+  w[0] = make_uint4(pack_lo(r.v[0].x, r.v[1].x), pack_lo(r.v[2].x, r.v[3].x),
+                    pack_lo(r.v[4].x, r.v[5].x), pack_lo(r.v[6].x, r.v[7].x));
+  w[1] = make_uint4(pack_hi(r.v[0].x, r.v[1].x), pack_hi(r.v[2].x, r.v[3].x),
+                    pack_hi(r.v[4].x, r.v[5].x), pack_hi(r.v[6].x, r.v[7].x));
+  w[2] = make_uint4(pack_lo(r.v[0].y, r.v[1].y), pack_lo(r.v[2].y, r.v[3].y),
+                    pack_lo(r.v[4].y, r.v[5].y), pack_lo(r.v[6].y, r.v[7].y));
+  w[3] = make_uint4(pack_hi(r.v[0].y, r.v[1].y), pack_hi(r.v[2].y, r.v[3].y),
+                    pack_hi(r.v[4].y, r.v[5].y), pack_hi(r.v[6].y, r.v[7].y));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    *reinterpret_cast<uint2*>(&sm.Vt[buf][8 * dg + 2 * e][4 * kq]) =
-        make_uint2(lo16w(w0[e]) | (lo16w(w1[e]) << 16), lo16w(w2[e]) | (lo16w(w3[e]) << 16));
-    *reinterpret_cast<uint2*>(&sm.Vt[buf][8 * dg + 2 * e + 1][4 * kq]) =
-        make_uint2(hi16w(w0[e]) | (hi16w(w1[e]) << 16), hi16w(w2[e]) | (hi16w(w3[e]) << 16));
-  }
+  for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(&sm.Vt[buf][4 * dq + e][8 * kq8]) = w[e];
 }
 
 // Key range of one branch for one query tile, in group-position space.
@@ -152,8 +230,7 @@ __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, i
   r.km.dil = dil;
   r.km.res = (int)(f_abs % dil);
   r.km.R = a.R;
-  r.km.T = a.T;
-  r.km.frame_offset = a.frame_offset;
+  r.km.frame_offset = (int)a.frame_offset;
   r.pq0 = (int)(f_abs / dil) * a.L;
   const long f_avail = a.frame_offset - a.R > 0 ? a.frame_offset - a.R : 0;
   const long f1 = f_avail + (((r.km.res - f_avail % dil) % dil) + dil) % dil;   // first frame of the group
@@ -165,7 +242,12 @@ __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, i
   return r;
 }
 
-template <bool FP8, bool HYBRID>
+// key offset inside a 64-key block of score register r of tile kt (lane group g)
+__device__ __forceinline__ constexpr int key_of(int kt, int r, int g) {
+  return 32 * kt + 16 * (r / 8) + 8 * g + 4 * ((r / 4) & 1) + (r & 3);
+}
+
+template <bool FP8, bool HYBRID, bool SHORTL>
 __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
   __shared__ WinSmem<FP8> sm;
   const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -188,6 +270,8 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
   // wave's query rows (clamped) for the block masking decision
   const int mw_lo = min(m0 + 32 * wave, m_last_wg);
   const int mw_hi = min(m0 + 32 * wave + 31, m_last_wg);
+  // score row of this lane's A operand: key pi(ql) of each 32-key tile
+  const int krow = 16 * (ql / 16) + 8 * ((ql / 4) & 1) + 4 * ((ql / 8) & 1) + (ql & 3);
 
   // ---- Q operand registers (B operand of S^T = K Q^T)
   bf16x8 qf[8];
@@ -209,14 +293,13 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
     }
     qscale = a.q_scales[((size_t)b * a.H + h) * a.nblk + tq / 64];
   }
-  // log2(e) / sqrt(d): scores in exp2 units
-  const float sc = 1.4426950408889634f * 0.08838834764831845f * qscale;
+  // log2(e) / sqrt(d) (x the query's block scale): scores in exp2 units
+  const float cq = 1.4426950408889634f * 0.08838834764831845f * qscale;
 
-  const int nbr = HYBRID ? 2 : 1;
-  BranchRange br[2];
-  br[0] = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
-  if (HYBRID) br[1] = branch_range(a, a.dil, f, m0, m_last_wg);
-  const int nb_total = br[0].nb + (HYBRID ? br[1].nb : 0);
+  // branch 0: SWA (or the single requested branch), branch 1: DSWA (hybrid only)
+  const BranchRange b0 = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
+  const BranchRange b1 = HYBRID ? branch_range(a, a.dil, f, m0, m_last_wg) : b0;
+  const int nb_total = b0.nb + (HYBRID ? b1.nb : 0);
 
   f32x16 O[4];
   f32x16 Y[4];
@@ -227,41 +310,41 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
   }
   float m_run = -1e30f, l_run = 0.f;
 
-  uint4 kr[4], vr[4];
-  float skr = 0.f;
-  win_load_block<FP8>(a, br[0].km, b, h, br[0].p_lo, br[0].p_hi, kr, vr, skr);
-  win_store_block<FP8>(sm, 0, kr, vr, skr);
+  BlockRegs<FP8> regs;
+  win_load_block<FP8, SHORTL>(a, b0.km, b, h, b0.p_lo, b0.p_hi, regs);
+  win_store_block<FP8>(sm, 0, regs);
   __syncthreads();
 
-  int cur_br = 0, jb_in = 0;
   for (int jb = 0; jb < nb_total; ++jb) {
     const int buf = jb & 1;
-    // next block's coordinates
-    int nbr_i = cur_br, njb = jb_in + 1;
-    if (njb >= br[cur_br].nb) { nbr_i = cur_br + 1; njb = 0; }
+    const bool in1 = HYBRID && jb >= b0.nb;          // uniform
+    const int jb_in = in1 ? jb - b0.nb : jb;
+    const int cb_nb = in1 ? b1.nb : b0.nb;
+    const int pb = (in1 ? b1.p_lo : b0.p_lo) + BK * jb_in;
+    const int pq0 = in1 ? b1.pq0 : b0.pq0;
+    // prefetch the next block (possibly the first block of branch 1)
     const bool has_next = jb + 1 < nb_total;
     if (has_next) {
-      const BranchRange& nb_r = br[nbr_i];
-      win_load_block<FP8>(a, nb_r.km, b, h, nb_r.p_lo + BK * njb, nb_r.p_hi, kr, vr, skr);
+      const bool n1 = HYBRID && jb + 1 >= b0.nb;
+      if (n1) win_load_block<FP8, SHORTL>(a, b1.km, b, h, b1.p_lo + BK * (jb + 1 - b0.nb), b1.p_hi, regs);
+      else win_load_block<FP8, SHORTL>(a, b0.km, b, h, b0.p_lo + BK * (jb + 1), b0.p_hi, regs);
     }
 
-    const BranchRange& cb = br[cur_br];
-    const int pb = cb.p_lo + BK * jb_in;
-    const int pq = cb.pq0 + mq;                      // this lane's query position
-    const bool full = (pb > cb.pq0 + mw_hi - a.w) && (pb + BK - 1 <= cb.pq0 + mw_lo);
+    const int pq = pq0 + mq;                         // this lane's query position
+    const bool full = (pb > pq0 + mw_hi - a.w) && (pb + BK - 1 <= pq0 + mw_lo);
 
-    // ---- scores S^T (two 32-key tiles), lane: query ql, keys 32kt + 8(r/4) + 4g + r%4
+    // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
     f32x16 S[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       S[kt] = f32x16{};
       if (!FP8) {
-        const uint16_t* Ks = reinterpret_cast<const uint16_t*>(sm.kbuf[buf]) + (32 * kt + ql) * KST;
+        const uint16_t* Ks = reinterpret_cast<const uint16_t*>(sm.kbuf[buf]) + (32 * kt + krow) * KST;
 #pragma unroll
         for (int s = 0; s < 8; ++s)
           S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * g)), qf[s], S[kt]);
       } else {
-        const uint8_t* K8 = sm.kbuf[buf] + (32 * kt + ql) * K8ST;
+        const uint8_t* K8 = sm.kbuf[buf] + (32 * kt + krow) * K8ST;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           uint4 lo = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * g);
@@ -271,27 +354,37 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
         }
       }
     }
-    // ---- scale, mask, running max
+    // ---- key scales, mask, block maximum (unscaled by cq > 0)
+    if (FP8) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float4 s4 = *reinterpret_cast<const float4*>(&sm.sk[buf][key_of(kt, 4 * rr, g)]);
+          S[kt][4 * rr] *= s4.x;
+          S[kt][4 * rr + 1] *= s4.y;
+          S[kt][4 * rr + 2] *= s4.z;
+          S[kt][4 * rr + 3] *= s4.w;
+        }
+    }
+    if (!full) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int pk = pb + key_of(kt, r, g);
+          if (pk > pq || pk <= pq - a.w) S[kt][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r / 4) + 4 * g + (r % 4);
-        float x = S[kt][r] * sc;
-        if (FP8) x *= sm.sk[buf][key];
-        if (!full) {
-          const int pk = pb + key;
-          if (pk > pq || pk <= pq - a.w) x = -INFINITY;
-        }
-        S[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run) != 0) {
-      const float alpha = exp2f(m_run - m_new);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cq;
+    if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
+      const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -299,14 +392,15 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
         for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
       m_run = m_new;
     }
-    // ---- probabilities -> bf16 operands
+    // ---- probabilities -> bf16 operands: registers 8j..8j+7 of a tile are keys
+    //      32 kt + 16 j + 8 g + 0..7
     bf16x8 P[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(S[kt][r] - m_run);
+        p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], cq, -m_run));
         l_run += p[r];
       }
 #pragma unroll
@@ -321,19 +415,17 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint2 lo = *reinterpret_cast<const uint2*>(vrow + 32 * kt + 16 * j + 4 * g);
-          uint2 hi = *reinterpret_cast<const uint2*>(vrow + 32 * kt + 16 * j + 8 + 4 * g);
-          O[dt] = mfma32x32x16(as_bf16x8(lo, hi), P[kt][j], O[dt]);
-        }
+        for (int j = 0; j < 2; ++j)
+          O[dt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 32 * kt + 16 * j + 8 * g)),
+                               P[kt][j], O[dt]);
     }
 
     // ---- end of a branch: normalise and fold into the output accumulator
-    if (jb_in + 1 == cb.nb) {
+    if (jb_in + 1 == cb_nb) {
       const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
       const float inv = 1.f / l_tot;
       float gsc = 1.f;
-      if (HYBRID) gsc = 1.f / (1.f + __expf(-a.gates[cur_br * a.H + h]));
+      if (HYBRID) gsc = 1.f / (1.f + __expf(-a.gates[(in1 ? 1 : 0) * a.H + h]));
       const float fac = gsc * inv;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -346,12 +438,9 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
       l_run = 0.f;
     }
 
-    if (has_next) win_store_block<FP8>(sm, buf ^ 1, kr, vr, skr);
+    if (has_next) win_store_block<FP8>(sm, buf ^ 1, regs);
     __syncthreads();
-    cur_br = nbr_i;
-    jb_in = njb;
   }
-  (void)nbr;
 
   // ---- epilogue: (+ gated GDN branch) -> bf16 output row of this lane's query
   if (!q_valid) return;
@@ -382,13 +471,16 @@ hipError_t launch_window(const WinArgs& args_in, bool fp8, bool hybrid, hipStrea
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
-  if (fp8) {
-    if (hybrid) win_attn_kernel<true, true><<<grid, 256, 0, stream>>>(a);
-    else win_attn_kernel<true, false><<<grid, 256, 0, stream>>>(a);
+  const bool shortl = a.L < BK;
+#define KAIROS_WIN_LAUNCH(F8, HY, SL) win_attn_kernel<F8, HY, SL><<<grid, 256, 0, stream>>>(a)
+  if (shortl) {
+    if (fp8) { if (hybrid) KAIROS_WIN_LAUNCH(true, true, true); else KAIROS_WIN_LAUNCH(true, false, true); }
+    else { if (hybrid) KAIROS_WIN_LAUNCH(false, true, true); else KAIROS_WIN_LAUNCH(false, false, true); }
   } else {
-    if (hybrid) win_attn_kernel<false, true><<<grid, 256, 0, stream>>>(a);
-    else win_attn_kernel<false, false><<<grid, 256, 0, stream>>>(a);
+    if (fp8) { if (hybrid) KAIROS_WIN_LAUNCH(true, true, false); else KAIROS_WIN_LAUNCH(true, false, false); }
+    else { if (hybrid) KAIROS_WIN_LAUNCH(false, true, false); else KAIROS_WIN_LAUNCH(false, false, false); }
   }
+#undef KAIROS_WIN_LAUNCH
   return hipGetLastError();
 }
 

@@ -154,3 +154,39 @@ def make_inputs(w: Workload | int, T: Optional[int] = None) -> dict:
         w = WORKLOADS[w]
     return make_custom(w.B, T if T is not None else w.T, w.H, w.d, w.io, w.seed,
                        w.alpha_kind, w.beta_kind)
+
+
+def make_device_inputs(w: Workload | int, device="cuda:0", seed_offset: int = 0, T: Optional[int] = None) -> dict:
+    """The workload's distributions drawn on the device with torch's generator
+    (seeded with the workload's seed; a different stream of numbers than the
+    NumPy recipe, used where only shapes and distributions matter, e.g. for
+    timing).  q, k, v bf16 (k L2-normalised in fp32 before rounding);
+    alpha, beta, gates fp32."""
+    import torch
+    if isinstance(w, int):
+        w = WORKLOADS[w]
+    T = w.T if T is None else T
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed + seed_offset)
+    shape = (w.B, T, w.H, w.d)
+    out = {}
+    dt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    q = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    out["q"] = q.to(dt)
+    del q
+    k = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    k /= torch.linalg.vector_norm(k, dim=-1, keepdim=True)
+    out["k"] = k.to(dt)
+    del k
+    out["v"] = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(dt)
+    if w.alpha_kind == "softplus":
+        x = torch.randn((w.B, T, w.H), generator=gen, device=device) - 4.0
+        out["alpha"] = torch.sigmoid(-x)                      # exp(-softplus(x))
+    else:
+        out["alpha"] = torch.rand((w.B, T, w.H), generator=gen, device=device) * 0.099 + 0.9
+    if w.beta_kind == "sigmoid":
+        out["beta"] = torch.sigmoid(torch.randn((w.B, T, w.H), generator=gen, device=device))
+    else:
+        out["beta"] = torch.rand((w.B, T, w.H), generator=gen, device=device) * 0.95 + 0.05
+    out["gates"] = torch.randn((3, w.H), generator=gen, device=device)
+    return out
