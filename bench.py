@@ -201,6 +201,7 @@ def main():
     sq = torch.empty((w.B, w.H, nb), dtype=torch.float32, device=dev)
     sk = torch.empty_like(sq)
     o_gdn = torch.empty_like(d["v"])
+    yws = torch.empty(4 * d["v"].numel(), dtype=torch.uint8, device=dev)
     S = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
     t_quant = st.run("fp8_quant_q", lambda: K.kairos_fp8_quantize(d["q"], codes_q, sq), reps)
     st.run("fp8_quant_k", lambda: K.kairos_fp8_quantize(d["k"], codes_k, sk), reps)
@@ -208,7 +209,7 @@ def main():
                                                          out=o_gdn, state_out=S), reps)
     t_win = st.run("window_hybrid", lambda: K.kairos_hlta_window_fwd(
         codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
-        k_scales=sk, out=bufs["out"]), reps)
+        k_scales=sk, out=bufs["out"], workspace=yws), reps)
 
     pairs = window_pairs(w.T, w.L, w.window, 1) + window_pairs(w.T, w.L, w.window, w.dilation)
     win_flops = pairs * 4 * w.d * w.B * w.H          # QK^T 2d + PV 2d per (query, key) pair

@@ -161,12 +161,15 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
  *   v          bf16 [B][T][H][128];  o_gdn bf16 [B][T][H][128]
  *   gate_logits [3][H] fp32;  k_ring / v_ring as in kairos_hlta_fwd (read only)
  *   out        bf16 [B][T][H][128], y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn
+ *   workspace  >= 4*B*T*H*128 bytes, 256-byte aligned (fp32 partial result of
+ *              the first branch, one row per query)
  * kairos_hlta_fwd = [kairos_fp8_quantize x2] + kairos_gdn_fwd + this call
  * [+ the ring update]; the stages are exposed for timing and composition. */
 int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const void* k,
                            const void* v, const float* q_scales, const float* k_scales,
                            const void* o_gdn, const float* gate_logits, const void* k_ring,
-                           const void* v_ring, void* out, void* stream);
+                           const void* v_ring, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block):
  * s = amax / 448 (fp32; 1 when amax == 0), code = E4M3(x / s) with an IEEE

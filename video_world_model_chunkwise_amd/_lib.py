@@ -56,7 +56,7 @@ def lib():
         L.kairos_gdn_fwd.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]
         L.kairos_window_fwd.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 9
         L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p]
-        L.kairos_hlta_window_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11
+        L.kairos_hlta_window_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_size_t, c_void_p]
         L.kairos_fp8_quantize.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                           c_int32, c_void_p]
         for name in symbols:
@@ -265,7 +265,7 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
 
 def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, frame_offset=0,
                            ring_frames=0, k_ring=None, v_ring=None, q_scales=None, k_scales=None,
-                           out=None, stream=None):
+                           out=None, workspace=None, stream=None):
     """Windowed stage of the hybrid layer: SWA + DSWA + gated combination with
     o_gdn.  q, k bf16 or uint8 E4M3 codes (with scales); v, o_gdn bf16."""
     torch = _torch()
@@ -290,8 +290,12 @@ def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, fra
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
     desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames,
                      FP8_E4M3 if fp8 else BF16)
+    nws = 4 * B * T * H * d
+    ws = workspace if workspace is not None else _workspace(nws, dev)
+    if ws.numel() < nws:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nws}")
     st = lib().kairos_hlta_window_fwd(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scales),
                                       _ptr(k_scales), _ptr(o_gdn), _ptr(gate_logits), _ptr(k_ring),
-                                      _ptr(v_ring), _ptr(out), _stream(stream))
+                                      _ptr(v_ring), _ptr(out), _ptr(ws), nws, _stream(stream))
     _check(st, "kairos_hlta_window_fwd")
     return out

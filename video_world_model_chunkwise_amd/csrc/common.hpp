@@ -75,6 +75,16 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which would drain the next
+// block's prefetch at each barrier; here only LDS operations are completed
+// before the barrier and global loads stay in flight (their own uses are
+// guarded by the compiler's waits).  The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Linear block id -> (xcd-major) id so that consecutive logical ids of one
 // group land on one XCD (blocks are dispatched round-robin over 8 XCDs).
 __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {

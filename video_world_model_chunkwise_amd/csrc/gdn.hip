@@ -300,6 +300,13 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const uint16_t* __restric
 }
 
 // ---- scan: per (b, h, 16*NW rows of S), chunks in order
+//
+// Staging maps (token quad, feature group) to lanes so that global loads read
+// >= 32 contiguous bytes per row while the transposed LDS writes of one
+// 32-lane phase land on distinct banks: 4 consecutive lanes share a row,
+// 16 rows per wave, and the wave index selects the next feature groups.
+__device__ __forceinline__ int kq_dgroup(int u) { return 4 * (u / 64) + (u % 4); }
+__device__ __forceinline__ int kq_tquad(int u) { return (u % 64) / 4; }
 template <int D, int NW>
 struct ScanSmem {
   static constexpr int NR = 16 * NW;
@@ -336,6 +343,12 @@ __device__ __forceinline__ void scan_fetch(ScanPrefetch<D, NW>& pf, const uint16
                                            const uint16_t* __restrict__ t_in,
                                            const float* __restrict__ g_in, int b, int h, int bh, int T,
                                            int H, int c, int nchunks, int n_base) {
+  // Branch-free: rows past the sequence are clamped to its last token (real,
+  // finite data).  They need no zeroing: such tokens get b = 0 when staged, so
+  // their rows of R and E are exactly zero and they add nothing to S, and
+  // T = (I + A)^{-1} is the identity on them; their outputs are not stored.
+  // Without branches the memory counters stay exact, so waits never drain
+  // unrelated stores.
   const int tid = threadIdx.x;
   constexpr int DG = D / 8;
   const int t0 = c * CH;
@@ -343,63 +356,56 @@ __device__ __forceinline__ void scan_fetch(ScanPrefetch<D, NW>& pf, const uint16
   const size_t base = ((size_t)b * T * H + h) * D;
 #pragma unroll
   for (int p = 0; p < ScanPrefetch<D, NW>::KQ_PASSES; ++p) {
-    const int u = tid + p * 64 * NW;
-    const int dg = u % DG, tq = u / DG;
+    const int u = min(tid + p * 64 * NW, ScanPrefetch<D, NW>::NQUADS - 1);
+    const int dg = kq_dgroup(u), tq = kq_tquad(u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 4 * tq + j;
-      if (u < ScanPrefetch<D, NW>::NQUADS && t < T) {
-        const size_t off = base + (size_t)t * tok_stride + 8 * dg;
-        pf.k[p][j] = *reinterpret_cast<const uint4*>(k + off);
-        pf.q[p][j] = *reinterpret_cast<const uint4*>(q + off);
-      } else {
-        pf.k[p][j] = make_uint4(0, 0, 0, 0);
-        pf.q[p][j] = make_uint4(0, 0, 0, 0);
-      }
+      const int t = min(t0 + 4 * tq + j, T - 1);
+      const size_t off = base + (size_t)t * tok_stride + 8 * dg;
+      pf.k[p][j] = *reinterpret_cast<const uint4*>(k + off);
+      pf.q[p][j] = *reinterpret_cast<const uint4*>(q + off);
     }
   }
   {
-    const int nq = tid % (4 * NW), tq = tid / (4 * NW);
+    const int nq = kq_dgroup(tid), tq = kq_tquad(tid);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 4 * tq + j;
-      pf.v[j] = (t < T) ? *reinterpret_cast<const uint2*>(v + base + (size_t)t * tok_stride + n_base + 4 * nq)
-                        : make_uint2(0, 0);
+      const int t = min(t0 + 4 * tq + j, T - 1);
+      pf.v[j] = *reinterpret_cast<const uint2*>(v + base + (size_t)t * tok_stride + n_base + 4 * nq);
     }
   }
   const uint16_t* tsrc = t_in + ((size_t)bh * nchunks + c) * CH * CH;
 #pragma unroll
   for (int p = 0; p < ScanPrefetch<D, NW>::T_PASSES; ++p) {
-    const int u = tid + p * 64 * NW;
-    pf.t[p] = u < ScanPrefetch<D, NW>::T_UNITS ? *reinterpret_cast<const uint4*>(tsrc + 8 * u)
-                                              : make_uint4(0, 0, 0, 0);
+    const int u = min(tid + p * 64 * NW, ScanPrefetch<D, NW>::T_UNITS - 1);
+    pf.t[p] = *reinterpret_cast<const uint4*>(tsrc + 8 * u);
   }
-  if (tid < 64) {
-    const int t = t0 + tid;
-    pf.g = g_in[((size_t)bh * nchunks + c) * CH + tid];
-    pf.b = t < T ? beta[((size_t)b * T + t) * H + h] : 0.f;
-  }
+  const int lt = tid % 64;
+  pf.g = g_in[((size_t)bh * nchunks + c) * CH + lt];
+  pf.b = beta[((size_t)b * T + min(t0 + lt, T - 1)) * H + h];
 }
 
 template <int D, int NW>
-__device__ __forceinline__ void scan_stage(const ScanPrefetch<D, NW>& pf, ScanSmem<D, NW>& sm, int buf) {
+__device__ __forceinline__ void scan_stage(const ScanPrefetch<D, NW>& pf, ScanSmem<D, NW>& sm, int buf,
+                                           int t0, int T) {
   const int tid = threadIdx.x;
   constexpr int DG = D / 8;
 #pragma unroll
   for (int p = 0; p < ScanPrefetch<D, NW>::KQ_PASSES; ++p) {
     const int u = tid + p * 64 * NW;
     if (u >= ScanPrefetch<D, NW>::NQUADS) break;
-    const int dg = u % DG, tq = u / DG;
+    const int dg = kq_dgroup(u), tq = kq_tquad(u);
+    const uint4* kk = pf.k[p];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       *reinterpret_cast<uint4*>(&sm.Ks[buf][4 * tq + j][8 * dg]) = pf.k[p][j];
       *reinterpret_cast<uint4*>(&sm.Qs[buf][4 * tq + j][8 * dg]) = pf.q[p][j];
     }
     // transpose the 4 tokens x 8 features block into Kt[d][t..t+3]
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&pf.k[p][0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&pf.k[p][1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&pf.k[p][2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&pf.k[p][3]);
+    const uint32_t w0[4] = {kk[0].x, kk[0].y, kk[0].z, kk[0].w};
+    const uint32_t w1[4] = {kk[1].x, kk[1].y, kk[1].z, kk[1].w};
+    const uint32_t w2[4] = {kk[2].x, kk[2].y, kk[2].z, kk[2].w};
+    const uint32_t w3[4] = {kk[3].x, kk[3].y, kk[3].z, kk[3].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint2 even = make_uint2(lo16(w0[e]) | (lo16(w1[e]) << 16), lo16(w2[e]) | (lo16(w3[e]) << 16));
@@ -409,9 +415,10 @@ __device__ __forceinline__ void scan_stage(const ScanPrefetch<D, NW>& pf, ScanSm
     }
   }
   {
-    const int nq = tid % (4 * NW), tq = tid / (4 * NW);
-    const uint32_t a0 = pf.v[0].x, a1 = pf.v[0].y, b0 = pf.v[1].x, b1 = pf.v[1].y;
-    const uint32_t c0 = pf.v[2].x, c1 = pf.v[2].y, d0 = pf.v[3].x, d1 = pf.v[3].y;
+    const int nq = kq_dgroup(tid), tq = kq_tquad(tid);
+    const uint2* vv = pf.v;
+    const uint32_t a0 = vv[0].x, a1 = vv[0].y, b0 = vv[1].x, b1 = vv[1].y;
+    const uint32_t c0 = vv[2].x, c1 = vv[2].y, d0 = vv[3].x, d1 = vv[3].y;
     *reinterpret_cast<uint2*>(&sm.Vt[buf][4 * nq + 0][4 * tq]) =
         make_uint2(lo16(a0) | (lo16(b0) << 16), lo16(c0) | (lo16(d0) << 16));
     *reinterpret_cast<uint2*>(&sm.Vt[buf][4 * nq + 1][4 * tq]) =
@@ -432,7 +439,7 @@ __device__ __forceinline__ void scan_stage(const ScanPrefetch<D, NW>& pf, ScanSm
     sm.g2[buf][tid] = pf.g;
     sm.gam[buf][tid] = __builtin_amdgcn_exp2f(pf.g);
     sm.wts[buf][tid] = __builtin_amdgcn_exp2f(gl - pf.g);
-    sm.bet[buf][tid] = pf.b;
+    sm.bet[buf][tid] = t0 + tid < T ? pf.b : 0.f;
   }
 }
 
@@ -478,31 +485,49 @@ __global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(
   ScanPrefetch<D, NW> pf;
   if (nchunks > 0) {
     scan_fetch<D, NW>(pf, q, k, v, beta, t_in, g_in, b, h, bh, T, H, 0, nchunks, n_base);
-    scan_stage<D, NW>(pf, sm, 0);
+    scan_stage<D, NW>(pf, sm, 0, 0, T);
   }
-  __syncthreads();
+  lds_barrier();
 
   const size_t tok_stride = (size_t)H * D;
+  // outputs of the previous chunk, stored one iteration late so that their
+  // completion never sits on a chunk's critical path
+  uint2 o_prev0 = make_uint2(0, 0), o_prev1 = o_prev0, o_prev2 = o_prev0, o_prev3 = o_prev0;
+  int t0_prev = -1;
+  uint16_t* const out_bh = out + (size_t)b * T * tok_stride + (size_t)h * D + n_w + 4 * g;
+#define KAIROS_STORE_PREV()                                                              \
+  if (t0_prev >= 0) {                                                                    \
+    const int tk = t0_prev + l16;                                                        \
+    if (tk < T) *reinterpret_cast<uint2*>(out_bh + (size_t)tk * tok_stride) = o_prev0;   \
+    if (tk + 16 < T) *reinterpret_cast<uint2*>(out_bh + (size_t)(tk + 16) * tok_stride) = o_prev1; \
+    if (tk + 32 < T) *reinterpret_cast<uint2*>(out_bh + (size_t)(tk + 32) * tok_stride) = o_prev2; \
+    if (tk + 48 < T) *reinterpret_cast<uint2*>(out_bh + (size_t)(tk + 48) * tok_stride) = o_prev3; \
+  }
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * CH;
     const int cur = c & 1;
+    KAIROS_STORE_PREV();
     if (c + 1 < nchunks)
       scan_fetch<D, NW>(pf, q, k, v, beta, t_in, g_in, b, h, bh, T, H, c + 1, nchunks, n_base);
 
     // ---- P = lower(2^{g_t - g_i} Q K^T)
+    // (computed as the tile (tj, ti) of K Q^T: lane holds P[t = 16 ti + l16][i = 16 tj + 4 g + r],
+    //  four consecutive entries of a row of P, written as one 8-byte store)
     for (int task = wave; task < 10; task += NW) {
       int ti, tj;
       tri_index(task, ti, tj);
-      const f32x4 acc = gram_tile<D>(&sm.Qs[cur][0][0], &sm.Ks[cur][0][0], D + KS_PAD, ti, tj, l16, g);
-      const int col = 16 * tj + l16;
-      const float gc = sm.g2[cur][col];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * ti + 4 * g + r;
-        sm.Pb[row][col] = bf16_bits(col <= row ? __builtin_amdgcn_exp2f(sm.g2[cur][row] - gc) * acc[r] : 0.f);
-      }
+      const f32x4 acc = gram_tile<D>(&sm.Ks[cur][0][0], &sm.Qs[cur][0][0], D + KS_PAD, tj, ti, l16, g);
+      const int t = 16 * ti + l16;
+      const int i0 = 16 * tj + 4 * g;
+      const float gt = sm.g2[cur][t];
+      const float4 gi = *reinterpret_cast<const float4*>(&sm.g2[cur][i0]);
+      const float p0 = i0 <= t ? __builtin_amdgcn_exp2f(gt - gi.x) * acc[0] : 0.f;
+      const float p1 = i0 + 1 <= t ? __builtin_amdgcn_exp2f(gt - gi.y) * acc[1] : 0.f;
+      const float p2 = i0 + 2 <= t ? __builtin_amdgcn_exp2f(gt - gi.z) * acc[2] : 0.f;
+      const float p3 = i0 + 3 <= t ? __builtin_amdgcn_exp2f(gt - gi.w) * acc[3] : 0.f;
+      *reinterpret_cast<uint2*>(&sm.Pb[t][i0]) = pack_bf16x4(p0, p1, p2, p3);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- state-dependent products for this wave's 16 rows of S
     {
@@ -556,12 +581,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(
         f32x4 o = f32x4{gm * Y[tt][0], gm * Y[tt][1], gm * Y[tt][2], gm * Y[tt][3]};
         o = mfma16x16x32(Eop0, row_operand_perm(&sm.Pb[t][0], 0, g), o);
         if (tt >= 2) o = mfma16x16x32(Eop1, row_operand_perm(&sm.Pb[t][0], 32, g), o);
-        const int tok = t0 + t;
-        if (tok < T) {
-          uint16_t* dst = out + ((size_t)b * T + tok) * tok_stride + (size_t)h * D + n_w + 4 * g;
-          *reinterpret_cast<uint2*>(dst) = pack_bf16x4(o[0], o[1], o[2], o[3]);
-        }
+        const uint2 packed = pack_bf16x4(o[0], o[1], o[2], o[3]);
+        if (tt == 0) o_prev0 = packed;
+        else if (tt == 1) o_prev1 = packed;
+        else if (tt == 2) o_prev2 = packed;
+        else o_prev3 = packed;
       }
+      t0_prev = t0;
       // S <- 2^{g_C} S + K^T diag(w) E
       const float gC = sm.gam[cur][CH - 1];
       f32x4 WE[4];
@@ -580,9 +606,11 @@ __global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(
         S[dt] = s;
       }
     }
-    if (c + 1 < nchunks) scan_stage<D, NW>(pf, sm, cur ^ 1);
-    __syncthreads();
+    if (c + 1 < nchunks) scan_stage<D, NW>(pf, sm, cur ^ 1, t0 + CH, T);
+    lds_barrier();
   }
+  KAIROS_STORE_PREV();
+#undef KAIROS_STORE_PREV
 
   if (state_out) {
     float* dst = state_out + ((size_t)bh * D + n_w + l16) * D;

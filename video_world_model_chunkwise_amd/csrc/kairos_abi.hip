@@ -65,7 +65,7 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
 }
 
 struct HltaWs {
-  size_t gdn, o_gdn, q8, k8, qs, ks, total;
+  size_t gdn, o_gdn, ypart, q8, k8, qs, ks, total;
 };
 
 size_t gdn_ws_bytes(const kairos_gdn_desc* d) {
@@ -81,6 +81,8 @@ HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
   off += align_up(gdn_ws_bytes(&d->g));
   w.o_gdn = off;
   off += align_up(n * 2);
+  w.ypart = off;
+  off += align_up(n * 4);
   if (d->window_qk == KAIROS_FP8_E4M3) {
     w.q8 = off;
     off += align_up(n);
@@ -246,9 +248,11 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
 int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const void* k,
                            const void* v, const float* q_scales, const float* k_scales,
                            const void* o_gdn, const float* gate_logits, const void* k_ring,
-                           const void* v_ring, void* out, void* stream) {
+                           const void* v_ring, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   int st = check_hlta_desc(desc, true);
   if (st != KAIROS_OK) return st;
+  const size_t nws = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk * 4;
   const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!q || !k || !v || !o_gdn || !gate_logits || !out) return KAIROS_ERR_NULL;
@@ -265,8 +269,15 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
       overlaps(out, 2 * n, o_gdn, 2 * n) || overlaps(out, 2 * n, k_ring, nring) ||
       overlaps(out, 2 * n, v_ring, nring))
     return KAIROS_ERR_ALIAS;
+  if (!workspace || workspace_bytes < nws) return KAIROS_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return KAIROS_ERR_ALIGN;
+  if (overlaps(workspace, nws, out, 2 * n) || overlaps(workspace, nws, q, nqk) ||
+      overlaps(workspace, nws, k, nqk) || overlaps(workspace, nws, v, 2 * n) ||
+      overlaps(workspace, nws, o_gdn, 2 * n))
+    return KAIROS_ERR_ALIAS;
   WinArgs a;
   fill_win_args(a, desc);
+  a.ypart = (float*)workspace;
   a.q = q;
   a.k = k;
   a.v = (const uint16_t*)v;
@@ -317,6 +328,7 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   a.v_ring = (const uint16_t*)v_ring;
   a.o_gdn = o_gdn;
   a.gates = gate_logits;
+  a.ypart = (float*)(wsb + ws.ypart);
   a.out = (uint16_t*)out;
   const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
   if (fp8) {

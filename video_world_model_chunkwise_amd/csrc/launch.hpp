@@ -17,6 +17,7 @@ struct WinArgs {
   const uint16_t* v_ring;
   const uint16_t* o_gdn;    // bf16 [B][T][H][128] (hybrid only)
   const float* gates;       // logits [3][H] (hybrid only)
+  float* ypart;             // fp32 [B][T][H][128] scratch for the first branch (hybrid only)
   uint16_t* out;            // bf16 [B][T][H][128]
   int B, T, H, L, F, QT;    // F frames in the call (last may be partial), QT query tiles per frame
   int w, dil, R, nblk;

@@ -35,6 +35,11 @@
 // more than 8 (log2 units): probabilities then stay <= 2^8, which is exact
 // to rescale away at the end, and the O rescale is skipped in almost every
 // block.
+//
+// Two workgroups share a CU (two waves per SIMD), so one wave's softmax
+// arithmetic overlaps the other's matrix products.  To fit, the hybrid
+// kernel parks the finished first branch (gated, normalised, fp32) in a
+// workspace row per query and adds it back in the epilogue.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -61,8 +66,8 @@ struct KeyMap {
   int L, dil, res, R, frame_offset;
 };
 
-// Element offset of row m of the frame at sub-frame index n of the group:
-// a frame of the call, or (frames before the call) a ring slot.
+// First element of the frame at sub-frame index n of the group: a frame of
+// the call, or (frames before the call) a ring slot.
 __device__ __forceinline__ const uint8_t* frame_base(const KeyMap& km, const uint8_t* x,
                                                      const uint8_t* ring, int esz, int b, int h,
                                                      int T, int H, int n) {
@@ -72,73 +77,56 @@ __device__ __forceinline__ const uint8_t* frame_base(const KeyMap& km, const uin
   return ring + (((size_t)b * km.R + f % km.R) * km.L * (size_t)H + h) * (size_t)WD * esz;
 }
 
-// Source rows of the 64 keys of a block starting at group position pb.  For
-// L >= 64 a block spans at most two frames: positions with offset m < L come
-// from frame n0, the rest from frame n0 + 1.  Positions past p_hi are clamped
-// to p_hi (they are masked out of the softmax; clamping keeps loads in bounds
-// and the loaded values finite).
+// Rows of one 64-key block starting at group position pb (offset m0 in
+// sub-frame n0).  For L >= 64 the block spans at most two frames: offsets
+// m < L come from frame n0, the rest from frame n0 + 1.  Positions past
+// p_hi are clamped to p_hi (masked out of the softmax; clamping keeps loads
+// in bounds and loaded values finite).
 template <bool SHORTL>
-struct BlockSrc {
-  const uint8_t* base0;
-  const uint8_t* base1;
-  int m0, L, p_hi, pb;
-  size_t rstride;             // bytes between consecutive rows of a frame
-  const KeyMap* km;
-  const uint8_t* x;
-  const uint8_t* ring;
-  int esz, b, h, T, H;
-  int tok0, tok1;             // token index (in the call) of row 0 of frames n0, n0 + 1
-  // token of the key at block offset off; only for blocks without ring rows
-  __device__ __forceinline__ int token(int off) const {
-    const int p = min(pb + off, p_hi);
+struct BlockRows {
+  const uint8_t* b0;
+  const uint8_t* b1;
+  int pb, m0, n0, p_hi, L;
+  size_t rs;                  // bytes between consecutive rows of a frame
+  __device__ __forceinline__ const uint8_t* row(const KeyMap& km, const uint8_t* x,
+                                                const uint8_t* ring, int esz, int b, int h, int T,
+                                                int H, int off) const {
+    const int d = min(pb + off, p_hi) - pb;
+    const int m = m0 + d;
     if (!SHORTL) {
-      const int m = m0 + (p - pb);
       const bool second = m >= L;
-      return (second ? tok1 : tok0) + (second ? m - L : m);
+      return (second ? b1 : b0) + (size_t)(unsigned)(second ? m - L : m) * rs;
     }
-    const int n = p / L, m = p - n * L;
-    return (n * km->dil + km->res - km->frame_offset) * L + m;
+    const int n = n0 + m / L;
+    return frame_base(km, x, ring, esz, b, h, T, H, n) + (size_t)(m - (m / L) * L) * rs;
   }
-  __device__ __forceinline__ const uint8_t* row(int off) const {
-    const int p = min(pb + off, p_hi);
-    if (!SHORTL) {
-      const int m = m0 + (p - pb);
-      const bool second = m >= L;
-      const uint8_t* base = second ? base1 : base0;
-      return base + (size_t)(unsigned)(second ? m - L : m) * rstride;
-    }
-    // frames shorter than a block: walk the frames
-    const int n = p / L, m = p - n * L;
-    return frame_base(*km, x, ring, esz, b, h, T, H, n) + (size_t)m * rstride;
+  // token (in the call) of the key at block offset off; blocks without ring rows only
+  __device__ __forceinline__ int token(const KeyMap& km, int off) const {
+    const int d = min(pb + off, p_hi) - pb;
+    const int m = m0 + d;
+    const int n = n0 + m / L;
+    return (n * km.dil + km.res - km.frame_offset) * L + (m - (m / L) * L);
   }
 };
 
 template <bool SHORTL>
-__device__ __forceinline__ BlockSrc<SHORTL> block_src(const KeyMap& km, const void* x, const void* ring,
-                                                      int esz, int b, int h, int T, int H, int pb,
-                                                      int p_hi) {
-  BlockSrc<SHORTL> s;
-  const int n0 = pb / km.L;
-  s.m0 = pb - n0 * km.L;
-  s.L = km.L;
-  s.p_hi = p_hi;
-  s.pb = pb;
-  s.rstride = (size_t)H * WD * esz;
-  s.km = &km;
-  s.x = reinterpret_cast<const uint8_t*>(x);
-  s.ring = reinterpret_cast<const uint8_t*>(ring);
-  s.esz = esz;
-  s.b = b;
-  s.h = h;
-  s.T = T;
-  s.H = H;
-  s.base0 = frame_base(km, s.x, s.ring, esz, b, h, T, H, n0);
-  // the second frame is only dereferenced for positions <= p_hi, which exist
-  const int n1 = min(n0 + 1, p_hi / km.L);
-  s.base1 = frame_base(km, s.x, s.ring, esz, b, h, T, H, n1);
-  s.tok0 = (n0 * km.dil + km.res - km.frame_offset) * km.L;
-  s.tok1 = (n1 * km.dil + km.res - km.frame_offset) * km.L;
-  return s;
+__device__ __forceinline__ BlockRows<SHORTL> block_rows(const KeyMap& km, const uint8_t* x,
+                                                        const uint8_t* ring, int esz, int b, int h,
+                                                        int T, int H, int pb, int n0, int m0,
+                                                        int p_hi) {
+  BlockRows<SHORTL> r;
+  r.pb = pb;
+  r.m0 = m0;
+  r.n0 = n0;
+  r.p_hi = p_hi;
+  r.L = km.L;
+  r.rs = (size_t)H * WD * esz;
+  if (!SHORTL) {
+    r.b0 = frame_base(km, x, ring, esz, b, h, T, H, n0);
+    const int n1 = min(n0 + 1, p_hi / km.L);           // only dereferenced for positions <= p_hi
+    r.b1 = frame_base(km, x, ring, esz, b, h, T, H, n1);
+  }
+  return r;
 }
 
 // Global loads of one 64-key block into registers.
@@ -154,28 +142,33 @@ struct BlockRegs {
 
 template <bool FP8, bool SHORTL>
 __device__ __forceinline__ void win_load_block(const WinArgs& a, const KeyMap& km, int b, int h,
-                                               int pb, int p_hi, BlockRegs<FP8>& r) {
+                                               int pb, int n0, int m0, int p_hi, BlockRegs<FP8>& r) {
   const int tid = threadIdx.x;
+  const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
+  const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
+  const BlockRows<SHORTL> vr = block_rows<SHORTL>(km, vx, vring, 2, b, h, a.T, a.H, pb, n0, m0, p_hi);
   {
-    const auto vs = block_src<SHORTL>(km, a.v, a.v_ring, 2, b, h, a.T, a.H, pb, p_hi);
     const int kq8 = tid % 8, dq = tid / 8;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      r.v[j] = *reinterpret_cast<const uint2*>(vs.row(8 * kq8 + j) + 8 * dq);
+      r.v[j] = *reinterpret_cast<const uint2*>(vr.row(km, vx, vring, 2, b, h, a.T, a.H, 8 * kq8 + j) + 8 * dq);
   }
+  const uint8_t* kx = reinterpret_cast<const uint8_t*>(a.k);
   if (!FP8) {
-    const auto ks = block_src<SHORTL>(km, a.k, a.k_ring, 2, b, h, a.T, a.H, pb, p_hi);
+    const uint8_t* kring = reinterpret_cast<const uint8_t*>(a.k_ring);
+    const BlockRows<SHORTL> kr = block_rows<SHORTL>(km, kx, kring, 2, b, h, a.T, a.H, pb, n0, m0, p_hi);
     const int kq = tid / 16, dg = tid % 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.k[j] = *reinterpret_cast<const uint4*>(ks.row(4 * kq + j) + 16 * dg);
+    for (int j = 0; j < 4; ++j)
+      r.k[j] = *reinterpret_cast<const uint4*>(kr.row(km, kx, kring, 2, b, h, a.T, a.H, 4 * kq + j) + 16 * dg);
   } else {
     // E4M3 codes; FP8 calls have no ring, so rows are tokens of the call
-    const auto ks = block_src<SHORTL>(km, a.k, nullptr, 1, b, h, a.T, a.H, pb, p_hi);
+    const BlockRows<SHORTL> kr = block_rows<SHORTL>(km, kx, nullptr, 1, b, h, a.T, a.H, pb, n0, m0, p_hi);
     const int key = tid / 4, part = tid % 4;
-    const uint8_t* src = ks.row(key);
+    const uint8_t* src = kr.row(km, kx, nullptr, 1, b, h, a.T, a.H, key);
     r.k[0] = *reinterpret_cast<const uint4*>(src + 32 * part);
     r.k[1] = *reinterpret_cast<const uint4*>(src + 32 * part + 16);
-    r.sk = a.k_scales[((size_t)b * a.H + h) * a.nblk + ks.token(key) / 64];
+    r.sk = a.k_scales[((size_t)b * a.H + h) * a.nblk + kr.token(km, key) / 64];
   }
 }
 
@@ -225,16 +218,16 @@ struct BranchRange {
 __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, int f, int m_first,
                                                     int m_last) {
   BranchRange r;
-  const long f_abs = a.frame_offset + f;
+  const int f_abs = (int)a.frame_offset + f;
   r.km.L = a.L;
   r.km.dil = dil;
-  r.km.res = (int)(f_abs % dil);
+  r.km.res = f_abs % dil;
   r.km.R = a.R;
   r.km.frame_offset = (int)a.frame_offset;
-  r.pq0 = (int)(f_abs / dil) * a.L;
-  const long f_avail = a.frame_offset - a.R > 0 ? a.frame_offset - a.R : 0;
-  const long f1 = f_avail + (((r.km.res - f_avail % dil) % dil) + dil) % dil;   // first frame of the group
-  const int p_avail = (int)(f1 / dil) * a.L;
+  r.pq0 = (f_abs / dil) * a.L;
+  const int f_avail = (int)a.frame_offset - a.R > 0 ? (int)a.frame_offset - a.R : 0;
+  const int f1 = f_avail + (((r.km.res - f_avail % dil) % dil) + dil) % dil;   // first frame of the group
+  const int p_avail = (f1 / dil) * a.L;
   const int lo = r.pq0 + m_first - a.w + 1;
   r.p_lo = lo > p_avail ? lo : p_avail;
   r.p_hi = r.pq0 + m_last;
@@ -247,91 +240,36 @@ __device__ __forceinline__ constexpr int key_of(int kt, int r, int g) {
   return 32 * kt + 16 * (r / 8) + 8 * g + 4 * ((r / 4) & 1) + (r & 3);
 }
 
-template <bool FP8, bool HYBRID, bool SHORTL>
-__global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
-  __shared__ WinSmem<FP8> sm;
-  const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int qt = lid % a.QT;
-  const int f = (lid / a.QT) % a.F;
-  const int bh = lid / (a.QT * a.F);
-  const int b = bh / a.H, h = bh % a.H;
-  const int Lf = min(a.L, a.T - f * a.L);          // tokens of this frame in the call
-  const int m0 = qt * BQ;
-  if (m0 >= Lf) return;
-  const int m_last_wg = min(m0 + BQ, Lf) - 1;
+// Per-lane query state shared by the branch loops.
+struct QueryCtx {
+  int b, h, mq, mw_lo, mw_hi, krow, ql, g;
+  float cq;
+};
 
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int ql = lane % 32, g = lane / 32;
-  const int m_row = m0 + 32 * wave + ql;           // query row in the frame
-  const bool q_valid = m_row < Lf;
-  const int mq = q_valid ? m_row : m_last_wg;      // clamped row for positions / loads
-  const long tq = (long)f * a.L + mq;              // token index of the query
-  const size_t tok_stride = (size_t)a.H * WD;
-  // wave's query rows (clamped) for the block masking decision
-  const int mw_lo = min(m0 + 32 * wave, m_last_wg);
-  const int mw_hi = min(m0 + 32 * wave + 31, m_last_wg);
-  // score row of this lane's A operand: key pi(ql) of each 32-key tile
-  const int krow = 16 * (ql / 16) + 8 * ((ql / 4) & 1) + 4 * ((ql / 8) & 1) + (ql & 3);
-
-  // ---- Q operand registers (B operand of S^T = K Q^T)
-  bf16x8 qf[8];
-  i32x8 q8f[2];
-  float qscale = 1.f;
-  if (!FP8) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.T + tq) * tok_stride +
-                         (size_t)h * WD;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s + 8 * g));
-  } else {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * a.T + tq) * tok_stride +
-                        (size_t)h * WD;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g);
-      uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g + 16);
-      q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    qscale = a.q_scales[((size_t)b * a.H + h) * a.nblk + tq / 64];
-  }
-  // log2(e) / sqrt(d) (x the query's block scale): scores in exp2 units
-  const float cq = 1.4426950408889634f * 0.08838834764831845f * qscale;
-
-  // branch 0: SWA (or the single requested branch), branch 1: DSWA (hybrid only)
-  const BranchRange b0 = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
-  const BranchRange b1 = HYBRID ? branch_range(a, a.dil, f, m0, m_last_wg) : b0;
-  const int nb_total = b0.nb + (HYBRID ? b1.nb : 0);
-
-  f32x16 O[4];
-  f32x16 Y[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    O[dt] = f32x16{};
-    Y[dt] = f32x16{};
-  }
-  float m_run = -1e30f, l_run = 0.f;
-
+// One windowed branch over its key blocks: online softmax into O (unnormalised)
+// with running max m_run and lane-partial sum l_run.
+template <bool FP8, bool SHORTL>
+__device__ __forceinline__ void run_branch(const WinArgs& a, WinSmem<FP8>& sm, const BranchRange& br,
+                                           const QueryCtx& qc, const bf16x8 (&qf)[8],
+                                           const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
+                                           float& l_run) {
+  const int L = a.L;
+  int n0 = br.p_lo / L, m0 = br.p_lo - (br.p_lo / L) * L;
   BlockRegs<FP8> regs;
-  win_load_block<FP8, SHORTL>(a, b0.km, b, h, b0.p_lo, b0.p_hi, regs);
+  win_load_block<FP8, SHORTL>(a, br.km, qc.b, qc.h, br.p_lo, n0, m0, br.p_hi, regs);
   win_store_block<FP8>(sm, 0, regs);
-  __syncthreads();
-
-  for (int jb = 0; jb < nb_total; ++jb) {
+  lds_barrier();
+  const int pq = br.pq0 + qc.mq;                         // this lane's query position
+  for (int jb = 0; jb < br.nb; ++jb) {
     const int buf = jb & 1;
-    const bool in1 = HYBRID && jb >= b0.nb;          // uniform
-    const int jb_in = in1 ? jb - b0.nb : jb;
-    const int cb_nb = in1 ? b1.nb : b0.nb;
-    const int pb = (in1 ? b1.p_lo : b0.p_lo) + BK * jb_in;
-    const int pq0 = in1 ? b1.pq0 : b0.pq0;
-    // prefetch the next block (possibly the first block of branch 1)
-    const bool has_next = jb + 1 < nb_total;
-    if (has_next) {
-      const bool n1 = HYBRID && jb + 1 >= b0.nb;
-      if (n1) win_load_block<FP8, SHORTL>(a, b1.km, b, h, b1.p_lo + BK * (jb + 1 - b0.nb), b1.p_hi, regs);
-      else win_load_block<FP8, SHORTL>(a, b0.km, b, h, b0.p_lo + BK * (jb + 1), b0.p_hi, regs);
-    }
+    const int pb = br.p_lo + BK * jb;
+    // next block's (sub-frame, offset)
+    int n1 = n0, m1 = m0 + BK;
+    while (m1 >= L) { m1 -= L; ++n1; }
+    const bool has_next = jb + 1 < br.nb;
+    if (has_next) win_load_block<FP8, SHORTL>(a, br.km, qc.b, qc.h, pb + BK, n1, m1, br.p_hi, regs);
 
-    const int pq = pq0 + mq;                         // this lane's query position
-    const bool full = (pb > pq0 + mw_hi - a.w) && (pb + BK - 1 <= pq0 + mw_lo);
+    const bool full = (pb > br.pq0 + qc.mw_hi - a.w) && (pb + BK - 1 <= br.pq0 + qc.mw_lo);
 
     // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
     f32x16 S[2];
@@ -339,28 +277,29 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
     for (int kt = 0; kt < 2; ++kt) {
       S[kt] = f32x16{};
       if (!FP8) {
-        const uint16_t* Ks = reinterpret_cast<const uint16_t*>(sm.kbuf[buf]) + (32 * kt + krow) * KST;
+        const uint16_t* Ks = reinterpret_cast<const uint16_t*>(sm.kbuf[buf]) + (32 * kt + qc.krow) * KST;
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-          S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * g)), qf[s], S[kt]);
+          S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * qc.g)), qf[s], S[kt]);
       } else {
-        const uint8_t* K8 = sm.kbuf[buf] + (32 * kt + krow) * K8ST;
+        const uint8_t* K8 = sm.kbuf[buf] + (32 * kt + qc.krow) * K8ST;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          uint4 lo = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * g);
-          uint4 hi = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * g + 16);
-          i32x8 ka = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          const uint4 lo = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g);
+          const uint4 hi = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g + 16);
+          const i32x8 ka = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           S[kt] = mfma32x32x64_fp8(ka, q8f[s], S[kt]);
         }
       }
     }
-    // ---- key scales, mask, block maximum (unscaled by cq > 0)
+    // ---- key scales, mask, block maximum (before the positive factor cq)
     if (FP8) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float4 s4 = *reinterpret_cast<const float4*>(&sm.sk[buf][key_of(kt, 4 * rr, g)]);
+          const float4 s4 = *reinterpret_cast<const float4*>(&sm.sk[buf][key_of(kt, 4 * rr, qc.g)]);
           S[kt][4 * rr] *= s4.x;
           S[kt][4 * rr + 1] *= s4.y;
           S[kt][4 * rr + 2] *= s4.z;
@@ -368,20 +307,20 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
         }
     }
     if (!full) {
+      // valid iff pq - w < pk <= pq, i.e. (unsigned)(pq - pk) < w
+      const int base = pq - pb;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int pk = pb + key_of(kt, r, g);
-          if (pk > pq || pk <= pq - a.w) S[kt][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)a.w) S[kt][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cq;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qc.cq;
     if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
       const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -400,7 +339,7 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], cq, -m_run));
+        p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], qc.cq, -m_run));
         l_run += p[r];
       }
 #pragma unroll
@@ -411,54 +350,123 @@ __global__ __launch_bounds__(256) void win_attn_kernel(WinArgs a) {
     // ---- O^T += V^T P^T   (lane: O^T[32dt + 8(r/4) + 4g + r%4][query ql])
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* vrow = &sm.Vt[buf][32 * dt + ql][0];
+      const uint16_t* vrow = &sm.Vt[buf][32 * dt + qc.ql][0];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          O[dt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 32 * kt + 16 * j + 8 * g)),
+          O[dt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 32 * kt + 16 * j + 8 * qc.g)),
                                P[kt][j], O[dt]);
     }
+    if (has_next) win_store_block<FP8>(sm, buf ^ 1, regs);
+    lds_barrier();
+    n0 = n1;
+    m0 = m1;
+  }
+}
 
-    // ---- end of a branch: normalise and fold into the output accumulator
-    if (jb_in + 1 == cb_nb) {
-      const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-      const float inv = 1.f / l_tot;
-      float gsc = 1.f;
-      if (HYBRID) gsc = 1.f / (1.f + __expf(-a.gates[(in1 ? 1 : 0) * a.H + h]));
-      const float fac = gsc * inv;
+template <bool FP8, bool HYBRID, bool SHORTL>
+__global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
+  __shared__ WinSmem<FP8> sm;
+  const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int qt = lid % a.QT;
+  const int f = (lid / a.QT) % a.F;
+  const int bh = lid / (a.QT * a.F);
+  QueryCtx qc;
+  qc.b = bh / a.H;
+  qc.h = bh % a.H;
+  const int Lf = min(a.L, a.T - f * a.L);          // tokens of this frame in the call
+  const int m0 = qt * BQ;
+  if (m0 >= Lf) return;
+  const int m_last_wg = min(m0 + BQ, Lf) - 1;
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  qc.ql = lane % 32;
+  qc.g = lane / 32;
+  const int m_row = m0 + 32 * wave + qc.ql;        // query row in the frame
+  const bool q_valid = m_row < Lf;
+  qc.mq = q_valid ? m_row : m_last_wg;             // clamped row for positions / loads
+  const size_t tq = (size_t)f * a.L + qc.mq;       // token index of the query
+  const size_t tok_stride = (size_t)a.H * WD;
+  qc.mw_lo = min(m0 + 32 * wave, m_last_wg);       // wave's query rows (clamped)
+  qc.mw_hi = min(m0 + 32 * wave + 31, m_last_wg);
+  // score row of this lane's A operand: key pi(ql) of each 32-key tile
+  qc.krow = 16 * (qc.ql / 16) + 8 * ((qc.ql / 4) & 1) + 4 * ((qc.ql / 8) & 1) + (qc.ql & 3);
+  const int b = qc.b, h = qc.h, g = qc.g;
+
+  // ---- Q operand registers (B operand of S^T = K Q^T)
+  bf16x8 qf[8];
+  i32x8 q8f[2];
+  float qscale = 1.f;
+  if (!FP8) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.T + tq) * tok_stride +
+                         (size_t)h * WD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s + 8 * g));
+  } else {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * a.T + tq) * tok_stride +
+                        (size_t)h * WD;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g);
+      const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g + 16);
+      q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    qscale = a.q_scales[((size_t)b * a.H + h) * a.nblk + tq / 64];
+  }
+  // log2(e) / sqrt(d) (x the query's block scale): scores in exp2 units
+  qc.cq = 1.4426950408889634f * 0.08838834764831845f * qscale;
+
+  const size_t rowoff = ((size_t)b * a.T + tq) * tok_stride + (size_t)h * WD;
+  f32x16 O[4];
+  float m_run = -1e30f, l_run = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
+
+  // ---- first branch: SWA (or the single requested branch)
+  const BranchRange b0 = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
+  run_branch<FP8, SHORTL>(a, sm, b0, qc, qf, q8f, O, m_run, l_run);
+  float fac = 1.f / (l_run + __shfl_xor(l_run, 32, 64));
+  if (HYBRID) {
+    fac *= 1.f / (1.f + __expf(-a.gates[h]));
+    // park sig(z_swa) o_swa (fp32) in this query's workspace row
+    if (q_valid) {
+      float* yp = a.ypart + rowoff;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          Y[dt][r] += fac * O[dt][r];
-          O[dt][r] = 0.f;
-        }
-      m_run = -1e30f;
-      l_run = 0.f;
+        for (int rq = 0; rq < 4; ++rq)
+          *reinterpret_cast<float4*>(yp + 32 * dt + 8 * rq + 4 * g) =
+              make_float4(fac * O[dt][4 * rq], fac * O[dt][4 * rq + 1], fac * O[dt][4 * rq + 2],
+                          fac * O[dt][4 * rq + 3]);
     }
-
-    if (has_next) win_store_block<FP8>(sm, buf ^ 1, regs);
-    __syncthreads();
+    // ---- second branch: DSWA
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
+    m_run = -1e30f;
+    l_run = 0.f;
+    const BranchRange b1 = branch_range(a, a.dil, f, m0, m_last_wg);
+    run_branch<FP8, SHORTL>(a, sm, b1, qc, qf, q8f, O, m_run, l_run);
+    fac = 1.f / (l_run + __shfl_xor(l_run, 32, 64)) / (1.f + __expf(-a.gates[a.H + h]));
   }
 
-  // ---- epilogue: (+ gated GDN branch) -> bf16 output row of this lane's query
+  // ---- epilogue: (+ parked first branch + gated GDN branch) -> bf16 output row
   if (!q_valid) return;
-  const size_t rowoff = ((size_t)b * a.T + tq) * tok_stride + (size_t)h * WD;
-  float gg = 0.f;
-  if (HYBRID) gg = 1.f / (1.f + __expf(-a.gates[2 * a.H + h]));
+  const float gg = HYBRID ? 1.f / (1.f + __expf(-a.gates[2 * a.H + h])) : 0.f;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int d0 = 32 * dt + 8 * rq + 4 * g;
-      float y0 = Y[dt][4 * rq], y1 = Y[dt][4 * rq + 1], y2 = Y[dt][4 * rq + 2], y3 = Y[dt][4 * rq + 3];
+      float y0 = fac * O[dt][4 * rq], y1 = fac * O[dt][4 * rq + 1];
+      float y2 = fac * O[dt][4 * rq + 2], y3 = fac * O[dt][4 * rq + 3];
       if (HYBRID) {
+        const float4 yp = *reinterpret_cast<const float4*>(a.ypart + rowoff + d0);
         const uint2 og = *reinterpret_cast<const uint2*>(a.o_gdn + rowoff + d0);
-        y0 += gg * bf16_to_f32(lo16w(og.x));
-        y1 += gg * bf16_to_f32(hi16w(og.x));
-        y2 += gg * bf16_to_f32(lo16w(og.y));
-        y3 += gg * bf16_to_f32(hi16w(og.y));
+        y0 += yp.x + gg * bf16_to_f32(lo16w(og.x));
+        y1 += yp.y + gg * bf16_to_f32(hi16w(og.x));
+        y2 += yp.z + gg * bf16_to_f32(lo16w(og.y));
+        y3 += yp.w + gg * bf16_to_f32(hi16w(og.y));
       }
       *reinterpret_cast<uint2*>(a.out + rowoff + d0) = pack_bf16x4(y0, y1, y2, y3);
     }
@@ -470,6 +478,7 @@ hipError_t launch_window(const WinArgs& args_in, bool fp8, bool hybrid, hipStrea
   const long nwg = (long)a.B * a.H * a.F * a.QT;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (hybrid && !a.ypart) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
   const bool shortl = a.L < BK;
 #define KAIROS_WIN_LAUNCH(F8, HY, SL) win_attn_kernel<F8, HY, SL><<<grid, 256, 0, stream>>>(a)
