@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--quick", action="store_true", help="skip the per-workload breakdown")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for memory counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -224,12 +226,17 @@ def main():
                 "kernel": "win_attn_kernel<fp8, hybrid>",
                 "algorithmic_flops_per_launch": win_flops,
                 "avg_launch_ms": round(t_win, 4)}
-    cpath = os.path.join(ROOT, "profiles", "window_hybrid_fp8_B4H24F16L3600_counters.json")
+    # HBM traffic of the kernel from the committed counter summary, valid only
+    # while the kernel's sources are the ones the counters were taken on
+    cpath = os.path.join(ROOT, "profiles", "win_attn_fp8_hybrid_B4H24F16L3600_counters.txt")
     if os.path.exists(cpath):
-        with open(cpath) as f:
-            cnt = json.load(f)
-        if cnt.get("source_sha") == src_sha("window_attn.hip", "common.hpp"):
-            roofline["traffic"] = cnt.get("traffic_bytes_per_launch")
+        cnt = {}
+        for line in open(cpath):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                cnt[key.strip()] = val.strip()
+        if cnt.get("source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
+            roofline["traffic"] = float(cnt["traffic_bytes_per_launch"])
 
     gdn_tok_heads = w.B * w.T * w.H
     gdn_bytes = gdn_tok_heads * GDN_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * w.d * w.d * 4
@@ -251,6 +258,12 @@ def main():
 
     if not args.quick:
         breakdown.update(workload_breakdown(K, torch, WORKLOADS, make_device_inputs, reps))
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,0 +1,169 @@
+"""The C ABI on the host, without a GPU: the library loads, exports every
+symbol include/kairos.h declares, sizes workspaces, and rejects invalid calls
+with the documented status before anything is enqueued (only validation
+paths are exercised here; no pointer passed below is ever dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_world_model_chunkwise_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, WS = 0, -1, -2, -3, -4, -5, -6, -7
+
+pytestmark = pytest.mark.skipif(not os.path.exists(K.lib_path), reason="libkairos.so not built")
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0      # counts devices without initialising them
+
+
+# The calls below pass fake addresses and rely on being rejected before any
+# launch; they never run where a GPU is visible, so a regression in a check
+# cannot turn into a launch with fake pointers.
+host_only = pytest.mark.skipif(_gpu_visible(), reason="host-only validation tests")
+
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "kairos.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(kairos_\w+)\s*\(", header, re.M))
+    assert declared == set(K.symbols)
+    lib = ctypes.CDLL(K.lib_path)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    assert K.version() == 100
+    assert K.status_string(0) == "ok"
+    assert "align" in K.status_string(ALIGN)
+    assert K.status_string(12345) == "unknown status"
+
+
+def test_workspace_sizes():
+    d = K.gdn_desc(4, 57600, 24, 128)
+    nchunks = 900
+    expect = ((4 * 24 * nchunks * 64 * 64 * 2 + 255) // 256) * 256 + 4 * 24 * nchunks * 64 * 4
+    assert K.kairos_gdn_workspace_size(d) == expect
+    assert K.kairos_gdn_workspace_size(K.gdn_desc(1, 64, 2, 32, io=K.F32)) == 0
+    h = K.hlta_desc(4, 57600, 24, 128, 3600, 3600, 4, window_qk=K.FP8_E4M3)
+    n = 4 * 57600 * 24 * 128
+    assert K.kairos_hlta_workspace_size(h) >= expect + 2 * n + 4 * n + 2 * n
+    assert K.kairos_hlta_ring_frames_required(K.hlta_desc(1, 1560, 24, 128, 1560, 1560, 4)) == 4
+    assert K.kairos_hlta_ring_frames_required(K.hlta_desc(1, 1560, 24, 128, 1560, 1561, 4)) == 4
+    assert K.kairos_hlta_ring_frames_required(K.hlta_desc(1, 1560, 24, 128, 1560, 1562, 4)) == 8
+    assert K.kairos_hlta_ring_frames_required(K.hlta_desc(1, 1560, 24, 128, 1560, 1, 4)) == 0
+
+
+@pytest.mark.parametrize("desc,status", [
+    (K.gdn_desc(0, 64, 2, 128), SHAPE),
+    (K.gdn_desc(1, -1, 2, 128), SHAPE),
+    (K.gdn_desc(1, 64, 2, 96), SHAPE),
+    (K.GdnDesc(1, 64, 2, 128, 64, 64, K.BF16), SHAPE),
+    (K.gdn_desc(1, 64, 2, 128, chunk=32), SHAPE),
+    (K.gdn_desc(1, 64, 2, 128, io=7), DTYPE),
+    (K.gdn_desc(1, 64, 2, 32, io=K.BF16), UNSUP),
+])
+@host_only
+def test_gdn_descriptor_errors(desc, status):
+    n = ctypes.c_size_t(0)
+    assert K.lib().kairos_gdn_workspace_size(ctypes.byref(desc), ctypes.byref(n)) == status
+    rc = K.lib().kairos_gdn_fwd(ctypes.byref(desc), *([None] * 8), None, 0, None)
+    assert rc == status
+
+
+def _gdn_call(desc, q=0x10000, k=0x20000, v=0x30000, a=0x40000, b=0x50000, s_in=None,
+              out=0x60000, s_out=None, ws=None, nws=0):
+    L = K.lib()
+    cv = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kairos_gdn_fwd(ctypes.byref(desc), cv(q), cv(k), cv(v), cv(a), cv(b), cv(s_in),
+                            cv(out), cv(s_out), cv(ws), nws, None)
+
+
+@host_only
+def test_gdn_pointer_errors():
+    d = K.gdn_desc(1, 64, 2, 128, io=K.F32)          # fp32: no workspace needed
+    assert _gdn_call(d, q=None) == NULL
+    assert _gdn_call(d, out=None) == NULL
+    assert _gdn_call(d, q=0x10008) == ALIGN           # not 16-byte aligned
+    assert _gdn_call(d, a=0x40002) == ALIGN           # not 4-byte aligned
+    nx = 64 * 2 * 128 * 4
+    assert _gdn_call(d, out=0x10000 + nx // 2) == ALIAS          # out overlaps q
+    assert _gdn_call(d, s_in=0x90000, s_out=0x90000 + 16) == ALIAS  # partial state overlap
+    db = K.gdn_desc(1, 64, 2, 128)
+    assert _gdn_call(db) == WS                        # bf16 needs a workspace
+    need = K.kairos_gdn_workspace_size(db)
+    assert _gdn_call(db, ws=0x100040, nws=need) == ALIGN        # workspace not 256-aligned
+    assert _gdn_call(db, ws=0x100000, nws=need - 1) == WS
+
+
+G = 1 << 36          # fake, never dereferenced, far-apart addresses
+
+
+def _hlta_call(desc, ws=None, nws=0, gates=6 * G, k_ring=None, v_ring=None, out=7 * G):
+    L = K.lib()
+    cv = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.kairos_hlta_fwd(ctypes.byref(desc), cv(1 * G), cv(2 * G), cv(3 * G),
+                             cv(4 * G), cv(5 * G), cv(gates), None, cv(k_ring), cv(v_ring),
+                             cv(out), None, cv(ws), nws, None)
+
+
+@host_only
+def test_hlta_validation():
+    base = dict(B=1, T=4 * 1560, H=2, d=128, L=1560, window=1560, dilation=4)
+    d = K.hlta_desc(**base)
+    assert _hlta_call(d) == WS
+    assert _hlta_call(d, gates=None) == NULL
+    assert _hlta_call(K.hlta_desc(**{**base, "d": 64})) == UNSUP
+    assert _hlta_call(K.hlta_desc(**base, io=K.F32)) == DTYPE
+    assert _hlta_call(K.hlta_desc(**{**base, "window": 0})) == SHAPE
+    assert _hlta_call(K.hlta_desc(**{**base, "dilation": 0})) == SHAPE
+    assert _hlta_call(K.hlta_desc(**base, frame_offset=-1)) == SHAPE
+    # a ring needs whole frames and enough of them, and no fp8
+    assert _hlta_call(K.hlta_desc(**{**base, "T": 1560 + 7}, ring_frames=4)) == SHAPE
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=3)) == SHAPE
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4)) == NULL          # ring pointers missing
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, window_qk=K.FP8_E4M3)) == UNSUP
+    d2 = K.hlta_desc(**base)
+    d2.reserved = 1
+    assert _hlta_call(d2) == SHAPE
+    nws = K.kairos_hlta_workspace_size(d)
+    assert _hlta_call(d, ws=8 * G, nws=nws - 256) == WS
+    # workspace overlapping the output
+    assert _hlta_call(d, ws=7 * G, nws=nws) == ALIAS
+
+
+@host_only
+def test_window_and_quantiser_validation():
+    L = K.lib()
+    d = K.hlta_desc(1, 1000, 2, 128, 100, 150, 2)
+    cv = ctypes.c_void_p
+    assert L.kairos_window_fwd(ctypes.byref(d), 0, cv(0x1000), cv(0x2000), cv(0x3000), None, None,
+                               None, None, cv(0x4000), None) == SHAPE
+    # bf16 windows take no scales
+    assert L.kairos_window_fwd(ctypes.byref(d), 2, cv(0x1000), cv(0x2000), cv(0x3000), cv(0x5000),
+                               None, None, None, cv(0x4000), None) == UNSUP
+    d8 = K.hlta_desc(1, 1000, 2, 128, 100, 150, 2, window_qk=K.FP8_E4M3)
+    assert L.kairos_window_fwd(ctypes.byref(d8), 2, cv(0x1000), cv(0x2000), cv(0x3000), None, None,
+                               None, None, cv(0x4000), None) == NULL
+    assert L.kairos_hlta_window_fwd(ctypes.byref(d), cv(0x100000), cv(0x200000), cv(0x300000), None,
+                                    None, cv(0x400000), cv(0x500), None, None, cv(0x600000), None, 0,
+                                    None) == WS
+    assert L.kairos_fp8_quantize(cv(0x1000), cv(0x2000), cv(0x3000), 1, 64, 2, 96, None) == SHAPE
+    assert L.kairos_fp8_quantize(None, cv(0x2000), cv(0x3000), 1, 64, 2, 128, None) == NULL
+    assert L.kairos_fp8_quantize(cv(0x1008), cv(0x2000), cv(0x3000), 1, 64, 2, 128, None) == ALIGN
+    assert L.kairos_fp8_quantize(cv(0x1000), cv(0x1000), cv(0x9000000), 1, 64, 2, 128, None) == ALIAS
+    assert L.kairos_fp8_quantize(None, None, None, 1, 0, 2, 128, None) == OK   # empty: nothing to do
+
+
+def test_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    q = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)
+    a = torch.zeros((1, 8, 2), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        K.kairos_gdn_fwd(q, q.float(), q, a, a)
+    with pytest.raises(ValueError):
+        K.kairos_gdn_fwd(q, q, q, a[:, :4], a)

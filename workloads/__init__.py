@@ -9,15 +9,19 @@ bench) alike.
 
 Recipe (per workload index i): NumPy PCG64 seeded with ``1000 + i``; a
 SeedSequence is spawned into six child streams used in the fixed order
-q, k, v, alpha-source, beta-source, gates.  Draws are fp32 in C order
-``[B, T, H, d]``; k is L2-normalised per (token, head) in fp64 and then
-rounded; bf16 workloads round q, k, v to bf16 (round to nearest even).
+q, k, v, alpha-source, beta-source, gates.  q, k, v are standard normal fp32
+in C order ``[B, T, H, d]``, drawn in consecutive chunks of 2^22 elements,
+chunk j from child j of the tensor's stream (so chunks can be drawn in
+parallel and the result does not depend on the thread count); k is
+L2-normalised per (token, head) in fp64 and then rounded; bf16 workloads
+round q, k, v to bf16 (round to nearest even).
 alpha and beta stay fp32, shape ``[B, T, H]``; gate logits are fp32 ``[3, H]``
 in the order (swa, dswa, gdn).
 """
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -72,9 +76,13 @@ def workload(i: int) -> Workload:
 # --------------------------------------------------------------------------- bf16
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns (uint16), round to nearest even.  Inputs are finite."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even.  Inputs are
+    finite, so the 32-bit sum cannot wrap (largest pattern 0xFF7FFFFF)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
     return r.astype(np.uint16)
 
 
@@ -88,22 +96,49 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 # --------------------------------------------------------------------------- draws
 
-def _l2_normalise_rows(k: np.ndarray, block: int = 1 << 20) -> np.ndarray:
-    """Normalise the last axis to unit L2 norm in fp64, in slices to bound memory."""
+def _l2_normalise_rows(k: np.ndarray, block: int = 1 << 16) -> np.ndarray:
+    """Normalise the last axis to unit L2 norm in fp64 (in place, slices in
+    parallel); the result is rounded to fp32 once."""
+    import concurrent.futures as cf
     flat = k.reshape(-1, k.shape[-1])
-    out = np.empty_like(flat)
-    for s in range(0, flat.shape[0], block):
+
+    def norm(s):
         x = flat[s:s + block].astype(np.float64)
-        n = np.sqrt(np.sum(x * x, axis=1, keepdims=True))
-        out[s:s + block] = (x / n).astype(np.float32)
-    return out.reshape(k.shape)
+        n = np.sqrt(np.einsum("ij,ij->i", x, x))[:, None]
+        np.divide(x, n, out=x)
+        flat[s:s + block] = x
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as pool:
+        list(pool.map(norm, range(0, flat.shape[0], block)))
+    return k
 
 
-def _draw(rngs, B, T, H, d, alpha_kind, beta_kind):
-    rq, rk, rv, ra, rb, rg = rngs
-    q = rq.standard_normal((B, T, H, d), dtype=np.float32)
-    k = _l2_normalise_rows(rk.standard_normal((B, T, H, d), dtype=np.float32))
-    v = rv.standard_normal((B, T, H, d), dtype=np.float32)
+_CHUNK = 1 << 22
+
+
+def _normal_chunked(ss: np.random.SeedSequence, shape, pool) -> np.ndarray:
+    """Standard normal fp32 array; chunk j drawn from child j of ss."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    nchunks = max(1, -(-n // _CHUNK))
+    children = ss.spawn(nchunks)
+
+    def fill(j):
+        g = np.random.Generator(np.random.PCG64(children[j]))
+        s0 = j * _CHUNK
+        out[s0:min(n, s0 + _CHUNK)] = g.standard_normal(min(n, s0 + _CHUNK) - s0, dtype=np.float32)
+    list(pool.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def _draw(seqs, B, T, H, d, alpha_kind, beta_kind):
+    import concurrent.futures as cf
+    sq, sk, sv, sa, sb, sg = seqs
+    ra, rb, rg = (np.random.Generator(np.random.PCG64(x)) for x in (sa, sb, sg))
+    shape = (B, T, H, d)
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as pool:
+        q = _normal_chunked(sq, shape, pool)
+        k = _l2_normalise_rows(_normal_chunked(sk, shape, pool))
+        v = _normal_chunked(sv, shape, pool)
     if alpha_kind == "uniform":
         alpha = ra.uniform(0.9, 0.999, size=(B, T, H)).astype(np.float32)
     elif alpha_kind == "softplus":
@@ -130,15 +165,20 @@ def make_custom(B: int, T: int, H: int, d: int, io: str = "bf16", seed: int = 0,
     values when ``io == "bf16"``) plus ``q_bits``/``k_bits``/``v_bits`` uint16
     bf16 patterns for bf16 io.
     """
-    rngs = [np.random.Generator(np.random.PCG64(s))
-            for s in np.random.SeedSequence(seed).spawn(6)]
-    q, k, v, alpha, beta, gates = _draw(rngs, B, T, H, d, alpha_kind, beta_kind)
+    seqs = np.random.SeedSequence(seed).spawn(6)
+    q, k, v, alpha, beta, gates = _draw(seqs, B, T, H, d, alpha_kind, beta_kind)
     out = dict(alpha=alpha, beta=beta, gates=gates)
     if io == "bf16":
-        for name, x in (("q", q), ("k", k), ("v", v)):
+        import concurrent.futures as cf
+
+        def conv(x):
             bits = to_bf16_bits(x)
+            return bits, bf16_bits_to_f32(bits)
+        with cf.ThreadPoolExecutor(3) as ex:
+            res = list(ex.map(conv, (q, k, v)))
+        for name, (bits, vals) in zip(("q", "k", "v"), res):
             out[name + "_bits"] = bits
-            out[name] = bf16_bits_to_f32(bits)
+            out[name] = vals
     elif io == "f32":
         out.update(q=q, k=k, v=v)
     else:
