@@ -228,15 +228,15 @@ def main():
                 "avg_launch_ms": round(t_win, 4)}
     # HBM traffic of the kernel from the committed counter summary, valid only
     # while the kernel's sources are the ones the counters were taken on
-    cpath = os.path.join(ROOT, "profiles", "win_attn_fp8_hybrid_B4H24F16L3600_counters.txt")
-    if os.path.exists(cpath):
+    cpath = os.path.join(ROOT, "profiles", "hlta_fp8_B4H24F16L3600_hbm_counters.txt")
+    if fp8 and os.path.exists(cpath):
         cnt = {}
         for line in open(cpath):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 cnt[key.strip()] = val.strip()
-        if cnt.get("source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
-            roofline["traffic"] = float(cnt["traffic_bytes_per_launch"])
+        if cnt.get("win_attn_kernel.source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
+            roofline["traffic"] = float(cnt["win_attn_kernel.traffic_bytes_per_launch"])
 
     gdn_tok_heads = w.B * w.T * w.H
     gdn_bytes = gdn_tok_heads * GDN_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * w.d * w.d * 4
