@@ -27,6 +27,12 @@ CFLAGS = [
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 
+# per-source options: the gated delta rule keeps every MFMA result in
+# architectural VGPRs (its chained products feed VALU work directly)
+EXTRA = {
+    "gdn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
@@ -52,7 +58,7 @@ def build(verbose: bool = False) -> str:
             for src in SOURCES:
                 obj = os.path.join(tmp, src.replace(".hip", ".o"))
                 objs.append(obj)
-                cmd = [hipcc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+                cmd = [hipcc, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
                 jobs.append(ex.submit(_run, cmd))
             for j in jobs:
                 out = j.result()

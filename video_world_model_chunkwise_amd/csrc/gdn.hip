@@ -301,322 +301,452 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const uint16_t* __restric
 
 // ---- scan: per (b, h, 16*NW rows of S), chunks in order
 //
-// Staging maps (token quad, feature group) to lanes so that global loads read
-// >= 32 contiguous bytes per row while the transposed LDS writes of one
-// 32-lane phase land on distinct banks: 4 consecutive lanes share a row,
-// 16 rows per wave, and the wave index selects the next feature groups.
-__device__ __forceinline__ int kq_dgroup(int u) { return 4 * (u / 64) + (u % 4); }
-__device__ __forceinline__ int kq_tquad(int u) { return (u % 64) / 4; }
-template <int D, int NW>
-struct ScanSmem {
-  static constexpr int NR = 16 * NW;
-  uint16_t Ks[2][CH][D + KS_PAD];     // K chunk, token-major
-  uint16_t Qs[2][CH][D + KS_PAD];     // Q chunk, token-major
-  uint16_t Kt[2][D][TS];              // K chunk, feature-major
-  uint16_t Vt[2][NR][TS];             // V chunk (owned rows), feature-major
-  uint16_t Tb[2][CH][TS];             // T = (I + A)^{-1}
-  float g2[2][CH];                    // g_t (log2 units)
-  float gam[2][CH];                   // 2^{g_t}
-  float wts[2][CH];                   // 2^{g_C - g_t}
-  float bet[2][CH];                   // b_t
-  uint16_t Pb[CH][TS];                // P = lower(2^{dg} Q K^T)
-};
+// Token order inside LDS.  The products that chain through registers need
+// their reduction slots in natural token order: the C registers of 16x16
+// tiles 2p and 2p+1 form one operand whose slot 8g + i is token 32p + 8g + i
+// when tile 2p row 4g + r holds token 32p + 8g + r and tile 2p+1 row 4g + r
+// holds token 32p + 8g + 4 + r.  Every token-major tile (K, Q, V, T, P) is
+// therefore staged with token t = 32p + 8g + 4h + r in LDS row
+// 32p + 16h + 4g + r, so that the rows of every 16x16 tile are 16
+// consecutive LDS rows and each transposed read takes 4 consecutive rows.
+//
+// State layout: wave w owns rows n_w .. n_w + 15 of S.  S[dt] is a C tile
+// whose row 4g + r holds feature (column of S) cb(dt, g) + r with
+// cb(2s, g) = 32s + 8g and cb(2s + 1, g) = 32s + 8g + 4, and whose column is
+// row n_w + l16 of S; the pair (S[2s], S[2s+1]) is then an operand over 32
+// consecutive features in natural order, matching 16-byte reads of K and Q.
+//
+// Staging: the next chunk's tiles go from HBM straight into the other LDS
+// buffer (buffer loads with the LDS flag: lane l of a load writes 16 bytes at
+// the load's LDS base + 16 l), so staging costs neither registers nor LDS
+// write instructions.  Each buffer is a separate LDS variable so that the
+// compiler can tell the in-flight loads from the reads of the current chunk.
+// LDS row strides are 16 mod 32 bf16 elements: 16-byte operand reads and
+// transposed reads of a 16-row tile then touch distinct banks; padding
+// units are filled with copies of real units.
+__device__ __forceinline__ int lds_row(int t) {       // token -> LDS row
+  return (t & ~31) | ((t & 4) << 2) | ((t & 24) >> 1) | (t & 3);
+}
+__device__ __forceinline__ int row_token(int row) {   // LDS row -> token
+  return (row & ~31) | ((row & 16) >> 2) | ((row & 12) << 1) | (row & 3);
+}
+__device__ __forceinline__ int s_feature(int dt, int g) {   // cb(dt, g)
+  return 32 * (dt / 2) + 8 * g + 4 * (dt % 2);
+}
 
-template <int D, int NW>
-struct ScanPrefetch {
-  static constexpr int NQUADS = (CH / 4) * (D / 8);                 // 4-token x 8-feature quads
-  static constexpr int KQ_PASSES = (NQUADS + 64 * NW - 1) / (64 * NW);
-  static constexpr int T_UNITS = CH * CH / 8;                       // 16-byte units of T
-  static constexpr int T_PASSES = (T_UNITS + 64 * NW - 1) / (64 * NW);
-  uint4 k[KQ_PASSES][4];
-  uint4 q[KQ_PASSES][4];
-  uint2 v[4];
-  uint4 t[T_PASSES];
-  float g, b;
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int NW>
-__device__ __forceinline__ void scan_fetch(ScanPrefetch<D, NW>& pf, const uint16_t* __restrict__ q,
-                                           const uint16_t* __restrict__ k,
-                                           const uint16_t* __restrict__ v,
-                                           const float* __restrict__ beta,
-                                           const uint16_t* __restrict__ t_in,
-                                           const float* __restrict__ g_in, int b, int h, int bh, int T,
-                                           int H, int c, int nchunks, int n_base) {
-  // Branch-free: rows past the sequence are clamped to its last token (real,
-  // finite data).  They need no zeroing: such tokens get b = 0 when staged, so
-  // their rows of R and E are exactly zero and they add nothing to S, and
-  // T = (I + A)^{-1} is the identity on them; their outputs are not stored.
-  // Without branches the memory counters stay exact, so waits never drain
-  // unrelated stores.
-  const int tid = threadIdx.x;
-  constexpr int DG = D / 8;
-  const int t0 = c * CH;
-  const size_t tok_stride = (size_t)H * D;
-  const size_t base = ((size_t)b * T * H + h) * D;
-#pragma unroll
-  for (int p = 0; p < ScanPrefetch<D, NW>::KQ_PASSES; ++p) {
-    const int u = min(tid + p * 64 * NW, ScanPrefetch<D, NW>::NQUADS - 1);
-    const int dg = kq_dgroup(u), tq = kq_tquad(u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = min(t0 + 4 * tq + j, T - 1);
-      const size_t off = base + (size_t)t * tok_stride + 8 * dg;
-      pf.k[p][j] = *reinterpret_cast<const uint4*>(k + off);
-      pf.q[p][j] = *reinterpret_cast<const uint4*>(q + off);
-    }
-  }
-  {
-    const int nq = kq_dgroup(tid), tq = kq_tquad(tid);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = min(t0 + 4 * tq + j, T - 1);
-      pf.v[j] = *reinterpret_cast<const uint2*>(v + base + (size_t)t * tok_stride + n_base + 4 * nq);
-    }
-  }
-  const uint16_t* tsrc = t_in + ((size_t)bh * nchunks + c) * CH * CH;
-#pragma unroll
-  for (int p = 0; p < ScanPrefetch<D, NW>::T_PASSES; ++p) {
-    const int u = min(tid + p * 64 * NW, ScanPrefetch<D, NW>::T_UNITS - 1);
-    pf.t[p] = *reinterpret_cast<const uint4*>(tsrc + 8 * u);
-  }
-  const int lt = tid % 64;
-  pf.g = g_in[((size_t)bh * nchunks + c) * CH + lt];
-  pf.b = beta[((size_t)b * T + min(t0 + lt, T - 1)) * H + h];
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
+// 4j + i/4, j = 0..3.  With lane s addressing row k0 + s/4, columns
+// c(s % 4) .. c(s % 4) + 3, lane i receives column c(i/4) + i%4 of rows
+// k0 .. k0 + 3.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Raw buffer descriptor: loads at byte offsets >= nbytes return zero and
+// stores there are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void buf_to_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(uint2 x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// bytes from a chunk's first token to the end of its last valid token row
+__device__ __forceinline__ uint32_t chunk_bytes(int T, int c, uint32_t tok_bytes, int D) {
+  const int valid = min(CH, T - c * CH);
+  return (uint32_t)(valid - 1) * tok_bytes + (uint32_t)D * 2;
 }
 
 template <int D, int NW>
-__device__ __forceinline__ void scan_stage(const ScanPrefetch<D, NW>& pf, ScanSmem<D, NW>& sm, int buf,
-                                           int t0, int T) {
-  const int tid = threadIdx.x;
-  constexpr int DG = D / 8;
-#pragma unroll
-  for (int p = 0; p < ScanPrefetch<D, NW>::KQ_PASSES; ++p) {
-    const int u = tid + p * 64 * NW;
-    if (u >= ScanPrefetch<D, NW>::NQUADS) break;
-    const int dg = kq_dgroup(u), tq = kq_tquad(u);
-    const uint4* kk = pf.k[p];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<uint4*>(&sm.Ks[buf][4 * tq + j][8 * dg]) = pf.k[p][j];
-      *reinterpret_cast<uint4*>(&sm.Qs[buf][4 * tq + j][8 * dg]) = pf.q[p][j];
-    }
-    // transpose the 4 tokens x 8 features block into Kt[d][t..t+3]
-    const uint32_t w0[4] = {kk[0].x, kk[0].y, kk[0].z, kk[0].w};
-    const uint32_t w1[4] = {kk[1].x, kk[1].y, kk[1].z, kk[1].w};
-    const uint32_t w2[4] = {kk[2].x, kk[2].y, kk[2].z, kk[2].w};
-    const uint32_t w3[4] = {kk[3].x, kk[3].y, kk[3].z, kk[3].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint2 even = make_uint2(lo16(w0[e]) | (lo16(w1[e]) << 16), lo16(w2[e]) | (lo16(w3[e]) << 16));
-      const uint2 odd = make_uint2(hi16(w0[e]) | (hi16(w1[e]) << 16), hi16(w2[e]) | (hi16(w3[e]) << 16));
-      *reinterpret_cast<uint2*>(&sm.Kt[buf][8 * dg + 2 * e][4 * tq]) = even;
-      *reinterpret_cast<uint2*>(&sm.Kt[buf][8 * dg + 2 * e + 1][4 * tq]) = odd;
-    }
-  }
-  {
-    const int nq = kq_dgroup(tid), tq = kq_tquad(tid);
-    const uint2* vv = pf.v;
-    const uint32_t a0 = vv[0].x, a1 = vv[0].y, b0 = vv[1].x, b1 = vv[1].y;
-    const uint32_t c0 = vv[2].x, c1 = vv[2].y, d0 = vv[3].x, d1 = vv[3].y;
-    *reinterpret_cast<uint2*>(&sm.Vt[buf][4 * nq + 0][4 * tq]) =
-        make_uint2(lo16(a0) | (lo16(b0) << 16), lo16(c0) | (lo16(d0) << 16));
-    *reinterpret_cast<uint2*>(&sm.Vt[buf][4 * nq + 1][4 * tq]) =
-        make_uint2(hi16(a0) | (hi16(b0) << 16), hi16(c0) | (hi16(d0) << 16));
-    *reinterpret_cast<uint2*>(&sm.Vt[buf][4 * nq + 2][4 * tq]) =
-        make_uint2(lo16(a1) | (lo16(b1) << 16), lo16(c1) | (lo16(d1) << 16));
-    *reinterpret_cast<uint2*>(&sm.Vt[buf][4 * nq + 3][4 * tq]) =
-        make_uint2(hi16(a1) | (hi16(b1) << 16), hi16(c1) | (hi16(d1) << 16));
-  }
-#pragma unroll
-  for (int p = 0; p < ScanPrefetch<D, NW>::T_PASSES; ++p) {
-    const int u = tid + p * 64 * NW;
-    if (u < ScanPrefetch<D, NW>::T_UNITS)
-      *reinterpret_cast<uint4*>(&sm.Tb[buf][u / 8][8 * (u % 8)]) = pf.t[p];
-  }
-  if (tid < 64) {
-    const float gl = __shfl(pf.g, 63, 64);
-    sm.g2[buf][tid] = pf.g;
-    sm.gam[buf][tid] = __builtin_amdgcn_exp2f(pf.g);
-    sm.wts[buf][tid] = __builtin_amdgcn_exp2f(gl - pf.g);
-    sm.bet[buf][tid] = t0 + tid < T ? pf.b : 0.f;
-  }
+struct ScanGeom {
+  static constexpr int NR = 16 * NW;                               // S rows per workgroup
+  static constexpr int KST = D + 16;                               // K, Q row stride
+  static constexpr int VST = (NR % 32 == 0) ? NR + 16 : NR + 32;   // V slice row stride
+  static constexpr int TST = CH + 16;                              // T, P row stride
+  static constexpr int KU = KST / 8, VU = VST / 8, TU = TST / 8;   // 16-byte units per row
+  // a tile of 64 rows x U units is exactly U loads of 64 lanes
+  static constexpr int KJ = (KU + NW - 1) / NW, VJ = (VU + NW - 1) / NW, TJ = (TU + NW - 1) / NW;
+};
+
+// One LDS buffer (pointers into separate __shared__ variables).
+struct ScanBuf {
+  uint16_t* K;
+  uint16_t* Q;
+  uint16_t* V;
+  uint16_t* T;
+  float* g2;    // g_t (log2 units), natural token order
+  float* gam;   // 2^{g_t}
+  float* wts;   // 2^{g_C - g_t}
+  float* bet;   // b_t (0 past the sequence)
+};
+
+// P tiles: query LDS rows 16a.., key LDS rows 16b..; the 12 tiles with
+// floor(a/2) >= floor(b/2) cover the causal part (32-token blocks).
+__device__ __forceinline__ void p_tile_of(int task, int& a, int& b) {
+  a = task < 4 ? task / 2 : 2 + (task - 4) / 4;
+  b = task < 4 ? task % 2 : (task - 4) % 4;
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(
+struct ScanCtx {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* beta;
+  const uint16_t* t_in;
+  const float* g_in;
+  uint16_t* out;
+  size_t head0;          // element offset of (b, t = 0, h)
+  size_t chunk_elems;    // elements per 64 tokens of the [B][T][H][D] tensors
+  size_t tg0;            // chunk 0 of this head in the T / g workspace (in chunks)
+  size_t beta0;          // element offset of (b, t = 0, h) in beta
+  int T, H, nchunks, n_base, wave;
+  uint32_t tok_bytes;
+  uint32_t kq_off[ScanGeom<D, NW>::KJ];
+  uint32_t v_off[ScanGeom<D, NW>::VJ];
+  uint32_t t_off[ScanGeom<D, NW>::TJ];
+  uint32_t o_off[4];
+};
+
+// Chunk c: HBM -> LDS buffer bf (all waves; wave 0 also loads g and b).
+template <int D, int NW>
+__device__ __forceinline__ void scan_issue(const ScanCtx<D, NW>& x, const ScanBuf& bf, int c) {
+  using G = ScanGeom<D, NW>;
+  const size_t e0 = x.head0 + (size_t)c * x.chunk_elems;
+  const uint32_t nrec = chunk_bytes(x.T, c, x.tok_bytes, D);
+  const auto rk = buf_rsrc(x.k + e0, nrec), rq = buf_rsrc(x.q + e0, nrec);
+  const auto rv = buf_rsrc(x.v + e0 + x.n_base, nrec);
+  const auto rt = buf_rsrc(x.t_in + (x.tg0 + c) * CH * CH, CH * CH * 2);
+#pragma unroll
+  for (int j = 0; j < G::KJ; ++j) {
+    const int m = x.wave + NW * j;
+    if (m < G::KU) {
+      buf_to_lds16(rk, bf.K + 512 * m, x.kq_off[j]);
+      buf_to_lds16(rq, bf.Q + 512 * m, x.kq_off[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G::VJ; ++j) {
+    const int m = x.wave + NW * j;
+    if (m < G::VU) buf_to_lds16(rv, bf.V + 512 * m, x.v_off[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < G::TJ; ++j) {
+    const int m = x.wave + NW * j;
+    if (m < G::TU) buf_to_lds16(rt, bf.T + 512 * m, x.t_off[j]);
+  }
+  if (x.wave == 0) {
+    const int lane = threadIdx.x % 64;
+    const int valid = min(CH, x.T - c * CH);
+    const auto rg = buf_rsrc(x.g_in + (x.tg0 + c) * CH, CH * 4);
+    const auto rb = buf_rsrc(x.beta + x.beta0 + (size_t)c * CH * x.H, (uint32_t)((valid - 1) * x.H + 1) * 4);
+    buf_to_lds4(rg, bf.g2, lane * 4);
+    buf_to_lds4(rb, bf.bet, (uint32_t)lane * x.H * 4);
+  }
+}
+
+// 2^{g} and 2^{g_C - g} of a staged chunk (wave 0, after its loads landed)
+__device__ __forceinline__ void scan_decays(const ScanBuf& bf) {
+  const int lane = threadIdx.x % 64;
+  const float gv = bf.g2[lane];
+  const float gl = bf.g2[CH - 1];
+  bf.gam[lane] = __builtin_amdgcn_exp2f(gv);
+  bf.wts[lane] = __builtin_amdgcn_exp2f(gl - gv);
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void scan_store_o(const ScanCtx<D, NW>& x, const uint2 (&o)[4], int c) {
+  const auto ro = buf_rsrc(x.out + x.head0 + (size_t)c * x.chunk_elems, chunk_bytes(x.T, c, x.tok_bytes, D));
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) buf_store8(o[tt], ro, x.o_off[tt]);
+}
+
+// One chunk: reads buffer cb, loads chunk c + 1 into buffer nb.
+template <int D, int NW>
+__device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBuf& cb, const ScanBuf& nb,
+                                           uint16_t* Pb, f32x4 (&S)[D / 16], uint2 (&o_prev)[4], int c) {
+  using G = ScanGeom<D, NW>;
+  constexpr int DT = D / 16, DS = D / 32;
+  constexpr int KST = G::KST, VST = G::VST, TST = G::TST;
+  const int lane = threadIdx.x % 64, l16 = lane % 16, g = lane / 16;
+  const int wave = x.wave;
+
+  if (c > 0) scan_store_o<D, NW>(x, o_prev, c - 1);
+
+  // Each phase first issues all of its LDS reads, then its products: the
+  // scheduling fences keep the reads ahead, so a product waits at most for
+  // its own operands instead of a full LDS round trip per product.
+  // ---- P = lower(2^{g_t - g_i} q_t . k_i), as tiles of K Q^T: lane holds
+  //      keys i0 .. i0+3 (consecutive tokens) of query t
+#pragma unroll
+  for (int j0 = 0; j0 < 12 / NW; j0 += 3) {
+    uint4 pk[3][DS], pq[3][DS];
+    float gt[3];
+    float4 gi[3];
+    int prow[3], pi0[3], pt[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      int a, bb;
+      p_tile_of(wave + NW * (j0 + j), a, bb);
+      const uint16_t* krow = cb.K + (16 * bb + l16) * KST + 8 * g;
+      const uint16_t* qrow = cb.Q + (16 * a + l16) * KST + 8 * g;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        pk[j][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
+        pq[j][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+      }
+      pt[j] = row_token(16 * a + l16);
+      pi0[j] = row_token(16 * bb + 4 * g);
+      prow[j] = 16 * a + l16;
+      gt[j] = cb.g2[pt[j]];
+      gi[j] = *reinterpret_cast<const float4*>(cb.g2 + pi0[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(pk[j][s]), as_bf16x8(pq[j][s]), acc);
+      const int t = pt[j], i0 = pi0[j];
+      const float p0 = i0 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].x) * acc[0] : 0.f;
+      const float p1 = i0 + 1 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].y) * acc[1] : 0.f;
+      const float p2 = i0 + 2 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].z) * acc[2] : 0.f;
+      const float p3 = i0 + 3 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].w) * acc[3] : 0.f;
+      *reinterpret_cast<uint2*>(Pb + prow[j] * TST + i0) = pack_bf16x4(p0, p1, p2, p3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the next chunk's loads go out after this chunk's only LDS stores, which
+  // would otherwise wait for them
+  if (c + 1 < x.nchunks) scan_issue<D, NW>(x, nb, c + 1);
+
+  // ---- state-dependent products for this wave's 16 rows of S
+  // X = K S^T (tile tt row 4g + r: token 32(tt/2) + 8g + 4(tt%2) + r, column n_w + l16)
+  // Y^T = S Q^T (row n_w + 4g + r, column: token row_token(16 tt + l16))
+  f32x4 X[4], Y[4];
+  {
+    uint4 xk[4][DS], xq[4][DS];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const uint16_t* krow = cb.K + (16 * tt + l16) * KST + 8 * g;
+      const uint16_t* qrow = cb.Q + (16 * tt + l16) * KST + 8 * g;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        xk[tt][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
+        xq[tt][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 Sop[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) Sop[s] = regs_operand(S[2 * s], S[2 * s + 1]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      X[tt] = zero4();
+      Y[tt] = zero4();
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        X[tt] = mfma16x16x32(as_bf16x8(xk[tt][s]), Sop[s], X[tt]);
+        Y[tt] = mfma16x16x32(Sop[s], as_bf16x8(xq[tt][s]), Y[tt]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // R = b (V - 2^g X);  E = T R (rows as X; T is lower triangular)
+  f32x4 E[4];
+  {
+    uint2 vv[4];
+    float4 bt[4], gm[4];
+    uint4 tr[6];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tau0 = 32 * (tt / 2) + 8 * g + 4 * (tt % 2);
+      vv[tt] = lds_read_tr(cb.V + (16 * tt + 4 * g + l16 / 4) * VST + 16 * wave + 4 * (l16 % 4));
+      bt[tt] = *reinterpret_cast<const float4*>(cb.bet + tau0);
+      gm[tt] = *reinterpret_cast<const float4*>(cb.gam + tau0);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) tr[tt] = *reinterpret_cast<const uint4*>(cb.T + (16 * tt + l16) * TST + 8 * g);
+    tr[4] = *reinterpret_cast<const uint4*>(cb.T + (32 + l16) * TST + 32 + 8 * g);
+    tr[5] = *reinterpret_cast<const uint4*>(cb.T + (48 + l16) * TST + 32 + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      X[tt][0] = bt[tt].x * (bf16_to_f32(lo16(vv[tt].x)) - gm[tt].x * X[tt][0]);
+      X[tt][1] = bt[tt].y * (bf16_to_f32(hi16(vv[tt].x)) - gm[tt].y * X[tt][1]);
+      X[tt][2] = bt[tt].z * (bf16_to_f32(lo16(vv[tt].y)) - gm[tt].z * X[tt][2]);
+      X[tt][3] = bt[tt].w * (bf16_to_f32(hi16(vv[tt].y)) - gm[tt].w * X[tt][3]);
+    }
+    const bf16x8 Rop0 = regs_operand(X[0], X[1]);
+    const bf16x8 Rop1 = regs_operand(X[2], X[3]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) E[tt] = mfma16x16x32(as_bf16x8(tr[tt]), Rop0, zero4());
+    E[2] = mfma16x16x32(as_bf16x8(tr[4]), Rop1, E[2]);
+    E[3] = mfma16x16x32(as_bf16x8(tr[5]), Rop1, E[3]);
+  }
+  lds_barrier();                      // P complete
+
+  // O^T = 2^g Y^T + E^T P^T;  S <- 2^{g_C} S + K^T diag(w) E
+  {
+    uint4 po[6];
+    float gmo[4];
+    float4 w4[4];
+    uint2 kt[DT][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      po[tt] = *reinterpret_cast<const uint4*>(Pb + (16 * tt + l16) * TST + 8 * g);
+      gmo[tt] = cb.gam[row_token(16 * tt + l16)];
+      w4[tt] = *reinterpret_cast<const float4*>(cb.wts + 32 * (tt / 2) + 8 * g + 4 * (tt % 2));
+    }
+    po[4] = *reinterpret_cast<const uint4*>(Pb + (32 + l16) * TST + 32 + 8 * g);
+    po[5] = *reinterpret_cast<const uint4*>(Pb + (48 + l16) * TST + 32 + 8 * g);
+    const float gC = cb.gam[CH - 1];
+    const uint16_t* kcol = cb.K + (4 * g + l16 / 4) * KST;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* kc = kcol + s_feature(dt, l16 % 4);
+      kt[dt][0] = lds_read_tr(kc);
+      kt[dt][1] = lds_read_tr(kc + 16 * KST);
+      kt[dt][2] = lds_read_tr(kc + 32 * KST);
+      kt[dt][3] = lds_read_tr(kc + 48 * KST);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 Eop0 = regs_operand(E[0], E[1]);
+    const bf16x8 Eop1 = regs_operand(E[2], E[3]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 o = f32x4{gmo[tt] * Y[tt][0], gmo[tt] * Y[tt][1], gmo[tt] * Y[tt][2], gmo[tt] * Y[tt][3]};
+      o = mfma16x16x32(Eop0, as_bf16x8(po[tt]), o);
+      if (tt >= 2) o = mfma16x16x32(Eop1, as_bf16x8(po[tt + 2]), o);
+      o_prev[tt] = pack_bf16x4(o[0], o[1], o[2], o[3]);
+    }
+    f32x4 WE[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      WE[tt] = f32x4{w4[tt].x * E[tt][0], w4[tt].y * E[tt][1], w4[tt].z * E[tt][2], w4[tt].w * E[tt][3]};
+    const bf16x8 WEop0 = regs_operand(WE[0], WE[1]);
+    const bf16x8 WEop1 = regs_operand(WE[2], WE[3]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 s = f32x4{gC * S[dt][0], gC * S[dt][1], gC * S[dt][2], gC * S[dt][3]};
+      s = mfma16x16x32(as_bf16x8(kt[dt][0], kt[dt][1]), WEop0, s);
+      s = mfma16x16x32(as_bf16x8(kt[dt][2], kt[dt][3]), WEop1, s);
+      S[dt] = s;
+    }
+  }
+  // the next chunk's tiles have landed (each wave waits for its own loads)
+  wait_vmem();
+  if (wave == 0 && c + 1 < x.nchunks) scan_decays(nb);
+  lds_barrier();
+}
+
+// The double-buffered LDS tiles allow one workgroup per CU: one wave per
+// SIMD, which may then hold the whole register file.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ beta, const uint16_t* __restrict__ t_in, const float* __restrict__ g_in,
     const float* state_in, uint16_t* __restrict__ out, float* state_out, int B, int T, int H) {
-  constexpr int NR = 16 * NW;
-  constexpr int NT = D / NR;          // row tiles per head
-  constexpr int DT = D / 16;          // 16-wide feature tiles
-  constexpr int DS = D / 32;          // 32-wide feature slabs
-  __shared__ ScanSmem<D, NW> sm;
+  using G = ScanGeom<D, NW>;
+  constexpr int NR = G::NR;
+  constexpr int NT = D / NR;          // workgroups per head
+  constexpr int DT = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[CH * G::KST], K1[CH * G::KST];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[CH * G::KST], Q1[CH * G::KST];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[CH * G::VST], V1[CH * G::VST];
+  __shared__ __attribute__((aligned(16))) uint16_t T0[CH * G::TST], T1[CH * G::TST];
+  __shared__ __attribute__((aligned(16))) uint16_t Pb[CH * G::TST];
+  __shared__ __attribute__((aligned(16))) float g0[CH], g1[CH], gam0[CH], gam1[CH];
+  __shared__ __attribute__((aligned(16))) float w0[CH], w1[CH], b0[CH], b1[CH];
+  const ScanBuf B0{K0, Q0, V0, T0, g0, gam0, w0, b0};
+  const ScanBuf B1{K1, Q1, V1, T1, g1, gam1, w1, b1};
 
-  const int nblocks = gridDim.x;
-  const int lid = xcd_swizzle(blockIdx.x, nblocks);
+  const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int bh = lid / NT, tile = lid % NT;
   if (bh >= B * H) return;
   const int b = bh / H, h = bh % H;
-  const int n_base = tile * NR;
 
-  const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-  const int l16 = lane % 16, g = lane / 16;
-  const int n_w = n_base + 16 * wave;     // first S row of this wave
+  const int lane = threadIdx.x % 64, l16 = lane % 16, g = lane / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
 
-  // ---- state: S^T tiles in C layout, lane holds S[n_w + l16][16 dt + 4 g + r]
+  ScanCtx<D, NW> x;
+  x.q = q; x.k = k; x.v = v; x.beta = beta; x.t_in = t_in; x.g_in = g_in; x.out = out;
+  x.T = T; x.H = H;
+  x.nchunks = (T + CH - 1) / CH;
+  x.n_base = tile * NR;
+  x.wave = wave;
+  x.tok_bytes = (uint32_t)H * D * 2;
+  x.head0 = ((size_t)b * T * H + h) * D;
+  x.chunk_elems = (size_t)CH * H * D;
+  x.tg0 = (size_t)bh * x.nchunks;
+  x.beta0 = (size_t)b * T * H + h;
+#pragma unroll
+  for (int j = 0; j < G::KJ; ++j) {
+    const int U = 64 * (wave + NW * j) + lane;
+    x.kq_off[j] = (uint32_t)row_token(U / G::KU) * x.tok_bytes + (U % G::KU) % (D / 8) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < G::VJ; ++j) {
+    const int U = 64 * (wave + NW * j) + lane;
+    x.v_off[j] = (uint32_t)row_token(U / G::VU) * x.tok_bytes + (U % G::VU) % (NR / 8) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < G::TJ; ++j) {
+    const int U = 64 * (wave + NW * j) + lane;
+    x.t_off[j] = (uint32_t)row_token(U / G::TU) * (CH * 2) + (U % G::TU) % 8 * 16;
+  }
+  const int n_w = x.n_base + 16 * wave;     // first S row of this wave
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+    x.o_off[tt] = (uint32_t)row_token(16 * tt + l16) * x.tok_bytes + (uint32_t)(n_w + 4 * g) * 2;
+
+  // ---- state tiles
   f32x4 S[DT];
   if (state_in) {
     const float* src = state_in + ((size_t)bh * D + n_w + l16) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const float4 x = *reinterpret_cast<const float4*>(src + 16 * dt + 4 * g);
-      S[dt] = f32x4{x.x, x.y, x.z, x.w};
+      const float4 s4 = *reinterpret_cast<const float4*>(src + s_feature(dt, g));
+      S[dt] = f32x4{s4.x, s4.y, s4.z, s4.w};
     }
   } else {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) S[dt] = zero4();
   }
-  for (int i = tid; i < CH * TS; i += 64 * NW) (&sm.Pb[0][0])[i] = 0;   // upper blocks stay 0
 
-  const int nchunks = (T + CH - 1) / CH;
-  ScanPrefetch<D, NW> pf;
-  if (nchunks > 0) {
-    scan_fetch<D, NW>(pf, q, k, v, beta, t_in, g_in, b, h, bh, T, H, 0, nchunks, n_base);
-    scan_stage<D, NW>(pf, sm, 0, 0, T);
+  if (x.nchunks > 0) {
+    scan_issue<D, NW>(x, B0, 0);
+    wait_vmem();
+    if (wave == 0) scan_decays(B0);
   }
   lds_barrier();
 
-  const size_t tok_stride = (size_t)H * D;
-  // outputs of the previous chunk, stored one iteration late so that their
-  // completion never sits on a chunk's critical path
-  uint2 o_prev0 = make_uint2(0, 0), o_prev1 = o_prev0, o_prev2 = o_prev0, o_prev3 = o_prev0;
-  int t0_prev = -1;
-  uint16_t* const out_bh = out + (size_t)b * T * tok_stride + (size_t)h * D + n_w + 4 * g;
-#define KAIROS_STORE_PREV()                                                              \
-  if (t0_prev >= 0) {                                                                    \
-    const int tk = t0_prev + l16;                                                        \
-    if (tk < T) *reinterpret_cast<uint2*>(out_bh + (size_t)tk * tok_stride) = o_prev0;   \
-    if (tk + 16 < T) *reinterpret_cast<uint2*>(out_bh + (size_t)(tk + 16) * tok_stride) = o_prev1; \
-    if (tk + 32 < T) *reinterpret_cast<uint2*>(out_bh + (size_t)(tk + 32) * tok_stride) = o_prev2; \
-    if (tk + 48 < T) *reinterpret_cast<uint2*>(out_bh + (size_t)(tk + 48) * tok_stride) = o_prev3; \
+  uint2 o_prev[4] = {make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0)};
+  for (int c = 0; c < x.nchunks; c += 2) {
+    scan_chunk<D, NW>(x, B0, B1, Pb, S, o_prev, c);
+    if (c + 1 < x.nchunks) scan_chunk<D, NW>(x, B1, B0, Pb, S, o_prev, c + 1);
   }
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0 = c * CH;
-    const int cur = c & 1;
-    KAIROS_STORE_PREV();
-    if (c + 1 < nchunks)
-      scan_fetch<D, NW>(pf, q, k, v, beta, t_in, g_in, b, h, bh, T, H, c + 1, nchunks, n_base);
-
-    // ---- P = lower(2^{g_t - g_i} Q K^T)
-    // (computed as the tile (tj, ti) of K Q^T: lane holds P[t = 16 ti + l16][i = 16 tj + 4 g + r],
-    //  four consecutive entries of a row of P, written as one 8-byte store)
-    for (int task = wave; task < 10; task += NW) {
-      int ti, tj;
-      tri_index(task, ti, tj);
-      const f32x4 acc = gram_tile<D>(&sm.Ks[cur][0][0], &sm.Qs[cur][0][0], D + KS_PAD, tj, ti, l16, g);
-      const int t = 16 * ti + l16;
-      const int i0 = 16 * tj + 4 * g;
-      const float gt = sm.g2[cur][t];
-      const float4 gi = *reinterpret_cast<const float4*>(&sm.g2[cur][i0]);
-      const float p0 = i0 <= t ? __builtin_amdgcn_exp2f(gt - gi.x) * acc[0] : 0.f;
-      const float p1 = i0 + 1 <= t ? __builtin_amdgcn_exp2f(gt - gi.y) * acc[1] : 0.f;
-      const float p2 = i0 + 2 <= t ? __builtin_amdgcn_exp2f(gt - gi.z) * acc[2] : 0.f;
-      const float p3 = i0 + 3 <= t ? __builtin_amdgcn_exp2f(gt - gi.w) * acc[3] : 0.f;
-      *reinterpret_cast<uint2*>(&sm.Pb[t][i0]) = pack_bf16x4(p0, p1, p2, p3);
-    }
-    lds_barrier();
-
-    // ---- state-dependent products for this wave's 16 rows of S
-    {
-      bf16x8 Sop[DS];
-#pragma unroll
-      for (int s = 0; s < DS; ++s) Sop[s] = regs_operand(S[2 * s], S[2 * s + 1]);
-
-      // X = K S^T  (lane: X[16 tt + 4g + r][n = l16]);  Y^T = S Q^T (lane: Y^T[4g + r][t = 16 tt + l16])
-      f32x4 X[4], Y[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        X[tt] = zero4();
-        Y[tt] = zero4();
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          X[tt] = mfma16x16x32(row_operand_perm(&sm.Ks[cur][16 * tt + l16][0], 32 * s, g), Sop[s], X[tt]);
-          Y[tt] = mfma16x16x32(Sop[s], row_operand_perm(&sm.Qs[cur][16 * tt + l16][0], 32 * s, g), Y[tt]);
-        }
-      }
-      // R = b (V - 2^g X)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + 4 * g;
-        const uint2 vv = *reinterpret_cast<const uint2*>(&sm.Vt[cur][16 * wave + l16][t]);
-        const float vr[4] = {bf16_to_f32(lo16(vv.x)), bf16_to_f32(hi16(vv.x)),
-                             bf16_to_f32(lo16(vv.y)), bf16_to_f32(hi16(vv.y))};
-        const float4 bt = *reinterpret_cast<const float4*>(&sm.bet[cur][t]);
-        const float4 gm = *reinterpret_cast<const float4*>(&sm.gam[cur][t]);
-        X[tt][0] = bt.x * (vr[0] - gm.x * X[tt][0]);
-        X[tt][1] = bt.y * (vr[1] - gm.y * X[tt][1]);
-        X[tt][2] = bt.z * (vr[2] - gm.z * X[tt][2]);
-        X[tt][3] = bt.w * (vr[3] - gm.w * X[tt][3]);
-      }
-      const bf16x8 Rop0 = regs_operand(X[0], X[1]);
-      const bf16x8 Rop1 = regs_operand(X[2], X[3]);
-      // E = T R  (lane: E[16 tt + 4g + r][n = l16]); T is lower triangular
-      f32x4 E[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        E[tt] = mfma16x16x32(row_operand_perm(&sm.Tb[cur][16 * tt + l16][0], 0, g), Rop0, zero4());
-        if (tt >= 2)
-          E[tt] = mfma16x16x32(row_operand_perm(&sm.Tb[cur][16 * tt + l16][0], 32, g), Rop1, E[tt]);
-      }
-      const bf16x8 Eop0 = regs_operand(E[0], E[1]);
-      const bf16x8 Eop1 = regs_operand(E[2], E[3]);
-      // O^T = 2^g Y^T + E^T P^T  (lane: O^T[n = 4g + r][t = 16 tt + l16])
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + l16;
-        const float gm = sm.gam[cur][t];
-        f32x4 o = f32x4{gm * Y[tt][0], gm * Y[tt][1], gm * Y[tt][2], gm * Y[tt][3]};
-        o = mfma16x16x32(Eop0, row_operand_perm(&sm.Pb[t][0], 0, g), o);
-        if (tt >= 2) o = mfma16x16x32(Eop1, row_operand_perm(&sm.Pb[t][0], 32, g), o);
-        const uint2 packed = pack_bf16x4(o[0], o[1], o[2], o[3]);
-        if (tt == 0) o_prev0 = packed;
-        else if (tt == 1) o_prev1 = packed;
-        else if (tt == 2) o_prev2 = packed;
-        else o_prev3 = packed;
-      }
-      t0_prev = t0;
-      // S <- 2^{g_C} S + K^T diag(w) E
-      const float gC = sm.gam[cur][CH - 1];
-      f32x4 WE[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const float4 w4 = *reinterpret_cast<const float4*>(&sm.wts[cur][16 * tt + 4 * g]);
-        WE[tt] = f32x4{w4.x * E[tt][0], w4.y * E[tt][1], w4.z * E[tt][2], w4.w * E[tt][3]};
-      }
-      const bf16x8 WEop0 = regs_operand(WE[0], WE[1]);
-      const bf16x8 WEop1 = regs_operand(WE[2], WE[3]);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 s = f32x4{gC * S[dt][0], gC * S[dt][1], gC * S[dt][2], gC * S[dt][3]};
-        s = mfma16x16x32(row_operand_perm(&sm.Kt[cur][16 * dt + l16][0], 0, g), WEop0, s);
-        s = mfma16x16x32(row_operand_perm(&sm.Kt[cur][16 * dt + l16][0], 32, g), WEop1, s);
-        S[dt] = s;
-      }
-    }
-    if (c + 1 < nchunks) scan_stage<D, NW>(pf, sm, cur ^ 1, t0 + CH, T);
-    lds_barrier();
-  }
-  KAIROS_STORE_PREV();
-#undef KAIROS_STORE_PREV
+  if (x.nchunks > 0) scan_store_o<D, NW>(x, o_prev, x.nchunks - 1);
 
   if (state_out) {
     float* dst = state_out + ((size_t)bh * D + n_w + l16) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(dst + 16 * dt + 4 * g) = make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
+      *reinterpret_cast<float4*>(dst + s_feature(dt, g)) = make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
   }
 }
 
