@@ -379,7 +379,6 @@ struct ScanGeom {
   static constexpr int TST = CH + 16;                              // T, P row stride
   static constexpr int KU = KST / 8, VU = VST / 8, TU = TST / 8;   // 16-byte units per row
   // a tile of 64 rows x U units is exactly U loads of 64 lanes
-  static constexpr int KJ = (KU + NW - 1) / NW, VJ = (VU + NW - 1) / NW, TJ = (TU + NW - 1) / NW;
 };
 
 // One LDS buffer (pointers into separate __shared__ variables).
@@ -416,46 +415,62 @@ struct ScanCtx {
   size_t beta0;          // element offset of (b, t = 0, h) in beta
   int T, H, nchunks, n_base, wave;
   uint32_t tok_bytes;
-  uint32_t kq_off[ScanGeom<D, NW>::KJ];
-  uint32_t v_off[ScanGeom<D, NW>::VJ];
-  uint32_t t_off[ScanGeom<D, NW>::TJ];
   uint32_t o_off[4];
 };
 
-// Chunk c: HBM -> LDS buffer bf (all waves; wave 0 also loads g and b).
+// Per-lane byte offsets of the loader wave's loads inside a chunk: load m of
+// a tile fills 16-byte units 64 m .. 64 m + 63 (row = unit / units per row).
+// Each of the NW loader waves issues loads m = lw, lw + NW, ... of each tile.
 template <int D, int NW>
-__device__ __forceinline__ void scan_issue(const ScanCtx<D, NW>& x, const ScanBuf& bf, int c) {
+struct ScanLoadOffs {
+  static constexpr int KJ = (ScanGeom<D, NW>::KU + NW - 1) / NW;
+  static constexpr int VJ = (ScanGeom<D, NW>::VU + NW - 1) / NW;
+  static constexpr int TJ = (ScanGeom<D, NW>::TU + NW - 1) / NW;
+  uint32_t kq[KJ];
+  uint32_t v[VJ];
+  uint32_t t[TJ];
+  int lw;            // loader index 0 .. NW-1
+};
+
+// Chunk c: HBM -> LDS buffer bf, this loader wave's share.  A wave keeps
+// only a few loads in flight, so the chunk is split over NW loader waves.
+template <int D, int NW>
+__device__ __forceinline__ void scan_issue(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
+                                           const ScanBuf& bf, int c) {
   using G = ScanGeom<D, NW>;
+  using L = ScanLoadOffs<D, NW>;
+  const int lane = threadIdx.x % 64;
   const size_t e0 = x.head0 + (size_t)c * x.chunk_elems;
   const uint32_t nrec = chunk_bytes(x.T, c, x.tok_bytes, D);
   const auto rk = buf_rsrc(x.k + e0, nrec), rq = buf_rsrc(x.q + e0, nrec);
   const auto rv = buf_rsrc(x.v + e0 + x.n_base, nrec);
   const auto rt = buf_rsrc(x.t_in + (x.tg0 + c) * CH * CH, CH * CH * 2);
-#pragma unroll
-  for (int j = 0; j < G::KJ; ++j) {
-    const int m = x.wave + NW * j;
-    if (m < G::KU) {
-      buf_to_lds16(rk, bf.K + 512 * m, x.kq_off[j]);
-      buf_to_lds16(rq, bf.Q + 512 * m, x.kq_off[j]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < G::VJ; ++j) {
-    const int m = x.wave + NW * j;
-    if (m < G::VU) buf_to_lds16(rv, bf.V + 512 * m, x.v_off[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < G::TJ; ++j) {
-    const int m = x.wave + NW * j;
-    if (m < G::TU) buf_to_lds16(rt, bf.T + 512 * m, x.t_off[j]);
-  }
-  if (x.wave == 0) {
-    const int lane = threadIdx.x % 64;
+  if (lo.lw == 0) {
     const int valid = min(CH, x.T - c * CH);
     const auto rg = buf_rsrc(x.g_in + (x.tg0 + c) * CH, CH * 4);
     const auto rb = buf_rsrc(x.beta + x.beta0 + (size_t)c * CH * x.H, (uint32_t)((valid - 1) * x.H + 1) * 4);
     buf_to_lds4(rg, bf.g2, lane * 4);
     buf_to_lds4(rb, bf.bet, (uint32_t)lane * x.H * 4);
+  }
+#pragma unroll
+  for (int j = 0; j < L::KJ; ++j) {
+    const int m = lo.lw + NW * j;
+    if (m < G::KU) buf_to_lds16(rk, bf.K + 512 * m, lo.kq[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < L::TJ; ++j) {
+    const int m = lo.lw + NW * j;
+    if (m < G::TU) buf_to_lds16(rt, bf.T + 512 * m, lo.t[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < L::VJ; ++j) {
+    const int m = lo.lw + NW * j;
+    if (m < G::VU) buf_to_lds16(rv, bf.V + 512 * m, lo.v[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < L::KJ; ++j) {
+    const int m = lo.lw + NW * j;
+    if (m < G::KU) buf_to_lds16(rq, bf.Q + 512 * m, lo.kq[j]);
   }
 }
 
@@ -475,9 +490,9 @@ __device__ __forceinline__ void scan_store_o(const ScanCtx<D, NW>& x, const uint
   for (int tt = 0; tt < 4; ++tt) buf_store8(o[tt], ro, x.o_off[tt]);
 }
 
-// One chunk: reads buffer cb, loads chunk c + 1 into buffer nb.
+// One chunk of a compute wave: reads buffer cb.
 template <int D, int NW>
-__device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBuf& cb, const ScanBuf& nb,
+__device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBuf& cb,
                                            uint16_t* Pb, f32x4 (&S)[D / 16], uint2 (&o_prev)[4], int c) {
   using G = ScanGeom<D, NW>;
   constexpr int DT = D / 16, DS = D / 32;
@@ -487,103 +502,132 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
 
   if (c > 0) scan_store_o<D, NW>(x, o_prev, c - 1);
 
-  // Each phase first issues all of its LDS reads, then its products: the
-  // scheduling fences keep the reads ahead, so a product waits at most for
-  // its own operands instead of a full LDS round trip per product.
+  // LDS reads run ahead of the products that consume them: each step issues
+  // the next step's reads before its own products (rings of two register
+  // sets), and the scheduling fences keep that order.
   // ---- P = lower(2^{g_t - g_i} q_t . k_i), as tiles of K Q^T: lane holds
   //      keys i0 .. i0+3 (consecutive tokens) of query t
-#pragma unroll
-  for (int j0 = 0; j0 < 12 / NW; j0 += 3) {
-    uint4 pk[3][DS], pq[3][DS];
-    float gt[3];
-    float4 gi[3];
-    int prow[3], pi0[3], pt[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      int a, bb;
-      p_tile_of(wave + NW * (j0 + j), a, bb);
-      const uint16_t* krow = cb.K + (16 * bb + l16) * KST + 8 * g;
-      const uint16_t* qrow = cb.Q + (16 * a + l16) * KST + 8 * g;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        pk[j][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
-        pq[j][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
-      }
-      pt[j] = row_token(16 * a + l16);
-      pi0[j] = row_token(16 * bb + 4 * g);
-      prow[j] = 16 * a + l16;
-      gt[j] = cb.g2[pt[j]];
-      gi[j] = *reinterpret_cast<const float4*>(cb.g2 + pi0[j]);
+  constexpr int NTASK = 12 / NW;
+  {
+    uint4 pk[2][DS], pq[2][DS];
+    float gt[2];
+    float4 gi[2];
+    int pt[2], pi0[2], prow[2];
+#define KAIROS_P_LOAD(j, buf)                                                              \
+    {                                                                                      \
+      int a_, b_;                                                                          \
+      p_tile_of(wave + NW * (j), a_, b_);                                                  \
+      const uint16_t* krow = cb.K + (16 * b_ + l16) * KST + 8 * g;                         \
+      const uint16_t* qrow = cb.Q + (16 * a_ + l16) * KST + 8 * g;                         \
+      _Pragma("unroll") for (int s = 0; s < DS; ++s) {                                     \
+        pk[buf][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);                       \
+        pq[buf][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);                       \
+      }                                                                                    \
+      pt[buf] = row_token(16 * a_ + l16);                                                  \
+      pi0[buf] = row_token(16 * b_ + 4 * g);                                               \
+      prow[buf] = 16 * a_ + l16;                                                           \
+      gt[buf] = cb.g2[pt[buf]];                                                            \
+      gi[buf] = *reinterpret_cast<const float4*>(cb.g2 + pi0[buf]);                        \
     }
-    __builtin_amdgcn_sched_barrier(0);
+    KAIROS_P_LOAD(0, 0);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < NTASK; ++j) {
+      const int cur_b = j & 1;
+      if (j + 1 < NTASK) KAIROS_P_LOAD(j + 1, cur_b ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 acc = zero4();
 #pragma unroll
-      for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(pk[j][s]), as_bf16x8(pq[j][s]), acc);
-      const int t = pt[j], i0 = pi0[j];
-      const float p0 = i0 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].x) * acc[0] : 0.f;
-      const float p1 = i0 + 1 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].y) * acc[1] : 0.f;
-      const float p2 = i0 + 2 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].z) * acc[2] : 0.f;
-      const float p3 = i0 + 3 <= t ? __builtin_amdgcn_exp2f(gt[j] - gi[j].w) * acc[3] : 0.f;
-      *reinterpret_cast<uint2*>(Pb + prow[j] * TST + i0) = pack_bf16x4(p0, p1, p2, p3);
+      for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(pk[cur_b][s]), as_bf16x8(pq[cur_b][s]), acc);
+      const int t = pt[cur_b], i0 = pi0[cur_b];
+      const float gtv = gt[cur_b];
+      const float4 giv = gi[cur_b];
+      const float p0 = i0 <= t ? __builtin_amdgcn_exp2f(gtv - giv.x) * acc[0] : 0.f;
+      const float p1 = i0 + 1 <= t ? __builtin_amdgcn_exp2f(gtv - giv.y) * acc[1] : 0.f;
+      const float p2 = i0 + 2 <= t ? __builtin_amdgcn_exp2f(gtv - giv.z) * acc[2] : 0.f;
+      const float p3 = i0 + 3 <= t ? __builtin_amdgcn_exp2f(gtv - giv.w) * acc[3] : 0.f;
+      *reinterpret_cast<uint2*>(Pb + prow[cur_b] * TST + i0) = pack_bf16x4(p0, p1, p2, p3);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+#undef KAIROS_P_LOAD
   }
-  // the next chunk's loads go out after this chunk's only LDS stores, which
-  // would otherwise wait for them
-  if (c + 1 < x.nchunks) scan_issue<D, NW>(x, nb, c + 1);
 
   // ---- state-dependent products for this wave's 16 rows of S
   // X = K S^T (tile tt row 4g + r: token 32(tt/2) + 8g + 4(tt%2) + r, column n_w + l16)
   // Y^T = S Q^T (row n_w + 4g + r, column: token row_token(16 tt + l16))
   f32x4 X[4], Y[4];
+  uint2 vv[4];
+  float4 bt[4], gm[4];
+  uint4 tr[6];
   {
-    uint4 xk[4][DS], xq[4][DS];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const uint16_t* krow = cb.K + (16 * tt + l16) * KST + 8 * g;
-      const uint16_t* qrow = cb.Q + (16 * tt + l16) * KST + 8 * g;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        xk[tt][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);
-        xq[tt][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
-      }
+    uint4 xk[2][DS], xq[2][DS];
+#define KAIROS_XY_LOAD(tt, buf)                                                            \
+    {                                                                                      \
+      const uint16_t* krow = cb.K + (16 * (tt) + l16) * KST + 8 * g;                       \
+      const uint16_t* qrow = cb.Q + (16 * (tt) + l16) * KST + 8 * g;                       \
+      _Pragma("unroll") for (int s = 0; s < DS; ++s) {                                     \
+        xk[buf][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);                       \
+        xq[buf][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);                       \
+      }                                                                                    \
     }
-    __builtin_amdgcn_sched_barrier(0);
+    KAIROS_XY_LOAD(0, 0);
     bf16x8 Sop[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) Sop[s] = regs_operand(S[2 * s], S[2 * s + 1]);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
+      const int cur_b = tt & 1;
+      if (tt + 1 < 4) {
+        KAIROS_XY_LOAD(tt + 1, cur_b ^ 1);
+      } else {
+        // operands of R and E
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int tau0 = 32 * (u / 2) + 8 * g + 4 * (u % 2);
+          vv[u] = lds_read_tr(cb.V + (16 * u + 4 * g + l16 / 4) * VST + 16 * wave + 4 * (l16 % 4));
+          bt[u] = *reinterpret_cast<const float4*>(cb.bet + tau0);
+          gm[u] = *reinterpret_cast<const float4*>(cb.gam + tau0);
+          tr[u] = *reinterpret_cast<const uint4*>(cb.T + (16 * u + l16) * TST + 8 * g);
+        }
+        tr[4] = *reinterpret_cast<const uint4*>(cb.T + (32 + l16) * TST + 32 + 8 * g);
+        tr[5] = *reinterpret_cast<const uint4*>(cb.T + (48 + l16) * TST + 32 + 8 * g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       X[tt] = zero4();
       Y[tt] = zero4();
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        X[tt] = mfma16x16x32(as_bf16x8(xk[tt][s]), Sop[s], X[tt]);
-        Y[tt] = mfma16x16x32(Sop[s], as_bf16x8(xq[tt][s]), Y[tt]);
+        X[tt] = mfma16x16x32(as_bf16x8(xk[cur_b][s]), Sop[s], X[tt]);
+        Y[tt] = mfma16x16x32(Sop[s], as_bf16x8(xq[cur_b][s]), Y[tt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+#undef KAIROS_XY_LOAD
   }
+  // K^T operands of the first two S-update steps and the decay weights go
+  // out before R and E
+  uint2 kt[2][4];
+  float gmo[4];
+  float4 w4[4];
+  const uint16_t* kcol = cb.K + (4 * g + l16 / 4) * KST;
+#define KAIROS_KT_LOAD(dt, buf)                                                            \
+  {                                                                                        \
+    const uint16_t* kc = kcol + s_feature(dt, l16 % 4);                                    \
+    kt[buf][0] = lds_read_tr(kc);                                                          \
+    kt[buf][1] = lds_read_tr(kc + 16 * KST);                                               \
+    kt[buf][2] = lds_read_tr(kc + 32 * KST);                                               \
+    kt[buf][3] = lds_read_tr(kc + 48 * KST);                                               \
+  }
+  KAIROS_KT_LOAD(0, 0);
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    gmo[tt] = cb.gam[row_token(16 * tt + l16)];
+    w4[tt] = *reinterpret_cast<const float4*>(cb.wts + 32 * (tt / 2) + 8 * g + 4 * (tt % 2));
+  }
+  const float gC = cb.gam[CH - 1];
+  __builtin_amdgcn_sched_barrier(0);
   // R = b (V - 2^g X);  E = T R (rows as X; T is lower triangular)
   f32x4 E[4];
   {
-    uint2 vv[4];
-    float4 bt[4], gm[4];
-    uint4 tr[6];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tau0 = 32 * (tt / 2) + 8 * g + 4 * (tt % 2);
-      vv[tt] = lds_read_tr(cb.V + (16 * tt + 4 * g + l16 / 4) * VST + 16 * wave + 4 * (l16 % 4));
-      bt[tt] = *reinterpret_cast<const float4*>(cb.bet + tau0);
-      gm[tt] = *reinterpret_cast<const float4*>(cb.gam + tau0);
-    }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) tr[tt] = *reinterpret_cast<const uint4*>(cb.T + (16 * tt + l16) * TST + 8 * g);
-    tr[4] = *reinterpret_cast<const uint4*>(cb.T + (32 + l16) * TST + 32 + 8 * g);
-    tr[5] = *reinterpret_cast<const uint4*>(cb.T + (48 + l16) * TST + 32 + 8 * g);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       X[tt][0] = bt[tt].x * (bf16_to_f32(lo16(vv[tt].x)) - gm[tt].x * X[tt][0]);
@@ -603,28 +647,18 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
   // O^T = 2^g Y^T + E^T P^T;  S <- 2^{g_C} S + K^T diag(w) E
   {
     uint4 po[6];
-    float gmo[4];
-    float4 w4[4];
-    uint2 kt[DT][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      po[tt] = *reinterpret_cast<const uint4*>(Pb + (16 * tt + l16) * TST + 8 * g);
-      gmo[tt] = cb.gam[row_token(16 * tt + l16)];
-      w4[tt] = *reinterpret_cast<const float4*>(cb.wts + 32 * (tt / 2) + 8 * g + 4 * (tt % 2));
-    }
+    for (int tt = 0; tt < 4; ++tt) po[tt] = *reinterpret_cast<const uint4*>(Pb + (16 * tt + l16) * TST + 8 * g);
     po[4] = *reinterpret_cast<const uint4*>(Pb + (32 + l16) * TST + 32 + 8 * g);
     po[5] = *reinterpret_cast<const uint4*>(Pb + (48 + l16) * TST + 32 + 8 * g);
-    const float gC = cb.gam[CH - 1];
-    const uint16_t* kcol = cb.K + (4 * g + l16 / 4) * KST;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* kc = kcol + s_feature(dt, l16 % 4);
-      kt[dt][0] = lds_read_tr(kc);
-      kt[dt][1] = lds_read_tr(kc + 16 * KST);
-      kt[dt][2] = lds_read_tr(kc + 32 * KST);
-      kt[dt][3] = lds_read_tr(kc + 48 * KST);
-    }
+    KAIROS_KT_LOAD(1, 1);
     __builtin_amdgcn_sched_barrier(0);
+    f32x4 WE[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      WE[tt] = f32x4{w4[tt].x * E[tt][0], w4[tt].y * E[tt][1], w4[tt].z * E[tt][2], w4[tt].w * E[tt][3]};
+    const bf16x8 WEop0 = regs_operand(WE[0], WE[1]);
+    const bf16x8 WEop1 = regs_operand(WE[2], WE[3]);
     const bf16x8 Eop0 = regs_operand(E[0], E[1]);
     const bf16x8 Eop1 = regs_operand(E[2], E[3]);
 #pragma unroll
@@ -634,30 +668,41 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
       if (tt >= 2) o = mfma16x16x32(Eop1, as_bf16x8(po[tt + 2]), o);
       o_prev[tt] = pack_bf16x4(o[0], o[1], o[2], o[3]);
     }
-    f32x4 WE[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      WE[tt] = f32x4{w4[tt].x * E[tt][0], w4[tt].y * E[tt][1], w4[tt].z * E[tt][2], w4[tt].w * E[tt][3]};
-    const bf16x8 WEop0 = regs_operand(WE[0], WE[1]);
-    const bf16x8 WEop1 = regs_operand(WE[2], WE[3]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      f32x4 s = f32x4{gC * S[dt][0], gC * S[dt][1], gC * S[dt][2], gC * S[dt][3]};
-      s = mfma16x16x32(as_bf16x8(kt[dt][0], kt[dt][1]), WEop0, s);
-      s = mfma16x16x32(as_bf16x8(kt[dt][2], kt[dt][3]), WEop1, s);
-      S[dt] = s;
+      const int cur_b = dt & 1;
+      // kt[cur_b] holds step dt; refill the other set with step dt + 1 once it is free
+      f32x4 sv = f32x4{gC * S[dt][0], gC * S[dt][1], gC * S[dt][2], gC * S[dt][3]};
+      sv = mfma16x16x32(as_bf16x8(kt[cur_b][0], kt[cur_b][1]), WEop0, sv);
+      sv = mfma16x16x32(as_bf16x8(kt[cur_b][2], kt[cur_b][3]), WEop1, sv);
+      S[dt] = sv;
+      if (dt + 2 < DT) KAIROS_KT_LOAD(dt + 2, cur_b);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // the next chunk's tiles have landed (each wave waits for its own loads)
+#undef KAIROS_KT_LOAD
+  lds_barrier();                      // the next chunk has landed (loader wave)
+}
+
+// Loader wave, one chunk: the next chunk's loads, then the two barriers of
+// the compute waves' chunk; the loads must have landed by the second.
+template <int D, int NW>
+__device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
+                                                const ScanBuf& nb, int c) {
+  const bool more = c + 1 < x.nchunks;
+  if (more) scan_issue<D, NW>(x, lo, nb, c + 1);
+  lds_barrier();
   wait_vmem();
-  if (wave == 0 && c + 1 < x.nchunks) scan_decays(nb);
+  if (more && lo.lw == 0) scan_decays(nb);
   lds_barrier();
 }
 
-// The double-buffered LDS tiles allow one workgroup per CU: one wave per
-// SIMD, which may then hold the whole register file.
+// Workgroup: NW compute waves (16 rows of S each) and NW loader waves that
+// stream the next chunk into the other LDS buffer (each SIMD runs one of
+// each).  The double-buffered LDS tiles allow one workgroup per CU.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void gdn_scan_kernel(
+__global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ beta, const uint16_t* __restrict__ t_in, const float* __restrict__ g_in,
     const float* state_in, uint16_t* __restrict__ out, float* state_out, int B, int T, int H) {
@@ -694,27 +739,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
   x.chunk_elems = (size_t)CH * H * D;
   x.tg0 = (size_t)bh * x.nchunks;
   x.beta0 = (size_t)b * T * H + h;
+
+  if (wave >= NW) {                   // ---- loader waves
+    using L = ScanLoadOffs<D, NW>;
+    L lo;
+    lo.lw = wave - NW;
 #pragma unroll
-  for (int j = 0; j < G::KJ; ++j) {
-    const int U = 64 * (wave + NW * j) + lane;
-    x.kq_off[j] = (uint32_t)row_token(U / G::KU) * x.tok_bytes + (U % G::KU) % (D / 8) * 16;
-  }
+    for (int j = 0; j < L::KJ; ++j) {
+      const int U = 64 * (lo.lw + NW * j) + lane;
+      lo.kq[j] = (uint32_t)row_token(U / G::KU) * x.tok_bytes + (U % G::KU) % (D / 8) * 16;
+    }
 #pragma unroll
-  for (int j = 0; j < G::VJ; ++j) {
-    const int U = 64 * (wave + NW * j) + lane;
-    x.v_off[j] = (uint32_t)row_token(U / G::VU) * x.tok_bytes + (U % G::VU) % (NR / 8) * 16;
-  }
+    for (int j = 0; j < L::VJ; ++j) {
+      const int U = 64 * (lo.lw + NW * j) + lane;
+      lo.v[j] = (uint32_t)row_token(U / G::VU) * x.tok_bytes + (U % G::VU) % (NR / 8) * 16;
+    }
 #pragma unroll
-  for (int j = 0; j < G::TJ; ++j) {
-    const int U = 64 * (wave + NW * j) + lane;
-    x.t_off[j] = (uint32_t)row_token(U / G::TU) * (CH * 2) + (U % G::TU) % 8 * 16;
+    for (int j = 0; j < L::TJ; ++j) {
+      const int U = 64 * (lo.lw + NW * j) + lane;
+      lo.t[j] = (uint32_t)row_token(U / G::TU) * (CH * 2) + (U % G::TU) % 8 * 16;
+    }
+    if (x.nchunks > 0) {
+      scan_issue<D, NW>(x, lo, B0, 0);
+      wait_vmem();
+      if (lo.lw == 0) scan_decays(B0);
+    }
+    lds_barrier();
+    for (int c = 0; c < x.nchunks; c += 2) {
+      scan_load_chunk<D, NW>(x, lo, B1, c);
+      if (c + 1 < x.nchunks) scan_load_chunk<D, NW>(x, lo, B0, c + 1);
+    }
+    return;
   }
+
+  // ---- compute waves
   const int n_w = x.n_base + 16 * wave;     // first S row of this wave
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
     x.o_off[tt] = (uint32_t)row_token(16 * tt + l16) * x.tok_bytes + (uint32_t)(n_w + 4 * g) * 2;
 
-  // ---- state tiles
   f32x4 S[DT];
   if (state_in) {
     const float* src = state_in + ((size_t)bh * D + n_w + l16) * D;
@@ -727,18 +790,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) S[dt] = zero4();
   }
-
-  if (x.nchunks > 0) {
-    scan_issue<D, NW>(x, B0, 0);
-    wait_vmem();
-    if (wave == 0) scan_decays(B0);
-  }
-  lds_barrier();
+  lds_barrier();                      // chunk 0 has landed
 
   uint2 o_prev[4] = {make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0)};
   for (int c = 0; c < x.nchunks; c += 2) {
-    scan_chunk<D, NW>(x, B0, B1, Pb, S, o_prev, c);
-    if (c + 1 < x.nchunks) scan_chunk<D, NW>(x, B1, B0, Pb, S, o_prev, c + 1);
+    scan_chunk<D, NW>(x, B0, Pb, S, o_prev, c);
+    if (c + 1 < x.nchunks) scan_chunk<D, NW>(x, B1, Pb, S, o_prev, c + 1);
   }
   if (x.nchunks > 0) scan_store_o<D, NW>(x, o_prev, x.nchunks - 1);
 
@@ -787,7 +844,7 @@ static hipError_t launch_scan(const uint16_t* q, const uint16_t* k, const uint16
                               int H, hipStream_t stream) {
   constexpr int NT = D / (16 * NW);
   const int nblk = B * H * NT;
-  gdn_scan_kernel<D, NW><<<nblk, 64 * NW, 0, stream>>>(q, k, v, beta, t_ws, g_ws, state_in, out,
+  gdn_scan_kernel<D, NW><<<nblk, 128 * NW, 0, stream>>>(q, k, v, beta, t_ws, g_ws, state_in, out,
                                                        state_out, B, T, H);
   return hipGetLastError();
 }
