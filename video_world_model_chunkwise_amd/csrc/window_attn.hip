@@ -15,21 +15,22 @@
 // Work decomposition: one workgroup (4 waves) per (batch, head, frame,
 // 128-query tile); query tiles never straddle a frame, so each tile has one
 // contiguous key range per branch in group-position space.  Keys are walked
-// in blocks of 64 positions; each block's K and V rows are gathered (rows of
-// one block may come from two frames, or from the ring of a streamed
-// rollout) into double-buffered LDS, K token-major and V feature-major.
-// Each wave owns 32 queries: S^T = K Q^T on 32x32 matrix-core tiles with Q
-// held in registers, an online softmax in exp2 form (one query per lane, the
-// row reduction is within the lane plus one exchange with lane ^ 32), then
-// O^T += V^T P^T with P taken straight from the score registers.  With FP8
-// Q/K the score product uses the 32x32x64 E4M3 instruction and the per-64-
-// token-block scales multiply the fp32 scores; P V stays bf16.
+// in blocks of 64 positions; each block's K and V rows (rows of one block may
+// come from two frames, or from the ring of a streamed rollout) go from
+// global memory straight into double-buffered LDS, token-major, each lane of
+// a load writing 16 bytes of one row.  Each wave owns 32 queries:
+// S^T = K Q^T on 32x32 matrix-core tiles with Q held in registers, an online
+// softmax in exp2 form (one query per lane, the row reduction is within the
+// lane plus one exchange with lane ^ 32), then O^T += V^T P^T with P taken
+// straight from the score registers and the V^T operands read with the
+// transposing LDS read.  With FP8 Q/K the score product uses the 32x32x64
+// E4M3 instruction and the per-64-token-block scales multiply the fp32
+// scores; P V stays bf16.
 //
 // Key order inside a 32-key tile: the score tile's row r maps to key
 // pi(r) = 16 j + 8 g + 4 h + i for r = 16 j + 8 h + 4 g + i (bits g and h
 // swapped).  With that order the 8 score registers a lane feeds into one
-// P V product step are 8 consecutive keys, so each V^T operand is a single
-// 16-byte LDS read.
+// P V product step are 8 consecutive keys.
 //
 // The running maximum is only raised when a block's maximum exceeds it by
 // more than 8 (log2 units): probabilities then stay <= 2^8, which is exact
@@ -48,17 +49,40 @@ namespace kairos {
 constexpr int WD = 128;          // head dimension
 constexpr int BQ = 128;          // queries per workgroup
 constexpr int BK = 64;           // keys per block
-constexpr int KST = WD + 8;      // Ks row stride (bf16 elements)
-constexpr int K8ST = WD + 16;    // K8s row stride (bytes)
-constexpr int VST = BK + 8;      // Vt row stride (bf16 elements)
+constexpr int KST = WD + 16;     // bf16 K and V LDS row stride (elements): 16 mod 32
+constexpr int K8ST = WD + 16;    // E4M3 K LDS row stride (bytes)
 constexpr float RESCALE_SLACK = 8.f;
 
+typedef short wshort4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void wlds_void;
+
+// Transposed LDS read of 16-bit elements (see the lane map in the gated
+// delta rule scan): lane i of a 16-lane group gets column c(i/4) + i%4 of
+// rows k0..k0+3 when lane s addresses row k0 + s/4, columns c(s%4)...
+__device__ __forceinline__ uint2 win_read_tr(const uint16_t* p) {
+  const wshort4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((wshort4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+__device__ __forceinline__ void to_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (wlds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void to_lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (wlds_void*)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void win_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// LDS layout of one key block: K rows (E4M3: 128 bytes + 16 padding; bf16:
+// 256 + 32), V rows (256 + 32 bytes), fp32 key scales (E4M3 only).  A block
+// of U 16-byte units per row is U loads of 64 lanes (lane l of load m fills
+// unit 64 m + l).
 template <bool FP8>
-struct WinSmem {
-  static constexpr int KBYTES = FP8 ? BK * K8ST : BK * KST * 2;
-  uint8_t kbuf[2][KBYTES];
-  uint16_t Vt[2][WD][VST];
-  float sk[2][BK];
+struct WinGeom {
+  static constexpr int KU = FP8 ? K8ST / 16 : KST * 2 / 16;   // units per K row (9 / 18)
+  static constexpr int VU = KST * 2 / 16;                     // units per V row (18)
+  static constexpr int KBYTES = BK * KU * 16;
+  static constexpr int VBYTES = BK * VU * 16;
+  static constexpr int NLOAD = KU + VU + (FP8 ? 1 : 0);       // loads per block (all waves)
+  static constexpr int NJ = (NLOAD + 3) / 4;                  // loads per wave
 };
 
 // Position -> source row map of one branch for one workgroup.
@@ -75,137 +99,6 @@ __device__ __forceinline__ const uint8_t* frame_base(const KeyMap& km, const uin
   if (f >= km.frame_offset)
     return x + (((size_t)b * T + (size_t)(f - km.frame_offset) * km.L) * H + h) * (size_t)WD * esz;
   return ring + (((size_t)b * km.R + f % km.R) * km.L * (size_t)H + h) * (size_t)WD * esz;
-}
-
-// Rows of one 64-key block starting at group position pb (offset m0 in
-// sub-frame n0).  For L >= 64 the block spans at most two frames: offsets
-// m < L come from frame n0, the rest from frame n0 + 1.  Positions past
-// p_hi are clamped to p_hi (masked out of the softmax; clamping keeps loads
-// in bounds and loaded values finite).
-template <bool SHORTL>
-struct BlockRows {
-  const uint8_t* b0;
-  const uint8_t* b1;
-  int pb, m0, n0, p_hi, L;
-  size_t rs;                  // bytes between consecutive rows of a frame
-  __device__ __forceinline__ const uint8_t* row(const KeyMap& km, const uint8_t* x,
-                                                const uint8_t* ring, int esz, int b, int h, int T,
-                                                int H, int off) const {
-    const int d = min(pb + off, p_hi) - pb;
-    const int m = m0 + d;
-    if (!SHORTL) {
-      const bool second = m >= L;
-      return (second ? b1 : b0) + (size_t)(unsigned)(second ? m - L : m) * rs;
-    }
-    const int n = n0 + m / L;
-    return frame_base(km, x, ring, esz, b, h, T, H, n) + (size_t)(m - (m / L) * L) * rs;
-  }
-  // token (in the call) of the key at block offset off; blocks without ring rows only
-  __device__ __forceinline__ int token(const KeyMap& km, int off) const {
-    const int d = min(pb + off, p_hi) - pb;
-    const int m = m0 + d;
-    const int n = n0 + m / L;
-    return (n * km.dil + km.res - km.frame_offset) * L + (m - (m / L) * L);
-  }
-};
-
-template <bool SHORTL>
-__device__ __forceinline__ BlockRows<SHORTL> block_rows(const KeyMap& km, const uint8_t* x,
-                                                        const uint8_t* ring, int esz, int b, int h,
-                                                        int T, int H, int pb, int n0, int m0,
-                                                        int p_hi) {
-  BlockRows<SHORTL> r;
-  r.pb = pb;
-  r.m0 = m0;
-  r.n0 = n0;
-  r.p_hi = p_hi;
-  r.L = km.L;
-  r.rs = (size_t)H * WD * esz;
-  if (!SHORTL) {
-    r.b0 = frame_base(km, x, ring, esz, b, h, T, H, n0);
-    const int n1 = min(n0 + 1, p_hi / km.L);           // only dereferenced for positions <= p_hi
-    r.b1 = frame_base(km, x, ring, esz, b, h, T, H, n1);
-  }
-  return r;
-}
-
-// Global loads of one 64-key block into registers.
-//  V: thread -> keys 8*(tid%8) .. +7, features 4*(tid/8) .. +3 (8 loads of 8 bytes)
-//  bf16 K: thread -> keys 4*(tid/16) .. +3, features 8*(tid%16) .. +7 (4 loads of 16 bytes)
-//  E4M3 K: thread -> key tid/4, bytes 32*(tid%4) .. +31 (2 loads of 16 bytes) + its block scale
-template <bool FP8>
-struct BlockRegs {
-  uint2 v[8];
-  uint4 k[FP8 ? 2 : 4];
-  float sk;
-};
-
-template <bool FP8, bool SHORTL>
-__device__ __forceinline__ void win_load_block(const WinArgs& a, const KeyMap& km, int b, int h,
-                                               int pb, int n0, int m0, int p_hi, BlockRegs<FP8>& r) {
-  const int tid = threadIdx.x;
-  const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
-  const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
-  const BlockRows<SHORTL> vr = block_rows<SHORTL>(km, vx, vring, 2, b, h, a.T, a.H, pb, n0, m0, p_hi);
-  {
-    const int kq8 = tid % 8, dq = tid / 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      r.v[j] = *reinterpret_cast<const uint2*>(vr.row(km, vx, vring, 2, b, h, a.T, a.H, 8 * kq8 + j) + 8 * dq);
-  }
-  const uint8_t* kx = reinterpret_cast<const uint8_t*>(a.k);
-  if (!FP8) {
-    const uint8_t* kring = reinterpret_cast<const uint8_t*>(a.k_ring);
-    const BlockRows<SHORTL> kr = block_rows<SHORTL>(km, kx, kring, 2, b, h, a.T, a.H, pb, n0, m0, p_hi);
-    const int kq = tid / 16, dg = tid % 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      r.k[j] = *reinterpret_cast<const uint4*>(kr.row(km, kx, kring, 2, b, h, a.T, a.H, 4 * kq + j) + 16 * dg);
-  } else {
-    // E4M3 codes; FP8 calls have no ring, so rows are tokens of the call
-    const BlockRows<SHORTL> kr = block_rows<SHORTL>(km, kx, nullptr, 1, b, h, a.T, a.H, pb, n0, m0, p_hi);
-    const int key = tid / 4, part = tid % 4;
-    const uint8_t* src = kr.row(km, kx, nullptr, 1, b, h, a.T, a.H, key);
-    r.k[0] = *reinterpret_cast<const uint4*>(src + 32 * part);
-    r.k[1] = *reinterpret_cast<const uint4*>(src + 32 * part + 16);
-    r.sk = a.k_scales[((size_t)b * a.H + h) * a.nblk + kr.token(km, key) / 64];
-  }
-}
-
-__device__ __forceinline__ uint32_t lo16w(uint32_t x) { return x & 0xFFFFu; }
-__device__ __forceinline__ uint32_t hi16w(uint32_t x) { return x >> 16; }
-// (low half of a, low half of b) and (high half of a, high half of b)
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-template <bool FP8>
-__device__ __forceinline__ void win_store_block(WinSmem<FP8>& sm, int buf, const BlockRegs<FP8>& r) {
-  const int tid = threadIdx.x;
-  if (!FP8) {
-    const int kq = tid / 16, dg = tid % 16;
-    uint16_t* Ks = reinterpret_cast<uint16_t*>(sm.kbuf[buf]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(Ks + (4 * kq + j) * KST + 8 * dg) = r.k[j];
-  } else {
-    const int key = tid / 4, part = tid % 4;
-    uint8_t* K8 = sm.kbuf[buf];
-    *reinterpret_cast<uint4*>(K8 + key * K8ST + 32 * part) = r.k[0];
-    *reinterpret_cast<uint4*>(K8 + key * K8ST + 32 * part + 16) = r.k[1];
-    if (part == 0) sm.sk[buf][key] = r.sk;
-  }
-  // V^T: feature row 4 dq + e gets keys 8 kq8 .. +7 (one 16-byte write per feature)
-  const int kq8 = tid % 8, dq = tid / 8;
-  uint4 w[4];
-  w[0] = make_uint4(pack_lo(r.v[0].x, r.v[1].x), pack_lo(r.v[2].x, r.v[3].x),
-                    pack_lo(r.v[4].x, r.v[5].x), pack_lo(r.v[6].x, r.v[7].x));
-  w[1] = make_uint4(pack_hi(r.v[0].x, r.v[1].x), pack_hi(r.v[2].x, r.v[3].x),
-                    pack_hi(r.v[4].x, r.v[5].x), pack_hi(r.v[6].x, r.v[7].x));
-  w[2] = make_uint4(pack_lo(r.v[0].y, r.v[1].y), pack_lo(r.v[2].y, r.v[3].y),
-                    pack_lo(r.v[4].y, r.v[5].y), pack_lo(r.v[6].y, r.v[7].y));
-  w[3] = make_uint4(pack_hi(r.v[0].y, r.v[1].y), pack_hi(r.v[2].y, r.v[3].y),
-                    pack_hi(r.v[4].y, r.v[5].y), pack_hi(r.v[6].y, r.v[7].y));
-#pragma unroll
-  for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(&sm.Vt[buf][4 * dq + e][8 * kq8]) = w[e];
 }
 
 // Key range of one branch for one query tile, in group-position space.
@@ -242,132 +135,267 @@ __device__ __forceinline__ constexpr int key_of(int kt, int r, int g) {
 
 // Per-lane query state shared by the branch loops.
 struct QueryCtx {
-  int b, h, mq, mw_lo, mw_hi, krow, ql, g;
+  int b, h, mq, mw_lo, mw_hi, krow, ql, g, wave;
   float cq;
 };
+
+// One LDS buffer of a key block (pointers into separate __shared__ variables).
+struct WinBuf {
+  uint8_t* K;
+  uint16_t* V;
+  float* sk;
+};
+
+// This wave's share of a block's loads: entry j is load e = wave + 4 j of
+// the block (K loads, then V loads, then the E4M3 scales); per lane the key
+// row and byte offset inside the row, and the source address.
+template <bool FP8>
+struct WinLoads {
+  const uint8_t* src[WinGeom<FP8>::NJ];
+  int row[WinGeom<FP8>::NJ];
+  int col[WinGeom<FP8>::NJ];
+  uint32_t inc[WinGeom<FP8>::NJ];   // source step of a block inside one frame (64 rows)
+};
+
+template <bool FP8>
+__device__ __forceinline__ void win_load_setup(WinLoads<FP8>& ld, int wave, int H) {
+  using G = WinGeom<FP8>;
+  const int lane = threadIdx.x % 64;
+#pragma unroll
+  for (int j = 0; j < G::NJ; ++j) {
+    const int e = wave + 4 * j;
+    ld.inc[j] = e < G::KU ? (uint32_t)BK * H * WD * (FP8 ? 1 : 2)
+              : e < G::KU + G::VU ? (uint32_t)BK * H * WD * 2 : 4u;    // scales: next 64-token block
+  }
+#pragma unroll
+  for (int j = 0; j < G::NJ; ++j) {
+    const int e = wave + 4 * j;
+    int U, upr;
+    if (e < G::KU) { U = 64 * e + lane; upr = G::KU; }
+    else if (e < G::KU + G::VU) { U = 64 * (e - G::KU) + lane; upr = G::VU; }
+    else { U = lane; upr = 1; }                      // scales: one per key
+    ld.row[j] = U / upr;
+    const int u = U % upr;
+    if (e < G::KU) ld.col[j] = FP8 ? (u % 8) * 16 : (u % 16) * 16;     // padding units copy a real unit
+    else if (e < G::KU + G::VU) ld.col[j] = (u % 16) * 16;
+    else ld.col[j] = 0;
+  }
+}
+
+// Source addresses of the block at group position pb (sub-frame n0, offset
+// m0): positions past p_hi clamp to p_hi (masked out; clamping keeps loads in
+// bounds and values finite).
+template <bool FP8, bool SHORTL>
+__device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs& a, const KeyMap& km,
+                                                int b, int h, int wave, int pb, int n0, int m0,
+                                                int p_hi) {
+  using G = WinGeom<FP8>;
+  constexpr int KESZ = FP8 ? 1 : 2;
+  const uint8_t* kx = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* kring = reinterpret_cast<const uint8_t*>(a.k_ring);
+  const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
+  const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
+  const int L = km.L;
+  const size_t rs_k = (size_t)a.H * WD * KESZ, rs_v = (size_t)a.H * WD * 2;
+  const uint8_t* k0 = nullptr;
+  const uint8_t* k1 = nullptr;
+  const uint8_t* v0 = nullptr;
+  const uint8_t* v1 = nullptr;
+  if (!SHORTL) {
+    const int n1 = min(n0 + 1, p_hi / L);
+    k0 = frame_base(km, kx, kring, KESZ, b, h, a.T, a.H, n0);
+    k1 = frame_base(km, kx, kring, KESZ, b, h, a.T, a.H, n1);
+    v0 = frame_base(km, vx, vring, 2, b, h, a.T, a.H, n0);
+    v1 = frame_base(km, vx, vring, 2, b, h, a.T, a.H, n1);
+  }
+#pragma unroll
+  for (int j = 0; j < G::NJ; ++j) {
+    const int e = wave + 4 * j;
+    if (e >= G::NLOAD) continue;
+    const int d = min(pb + ld.row[j], p_hi) - pb;
+    const int m = m0 + d;
+    int n, mm;
+    if (SHORTL) { n = n0 + m / L; mm = m - (m / L) * L; }
+    else { n = n0 + (m >= L ? 1 : 0); mm = m >= L ? m - L : m; }
+    if (e < G::KU) {
+      const uint8_t* base = SHORTL ? frame_base(km, kx, kring, KESZ, b, h, a.T, a.H, n) : (n == n0 ? k0 : k1);
+      ld.src[j] = base + (size_t)mm * rs_k + ld.col[j];
+    } else if (e < G::KU + G::VU) {
+      const uint8_t* base = SHORTL ? frame_base(km, vx, vring, 2, b, h, a.T, a.H, n) : (n == n0 ? v0 : v1);
+      ld.src[j] = base + (size_t)mm * rs_v + ld.col[j];
+    } else {
+      // E4M3 calls have no ring: rows are tokens of the call
+      const int tok = (n * km.dil + km.res - km.frame_offset) * L + mm;
+      ld.src[j] = reinterpret_cast<const uint8_t*>(a.k_scales + ((size_t)b * a.H + h) * a.nblk + tok / 64);
+    }
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void win_issue(const WinLoads<FP8>& ld, const WinBuf& bf, int wave) {
+  using G = WinGeom<FP8>;
+#pragma unroll
+  for (int j = 0; j < G::NJ; ++j) {
+    const int e = wave + 4 * j;
+    if (e < G::KU) to_lds16(ld.src[j], bf.K + 1024 * e);
+    else if (e < G::KU + G::VU) to_lds16(ld.src[j], reinterpret_cast<uint8_t*>(bf.V) + 1024 * (e - G::KU));
+    else if (e < G::NLOAD) to_lds4(ld.src[j], bf.sk);
+  }
+}
+
+// One key block of a branch: scores from buffer cb, online softmax, O update.
+template <bool FP8>
+__device__ __forceinline__ void win_block(const WinArgs& a, const WinBuf& cb, const QueryCtx& qc, int pq,
+                                          int pb, bool full, const bf16x8 (&qf)[8], const i32x8 (&q8f)[2],
+                                          f32x16 (&O)[4], float& m_run, float& l_run) {
+  // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
+  f32x16 S[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    S[kt] = f32x16{};
+    if (!FP8) {
+      const uint16_t* Ks = reinterpret_cast<const uint16_t*>(cb.K) + (32 * kt + qc.krow) * KST;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * qc.g)), qf[s], S[kt]);
+    } else {
+      const uint8_t* K8 = cb.K + (32 * kt + qc.krow) * K8ST;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g);
+        const uint4 hi = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g + 16);
+        const i32x8 ka = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        S[kt] = mfma32x32x64_fp8(ka, q8f[s], S[kt]);
+      }
+    }
+  }
+  // ---- key scales, mask, block maximum (before the positive factor cq)
+  if (FP8) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float4 s4 = *reinterpret_cast<const float4*>(cb.sk + key_of(kt, 4 * rr, qc.g));
+        S[kt][4 * rr] *= s4.x;
+        S[kt][4 * rr + 1] *= s4.y;
+        S[kt][4 * rr + 2] *= s4.z;
+        S[kt][4 * rr + 3] *= s4.w;
+      }
+  }
+  if (!full) {
+    // valid iff pq - w < pk <= pq, i.e. (unsigned)(pq - pk) < w
+    const int base = pq - pb;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)a.w) S[kt][r] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qc.cq;
+  if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
+    const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    m_run = m_new;
+  }
+  // ---- probabilities -> bf16 operands: registers 8j..8j+7 of a tile are keys
+  //      32 kt + 16 j + 8 g + 0..7
+  bf16x8 P[2][2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], qc.cq, -m_run));
+      l_run += p[r];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      P[kt][j] = to_bf16x8(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3], p[8 * j + 4],
+                           p[8 * j + 5], p[8 * j + 6], p[8 * j + 7]);
+  }
+  // ---- O^T += V^T P^T   (lane: O^T[32dt + 8(r/4) + 4g + r%4][query ql]); the
+  //      V^T operand of (kt, j): features 32 dt + lane%32, keys 32 kt + 16 j + 8 g + 0..7
+  const int lane = threadIdx.x % 64;
+  const int G16 = lane / 16, s16 = lane % 16;
+  const uint16_t* vbase = cb.V + (8 * (G16 / 2) + s16 / 4) * KST + 16 * (G16 % 2) + 4 * (s16 % 4);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint16_t* vp = vbase + (32 * kt + 16 * j) * KST + 32 * dt;
+        O[dt] = mfma32x32x16(as_bf16x8(win_read_tr(vp), win_read_tr(vp + 4 * KST)), P[kt][j], O[dt]);
+      }
+}
 
 // One windowed branch over its key blocks: online softmax into O (unnormalised)
 // with running max m_run and lane-partial sum l_run.
 template <bool FP8, bool SHORTL>
-__device__ __forceinline__ void run_branch(const WinArgs& a, WinSmem<FP8>& sm, const BranchRange& br,
-                                           const QueryCtx& qc, const bf16x8 (&qf)[8],
-                                           const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
+__device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, const WinBuf& B1,
+                                           const BranchRange& br, const QueryCtx& qc,
+                                           const bf16x8 (&qf)[8], const i32x8 (&q8f)[2],
+                                           WinLoads<FP8>& ld, f32x16 (&O)[4], float& m_run,
                                            float& l_run) {
   const int L = a.L;
   int n0 = br.p_lo / L, m0 = br.p_lo - (br.p_lo / L) * L;
-  BlockRegs<FP8> regs;
-  win_load_block<FP8, SHORTL>(a, br.km, qc.b, qc.h, br.p_lo, n0, m0, br.p_hi, regs);
-  win_store_block<FP8>(sm, 0, regs);
+  win_block_addrs<FP8, SHORTL>(ld, a, br.km, qc.b, qc.h, qc.wave, br.p_lo, n0, m0, br.p_hi);
+  win_issue<FP8>(ld, B0, qc.wave);
+  win_wait_vmem();
   lds_barrier();
   const int pq = br.pq0 + qc.mq;                         // this lane's query position
-  for (int jb = 0; jb < br.nb; ++jb) {
-    const int buf = jb & 1;
-    const int pb = br.p_lo + BK * jb;
-    // next block's (sub-frame, offset)
-    int n1 = n0, m1 = m0 + BK;
-    while (m1 >= L) { m1 -= L; ++n1; }
-    const bool has_next = jb + 1 < br.nb;
-    if (has_next) win_load_block<FP8, SHORTL>(a, br.km, qc.b, qc.h, pb + BK, n1, m1, br.p_hi, regs);
-
-    const bool full = (pb > br.pq0 + qc.mw_hi - a.w) && (pb + BK - 1 <= br.pq0 + qc.mw_lo);
-
-    // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
-    f32x16 S[2];
+  for (int jb = 0; jb < br.nb; jb += 2) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      S[kt] = f32x16{};
-      if (!FP8) {
-        const uint16_t* Ks = reinterpret_cast<const uint16_t*>(sm.kbuf[buf]) + (32 * kt + qc.krow) * KST;
+    for (int half = 0; half < 2; ++half) {
+      const int jj = jb + half;
+      if (jj >= br.nb) break;
+      const WinBuf& cb = half ? B1 : B0;
+      const WinBuf& nb = half ? B0 : B1;
+      const int pb = br.p_lo + BK * jj;
+      // next block's (sub-frame, offset) and its loads
+      int n1 = n0, m1 = m0 + BK;
+      while (m1 >= L) { m1 -= L; ++n1; }
+      if (jj + 1 < br.nb) {
+        // inside one frame, unclamped, the next block's rows are this block's
+        // rows 64 positions on
+        const bool step = !SHORTL && m0 + BK <= L && n1 == n0 && m1 + BK <= L && pb + 2 * BK - 1 <= br.p_hi;
+        if (step) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * qc.g)), qf[s], S[kt]);
-      } else {
-        const uint8_t* K8 = sm.kbuf[buf] + (32 * kt + qc.krow) * K8ST;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g);
-          const uint4 hi = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g + 16);
-          const i32x8 ka = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          S[kt] = mfma32x32x64_fp8(ka, q8f[s], S[kt]);
+          for (int j = 0; j < WinGeom<FP8>::NJ; ++j) ld.src[j] += ld.inc[j];
+        } else {
+          win_block_addrs<FP8, SHORTL>(ld, a, br.km, qc.b, qc.h, qc.wave, pb + BK, n1, m1, br.p_hi);
         }
+        win_issue<FP8>(ld, nb, qc.wave);
       }
+      const bool full = (pb > br.pq0 + qc.mw_hi - a.w) && (pb + BK - 1 <= br.pq0 + qc.mw_lo);
+      win_block<FP8>(a, cb, qc, pq, pb, full, qf, q8f, O, m_run, l_run);
+      win_wait_vmem();
+      lds_barrier();
+      n0 = n1;
+      m0 = m1;
     }
-    // ---- key scales, mask, block maximum (before the positive factor cq)
-    if (FP8) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float4 s4 = *reinterpret_cast<const float4*>(&sm.sk[buf][key_of(kt, 4 * rr, qc.g)]);
-          S[kt][4 * rr] *= s4.x;
-          S[kt][4 * rr + 1] *= s4.y;
-          S[kt][4 * rr + 2] *= s4.z;
-          S[kt][4 * rr + 3] *= s4.w;
-        }
-    }
-    if (!full) {
-      // valid iff pq - w < pk <= pq, i.e. (unsigned)(pq - pk) < w
-      const int base = pq - pb;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)a.w) S[kt][r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qc.cq;
-    if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
-      const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-      m_run = m_new;
-    }
-    // ---- probabilities -> bf16 operands: registers 8j..8j+7 of a tile are keys
-    //      32 kt + 16 j + 8 g + 0..7
-    bf16x8 P[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], qc.cq, -m_run));
-        l_run += p[r];
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        P[kt][j] = to_bf16x8(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3], p[8 * j + 4],
-                             p[8 * j + 5], p[8 * j + 6], p[8 * j + 7]);
-    }
-    // ---- O^T += V^T P^T   (lane: O^T[32dt + 8(r/4) + 4g + r%4][query ql])
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* vrow = &sm.Vt[buf][32 * dt + qc.ql][0];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          O[dt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 32 * kt + 16 * j + 8 * qc.g)),
-                               P[kt][j], O[dt]);
-    }
-    if (has_next) win_store_block<FP8>(sm, buf ^ 1, regs);
-    lds_barrier();
-    n0 = n1;
-    m0 = m1;
   }
 }
 
 template <bool FP8, bool HYBRID, bool SHORTL>
 __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
-  __shared__ WinSmem<FP8> sm;
+  using G = WinGeom<FP8>;
+  __shared__ __attribute__((aligned(16))) uint8_t Kb0[G::KBYTES], Kb1[G::KBYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t Vb0[G::VBYTES / 2], Vb1[G::VBYTES / 2];
+  __shared__ __attribute__((aligned(16))) float sk0[BK], sk1[BK];
+  const WinBuf B0{Kb0, Vb0, sk0};
+  const WinBuf B1{Kb1, Vb1, sk1};
   const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int qt = lid % a.QT;
   const int f = (lid / a.QT) % a.F;
@@ -380,7 +408,9 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   if (m0 >= Lf) return;
   const int m_last_wg = min(m0 + BQ, Lf) - 1;
 
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  qc.wave = wave;
   qc.ql = lane % 32;
   qc.g = lane / 32;
   const int m_row = m0 + 32 * wave + qc.ql;        // query row in the frame
@@ -393,6 +423,9 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   // score row of this lane's A operand: key pi(ql) of each 32-key tile
   qc.krow = 16 * (qc.ql / 16) + 8 * ((qc.ql / 4) & 1) + 4 * ((qc.ql / 8) & 1) + (qc.ql & 3);
   const int b = qc.b, h = qc.h, g = qc.g;
+
+  WinLoads<FP8> ld;
+  win_load_setup<FP8>(ld, wave, a.H);
 
   // ---- Q operand registers (B operand of S^T = K Q^T)
   bf16x8 qf[8];
@@ -425,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
 
   // ---- first branch: SWA (or the single requested branch)
   const BranchRange b0 = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
-  run_branch<FP8, SHORTL>(a, sm, b0, qc, qf, q8f, O, m_run, l_run);
+  run_branch<FP8, SHORTL>(a, B0, B1, b0, qc, qf, q8f, ld, O, m_run, l_run);
   float fac = 1.f / (l_run + __shfl_xor(l_run, 32, 64));
   if (HYBRID) {
     fac *= 1.f / (1.f + __expf(-a.gates[h]));
@@ -446,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
     m_run = -1e30f;
     l_run = 0.f;
     const BranchRange b1 = branch_range(a, a.dil, f, m0, m_last_wg);
-    run_branch<FP8, SHORTL>(a, sm, b1, qc, qf, q8f, O, m_run, l_run);
+    run_branch<FP8, SHORTL>(a, B0, B1, b1, qc, qf, q8f, ld, O, m_run, l_run);
     fac = 1.f / (l_run + __shfl_xor(l_run, 32, 64)) / (1.f + __expf(-a.gates[a.H + h]));
   }
 
@@ -463,10 +496,10 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
       if (HYBRID) {
         const float4 yp = *reinterpret_cast<const float4*>(a.ypart + rowoff + d0);
         const uint2 og = *reinterpret_cast<const uint2*>(a.o_gdn + rowoff + d0);
-        y0 += yp.x + gg * bf16_to_f32(lo16w(og.x));
-        y1 += yp.y + gg * bf16_to_f32(hi16w(og.x));
-        y2 += yp.z + gg * bf16_to_f32(lo16w(og.y));
-        y3 += yp.w + gg * bf16_to_f32(hi16w(og.y));
+        y0 += yp.x + gg * bf16_to_f32(og.x & 0xFFFFu);
+        y1 += yp.y + gg * bf16_to_f32(og.x >> 16);
+        y2 += yp.z + gg * bf16_to_f32(og.y & 0xFFFFu);
+        y3 += yp.w + gg * bf16_to_f32(og.y >> 16);
       }
       *reinterpret_cast<uint2*>(a.out + rowoff + d0) = pack_bf16x4(y0, y1, y2, y3);
     }
