@@ -112,8 +112,7 @@ __global__ __launch_bounds__(D) void gdn_f32_kernel(const float* __restrict__ q,
 // ---------------------------------------------------------------- bf16 chunkwise path
 
 constexpr int CH = 64;          // chunk length
-constexpr int KS_PAD = 8;       // row padding (bf16 elements) of token-major tiles
-constexpr int TS = CH + 8;      // row stride of 64-wide bf16 tiles (Kt, Vt, Tb, Pb)
+constexpr int TS = CH + 8;      // row stride of the bf16 T tile in the prep kernel
 constexpr int AS = CH + 4;      // row stride of the fp32 A tile
 
 __device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xFFFFu; }
@@ -133,37 +132,22 @@ __device__ __forceinline__ bf16x8 regs_operand(const f32x4& top, const f32x4& bo
   return to_bf16x8(top[0], top[1], top[2], top[3], bot[0], bot[1], bot[2], bot[3]);
 }
 
-// Lower-triangular 16x16 tile (ti, tj), tj <= ti, of a 64x64 Gram product
-// R_ti . C_tj^T over D features (rows of two token-major LDS tiles).
-template <int D>
-__device__ __forceinline__ f32x4 gram_tile(const uint16_t* rows_a, const uint16_t* rows_b, int stride,
-                                           int ti, int tj, int l16, int g) {
-  f32x4 acc = zero4();
-  const uint16_t* arow = rows_a + (16 * ti + l16) * stride;
-  const uint16_t* brow = rows_b + (16 * tj + l16) * stride;
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-    acc = mfma16x16x32(as_bf16x8(*reinterpret_cast<const uint4*>(arow + 32 * s + 8 * g)),
-                       as_bf16x8(*reinterpret_cast<const uint4*>(brow + 32 * s + 8 * g)), acc);
-  return acc;
-}
-
-__device__ __forceinline__ void tri_index(int idx, int& ti, int& tj) {
-  ti = 0;
-  while (idx > ti) { idx -= ti + 1; ++ti; }
-  tj = idx;
+// Raw buffer descriptor: loads at byte offsets >= nbytes return zero and
+// stores there are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
 
 // ---- prep: per (b, h, chunk), independent of the state
 //   g_t = sum_{s<=t} log2 a_s            (written out, fp32)
 //   A   = strictlower(b_t 2^{g_t - g_i} k_t.k_i)
 //   T   = (I + A)^{-1}                   (written out, bf16, unit lower triangular)
-// T by blocks of 16: diagonal blocks by forward substitution, then the two
-// 16x16 off-diagonal blocks of each 32x32 half, then the lower-left 32x32
-// block T_LL = -T_H A_HL T_L (block inverse of a lower triangular matrix).
-template <int D>
+// One wave per chunk: the 64 x D key tile stays in registers (it is both
+// operands of the Gram product), A goes to LDS in fp32.  T by blocks of 16:
+// diagonal blocks by forward substitution, then the 16x16 off-diagonal block
+// of each 32x32 half, then the lower-left 32x32 block T_LL = -T_H A_HL T_L
+// (block inverse of a lower triangular matrix).
 struct PrepSmem {
-  uint16_t Ks[CH][D + KS_PAD];
   float Af[CH][AS];
   uint16_t Tb[CH][TS];
   float g2[CH];
@@ -171,49 +155,56 @@ struct PrepSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void gdn_prep_kernel(const uint16_t* __restrict__ k,
-                                                       const float* __restrict__ alpha,
-                                                       const float* __restrict__ beta,
-                                                       uint16_t* __restrict__ t_out,
-                                                       float* __restrict__ g_out, int T, int H,
-                                                       int nchunks) {
-  __shared__ PrepSmem<D> sm;
+__global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict__ k,
+                                                      const float* __restrict__ alpha,
+                                                      const float* __restrict__ beta,
+                                                      uint16_t* __restrict__ t_out,
+                                                      float* __restrict__ g_out, int T, int H,
+                                                      int nchunks) {
+  constexpr int DS = D / 32;
+  __shared__ PrepSmem sm;
   const int c = blockIdx.x % nchunks;
   const int bh = blockIdx.x / nchunks;
   const int b = bh / H, h = bh % H;
   const int t0 = c * CH;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int l16 = lane % 16, g = lane / 16;
-  const size_t tok_stride = (size_t)H * D;
-  const size_t base = ((size_t)b * T * H + h) * D;
+  const int valid = min(CH, T - t0);
+  const int lane = threadIdx.x, l16 = lane % 16, g = lane / 16;
 
-  for (int i = tid; i < CH * TS; i += 256) (&sm.Tb[0][0])[i] = 0;
-  for (int u = tid; u < CH * D / 8; u += 256) {
-    const int t = u / (D / 8), dg = u % (D / 8);
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (t0 + t < T) x = *reinterpret_cast<const uint4*>(k + base + (size_t)(t0 + t) * tok_stride + 8 * dg);
-    *reinterpret_cast<uint4*>(&sm.Ks[t][8 * dg]) = x;
-  }
-  if (wave == 0) {
+  // key tile: kr[a][s] = k[t0 + 16a + l16][32s + 8g .. +8] (zero past T)
+  const uint32_t tok_bytes = (uint32_t)H * D * 2;
+  const auto rk = buf_rsrc(k + (((size_t)b * T + t0) * H + h) * D, (uint32_t)(valid - 1) * tok_bytes + D * 2);
+  uint4 kr[4][DS];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      kr[a][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rk, (uint32_t)(16 * a + l16) * tok_bytes + (32 * s + 8 * g) * 2, 0, 0));
+  {
     const int t = t0 + lane;
-    const float a = t < T ? alpha[((size_t)b * T + t) * H + h] : 1.f;   // padding: no decay,
-    const float bb = t < T ? beta[((size_t)b * T + t) * H + h] : 0.f;   // no write
-    float x = __log2f(a);
+    const float av = lane < valid ? alpha[((size_t)b * T + t) * H + h] : 1.f;   // padding: no decay,
+    const float bv = lane < valid ? beta[((size_t)b * T + t) * H + h] : 0.f;    // no write
+    float x = __log2f(av);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
       if (lane >= off) x += y;
     }
     sm.g2[lane] = x;
-    sm.bet[lane] = bb;
+    sm.bet[lane] = bv;
+    g_out[((size_t)bh * nchunks + c) * CH + lane] = x;
   }
+  for (int i = lane; i < CH * TS / 8; i += 64) reinterpret_cast<uint4*>(&sm.Tb[0][0])[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   // A = strictlower(b 2^{dg} K K^T), fp32
-  for (int task = wave; task < 10; task += 4) {
-    int ti, tj;
-    tri_index(task, ti, tj);
-    const f32x4 acc = gram_tile<D>(&sm.Ks[0][0], &sm.Ks[0][0], D + KS_PAD, ti, tj, l16, g);
+#pragma unroll
+  for (int task = 0; task < 10; ++task) {
+    const int ti = task < 1 ? 0 : task < 3 ? 1 : task < 6 ? 2 : 3;
+    const int tj = task - ti * (ti + 1) / 2;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kr[ti][s]), as_bf16x8(kr[tj][s]), acc);
     const int col = 16 * tj + l16;
     const float gc = sm.g2[col];
 #pragma unroll
@@ -224,8 +215,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const uint16_t* __restric
   }
   __syncthreads();
 
-  // diagonal 16x16 blocks by forward substitution (wave 0: lane -> block g, column l16)
-  if (wave == 0) {
+  // diagonal 16x16 blocks by forward substitution (lane -> block g, column l16)
+  {
     const int blk = g, j = l16;
     float x[16];
 #pragma unroll
@@ -247,8 +238,9 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const uint16_t* __restric
 
   // T_{h1,h0} = -T_{h1,h1} A_{h1,h0} T_{h0,h0} for the two 32x32 halves
   // (K = 16 padded to 32: slots 8g + r <-> k = 4g + r, slots 8g+4.. are zero)
-  if (wave < 2) {
-    const int h0 = 2 * wave, h1 = 2 * wave + 1;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int h0 = 2 * half, h1 = 2 * half + 1;
     const float* arow = &sm.Af[16 * h1 + l16][16 * h0 + 4 * g];
     const bf16x8 a = to_bf16x8(arow[0], arow[1], arow[2], arow[3], 0.f, 0.f, 0.f, 0.f);
     const int col = 16 * h0 + l16;
@@ -264,9 +256,10 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const uint16_t* __restric
   }
   __syncthreads();
 
-  // lower-left 32x32 block: T_LL = -T_H A_HL T_L (wave tj: column tile tj)
-  if (wave < 2) {
-    const int tj = wave;
+  // lower-left 32x32 block: T_LL = -T_H A_HL T_L (column tile tj)
+  f32x4 tll[2][2];
+#pragma unroll
+  for (int tj = 0; tj < 2; ++tj) {
     f32x4 z[2];
 #pragma unroll
     for (int zi = 0; zi < 2; ++zi) {
@@ -282,21 +275,25 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(const uint16_t* __restric
     }
     const bf16x8 zb = regs_operand(z[0], z[1]);
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const f32x4 tll = mfma16x16x32(row_operand_perm(&sm.Tb[32 + 16 * ti + l16][0], 32, g), zb, zero4());
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.Tb[32 + 16 * ti + 4 * g + r][16 * tj + l16] = bf16_bits(-tll[r]);
-    }
+    for (int ti = 0; ti < 2; ++ti)
+      tll[tj][ti] = mfma16x16x32(row_operand_perm(&sm.Tb[32 + 16 * ti + l16][0], 32, g), zb, zero4());
   }
+  // (all reads of the lower-left block's inputs are done before it is written)
+#pragma unroll
+  for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.Tb[32 + 16 * ti + 4 * g + r][16 * tj + l16] = bf16_bits(-tll[tj][ti][r]);
   __syncthreads();
 
-  // write T (64 x 64 bf16, row-major) and g
+  // write T (64 x 64 bf16, row-major)
   uint16_t* tdst = t_out + ((size_t)bh * nchunks + c) * CH * CH;
-  for (int u = tid; u < CH * CH / 8; u += 256) {
+#pragma unroll
+  for (int u = lane; u < CH * CH / 8; u += 64) {
     const int row = u / 8, cg = u % 8;
     *reinterpret_cast<uint4*>(tdst + row * CH + 8 * cg) = *reinterpret_cast<const uint4*>(&sm.Tb[row][8 * cg]);
   }
-  if (wave == 0) g_out[((size_t)bh * nchunks + c) * CH + lane] = sm.g2[lane];
 }
 
 // ---- scan: per (b, h, 16*NW rows of S), chunks in order
@@ -349,11 +346,6 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// Raw buffer descriptor: loads at byte offsets >= nbytes return zero and
-// stores there are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
-}
 __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
 }
@@ -364,6 +356,12 @@ __device__ __forceinline__ void buf_store8(uint2 x, __amdgpu_buffer_rsrc_t r, ui
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, 0);
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// until at most N vector memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // bytes from a chunk's first token to the end of its last valid token row
 __device__ __forceinline__ uint32_t chunk_bytes(int T, int c, uint32_t tok_bytes, int D) {
@@ -379,6 +377,9 @@ struct ScanGeom {
   static constexpr int TST = CH + 16;                              // T, P row stride
   static constexpr int KU = KST / 8, VU = VST / 8, TU = TST / 8;   // 16-byte units per row
   // a tile of 64 rows x U units is exactly U loads of 64 lanes
+  // with four compute waves, wave w computes the P tiles of query block w
+  // inside its X/Y pass (it keeps that Q block in registers)
+  static constexpr bool PM = NW == 4;
 };
 
 // One LDS buffer (pointers into separate __shared__ variables).
@@ -430,21 +431,26 @@ struct ScanLoadOffs {
   uint32_t v[VJ];
   uint32_t t[TJ];
   int lw;            // loader index 0 .. NW-1
+  // loads m = lw, lw + NW, ... < U of a tile of U loads
+  static constexpr int share(int U, int lw) { return U > lw ? (U - 1 - lw) / NW + 1 : 0; }
+  static constexpr int qvt_loads(int lw) {
+    return share(ScanGeom<D, NW>::KU, lw) + share(ScanGeom<D, NW>::VU, lw) + share(ScanGeom<D, NW>::TU, lw);
+  }
 };
 
-// Chunk c: HBM -> LDS buffer bf, this loader wave's share.  A wave keeps
-// only a few loads in flight, so the chunk is split over NW loader waves.
+// Loads of chunk c into LDS buffer bf, this loader wave's share (loads
+// m = lw, lw + NW, ... of each tile).  Two batches per chunk: K with g and b
+// (needed through the whole chunk), and Q, V, T (read before the middle of
+// the chunk, so they are fetched one chunk earlier into the buffer that the
+// chunk two steps back has released).
 template <int D, int NW>
-__device__ __forceinline__ void scan_issue(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
-                                           const ScanBuf& bf, int c) {
+__device__ __forceinline__ void scan_issue_k(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
+                                             const ScanBuf& bf, int c) {
   using G = ScanGeom<D, NW>;
   using L = ScanLoadOffs<D, NW>;
   const int lane = threadIdx.x % 64;
   const size_t e0 = x.head0 + (size_t)c * x.chunk_elems;
-  const uint32_t nrec = chunk_bytes(x.T, c, x.tok_bytes, D);
-  const auto rk = buf_rsrc(x.k + e0, nrec), rq = buf_rsrc(x.q + e0, nrec);
-  const auto rv = buf_rsrc(x.v + e0 + x.n_base, nrec);
-  const auto rt = buf_rsrc(x.t_in + (x.tg0 + c) * CH * CH, CH * CH * 2);
+  const auto rk = buf_rsrc(x.k + e0, chunk_bytes(x.T, c, x.tok_bytes, D));
   if (lo.lw == 0) {
     const int valid = min(CH, x.T - c * CH);
     const auto rg = buf_rsrc(x.g_in + (x.tg0 + c) * CH, CH * 4);
@@ -457,6 +463,18 @@ __device__ __forceinline__ void scan_issue(const ScanCtx<D, NW>& x, const ScanLo
     const int m = lo.lw + NW * j;
     if (m < G::KU) buf_to_lds16(rk, bf.K + 512 * m, lo.kq[j]);
   }
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void scan_issue_qvt(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
+                                               const ScanBuf& bf, int c) {
+  using G = ScanGeom<D, NW>;
+  using L = ScanLoadOffs<D, NW>;
+  const size_t e0 = x.head0 + (size_t)c * x.chunk_elems;
+  const uint32_t nrec = chunk_bytes(x.T, c, x.tok_bytes, D);
+  const auto rq = buf_rsrc(x.q + e0, nrec);
+  const auto rv = buf_rsrc(x.v + e0 + x.n_base, nrec);
+  const auto rt = buf_rsrc(x.t_in + (x.tg0 + c) * CH * CH, CH * CH * 2);
 #pragma unroll
   for (int j = 0; j < L::TJ; ++j) {
     const int m = lo.lw + NW * j;
@@ -472,6 +490,17 @@ __device__ __forceinline__ void scan_issue(const ScanCtx<D, NW>& x, const ScanLo
     const int m = lo.lw + NW * j;
     if (m < G::KU) buf_to_lds16(rq, bf.Q + 512 * m, lo.kq[j]);
   }
+}
+
+// Wait until this loader wave's Q/V/T batch (the most recent one) is the
+// only one still in flight.
+template <int D, int NW>
+__device__ __forceinline__ void wait_all_but_qvt(int lw) {
+  using L = ScanLoadOffs<D, NW>;
+  if (lw == 0) wait_vmem_le<L::qvt_loads(0)>();
+  else if (lw == 1) wait_vmem_le<L::qvt_loads(1)>();
+  else if (lw == 2) wait_vmem_le<L::qvt_loads(2)>();
+  else wait_vmem_le<L::qvt_loads(3)>();
 }
 
 // 2^{g} and 2^{g_C - g} of a staged chunk (wave 0, after its loads landed)
@@ -508,7 +537,7 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
   // ---- P = lower(2^{g_t - g_i} q_t . k_i), as tiles of K Q^T: lane holds
   //      keys i0 .. i0+3 (consecutive tokens) of query t
   constexpr int NTASK = 12 / NW;
-  {
+  if constexpr (!G::PM) {
     uint4 pk[2][DS], pq[2][DS];
     float gt[2];
     float4 gi[2];
@@ -570,12 +599,26 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
       }                                                                                    \
     }
     KAIROS_XY_LOAD(0, 0);
+    // PM: query block `wave` of P = lower(2^{g_t - g_i} q_t . k_i); tile
+    // (wave, tt) for the key blocks tt of the same or an earlier 32-token half
+    uint4 qw[DS];
+    int p_t = 0;
+    float p_gt = 0.f;
+    if constexpr (G::PM) {
+      const uint16_t* qrow = cb.Q + (16 * wave + l16) * KST + 8 * g;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qw[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+      p_t = row_token(16 * wave + l16);
+      p_gt = cb.g2[p_t];
+    }
     bf16x8 Sop[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) Sop[s] = regs_operand(S[2 * s], S[2 * s + 1]);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const int cur_b = tt & 1;
+      float4 p_gi = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (G::PM) p_gi = *reinterpret_cast<const float4*>(cb.g2 + row_token(16 * tt + 4 * g));
       if (tt + 1 < 4) {
         KAIROS_XY_LOAD(tt + 1, cur_b ^ 1);
       } else {
@@ -598,6 +641,19 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
       for (int s = 0; s < DS; ++s) {
         X[tt] = mfma16x16x32(as_bf16x8(xk[cur_b][s]), Sop[s], X[tt]);
         Y[tt] = mfma16x16x32(Sop[s], as_bf16x8(xq[cur_b][s]), Y[tt]);
+      }
+      if constexpr (G::PM) {
+        if (wave >= 2 * (tt / 2)) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(xk[cur_b][s]), as_bf16x8(qw[s]), acc);
+          const int i0 = row_token(16 * tt + 4 * g);
+          const float p0 = i0 <= p_t ? __builtin_amdgcn_exp2f(p_gt - p_gi.x) * acc[0] : 0.f;
+          const float p1 = i0 + 1 <= p_t ? __builtin_amdgcn_exp2f(p_gt - p_gi.y) * acc[1] : 0.f;
+          const float p2 = i0 + 2 <= p_t ? __builtin_amdgcn_exp2f(p_gt - p_gi.z) * acc[2] : 0.f;
+          const float p3 = i0 + 3 <= p_t ? __builtin_amdgcn_exp2f(p_gt - p_gi.w) * acc[3] : 0.f;
+          *reinterpret_cast<uint2*>(Pb + (16 * wave + l16) * TST + i0) = pack_bf16x4(p0, p1, p2, p3);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -642,7 +698,7 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
     E[2] = mfma16x16x32(as_bf16x8(tr[4]), Rop1, E[2]);
     E[3] = mfma16x16x32(as_bf16x8(tr[5]), Rop1, E[3]);
   }
-  lds_barrier();                      // P complete
+  lds_barrier();                      // P complete; this chunk's Q, V, T released
 
   // O^T = 2^g Y^T + E^T P^T;  S <- 2^{g_C} S + K^T diag(w) E
   {
@@ -685,16 +741,28 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
   lds_barrier();                      // the next chunk has landed (loader wave)
 }
 
-// Loader wave, one chunk: the next chunk's loads, then the two barriers of
-// the compute waves' chunk; the loads must have landed by the second.
+// Loader wave, one chunk c (buffer cb; nb is the other buffer): K, g, b of
+// chunk c+1 into nb; after the middle barrier, when chunk c no longer reads
+// its Q, V, T, the Q/V/T batch of chunk c+2 into cb; 2^{g} and 2^{g_C - g}
+// of chunk c+1.  Before the end barrier everything but the newest batch has
+// landed.  Two barriers per chunk, as in the compute waves.
 template <int D, int NW>
 __device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
-                                                const ScanBuf& nb, int c) {
-  const bool more = c + 1 < x.nchunks;
-  if (more) scan_issue<D, NW>(x, lo, nb, c + 1);
+                                                const ScanBuf& cb, const ScanBuf& nb, int c) {
+  using L = ScanLoadOffs<D, NW>;
+  const bool more1 = c + 1 < x.nchunks, more2 = c + 2 < x.nchunks;
+  if (more1) scan_issue_k<D, NW>(x, lo, nb, c + 1);
   lds_barrier();
-  wait_vmem();
-  if (more && lo.lw == 0) scan_decays(nb);
+  if (more1 && lo.lw == 0) {
+    wait_vmem_le<L::share(ScanGeom<D, NW>::KU, 0)>();      // g and b of chunk c+1
+    scan_decays(nb);
+  }
+  if (more2) {
+    scan_issue_qvt<D, NW>(x, lo, cb, c + 2);
+    wait_all_but_qvt<D, NW>(lo.lw);
+  } else {
+    wait_vmem();
+  }
   lds_barrier();
 }
 
@@ -760,14 +828,16 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
       lo.t[j] = (uint32_t)row_token(U / G::TU) * (CH * 2) + (U % G::TU) % 8 * 16;
     }
     if (x.nchunks > 0) {
-      scan_issue<D, NW>(x, lo, B0, 0);
+      scan_issue_k<D, NW>(x, lo, B0, 0);
+      scan_issue_qvt<D, NW>(x, lo, B0, 0);
+      if (x.nchunks > 1) scan_issue_qvt<D, NW>(x, lo, B1, 1);
       wait_vmem();
       if (lo.lw == 0) scan_decays(B0);
     }
     lds_barrier();
     for (int c = 0; c < x.nchunks; c += 2) {
-      scan_load_chunk<D, NW>(x, lo, B1, c);
-      if (c + 1 < x.nchunks) scan_load_chunk<D, NW>(x, lo, B0, c + 1);
+      scan_load_chunk<D, NW>(x, lo, B0, B1, c);
+      if (c + 1 < x.nchunks) scan_load_chunk<D, NW>(x, lo, B1, B0, c + 1);
     }
     return;
   }
@@ -861,8 +931,8 @@ hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t
                                          ((nt * CH * CH * 2 + 255) / 256) * 256);
   if (nchunks > 0) {
     if (nt > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (D == 128) gdn_prep_kernel<128><<<(unsigned)nt, 256, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
-    else if (D == 64) gdn_prep_kernel<64><<<(unsigned)nt, 256, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
+    if (D == 128) gdn_prep_kernel<128><<<(unsigned)nt, 64, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
+    else if (D == 64) gdn_prep_kernel<64><<<(unsigned)nt, 64, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
     else return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
