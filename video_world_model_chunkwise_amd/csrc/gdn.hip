@@ -132,6 +132,18 @@ __device__ __forceinline__ bf16x8 regs_operand(const f32x4& top, const f32x4& bo
   return to_bf16x8(top[0], top[1], top[2], top[3], bot[0], bot[1], bot[2], bot[3]);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
+// 4j + i/4, j = 0..3.  With lane s addressing row k0 + s/4, columns
+// c(s % 4) .. c(s % 4) + 3, lane i receives column c(i/4) + i%4 of rows
+// k0 .. k0 + 3.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
 // Raw buffer descriptor: loads at byte offsets >= nbytes return zero and
 // stores there are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
                                                       float* __restrict__ g_out, int T, int H,
                                                       int nchunks) {
   constexpr int DS = D / 32;
-  __shared__ PrepSmem sm;
+  __shared__ __attribute__((aligned(16))) PrepSmem sm;
   const int c = blockIdx.x % nchunks;
   const int bh = blockIdx.x / nchunks;
   const int b = bh / H, h = bh % H;
@@ -197,7 +209,16 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
   for (int i = lane; i < CH * TS / 8; i += 64) reinterpret_cast<uint4*>(&sm.Tb[0][0])[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  // A = strictlower(b 2^{dg} K K^T), fp32
+  // A = strictlower(b 2^{dg} K K^T), fp32.  Lane (l16, g) of tile (ti, tj)
+  // holds rows 16 ti + 4g + r (r = 0..3) of column 16 tj + l16.
+  float4 grow[4], brow[4];
+  float gcol[4];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
+    grow[ti] = *reinterpret_cast<const float4*>(&sm.g2[16 * ti + 4 * g]);
+    brow[ti] = *reinterpret_cast<const float4*>(&sm.bet[16 * ti + 4 * g]);
+    gcol[ti] = sm.g2[16 * ti + l16];
+  }
 #pragma unroll
   for (int task = 0; task < 10; ++task) {
     const int ti = task < 1 ? 0 : task < 3 ? 1 : task < 6 ? 2 : 3;
@@ -206,30 +227,36 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int s = 0; s < DS; ++s) acc = mfma16x16x32(as_bf16x8(kr[ti][s]), as_bf16x8(kr[tj][s]), acc);
     const int col = 16 * tj + l16;
-    const float gc = sm.g2[col];
+    const float gr[4] = {grow[ti].x, grow[ti].y, grow[ti].z, grow[ti].w};
+    const float br[4] = {brow[ti].x, brow[ti].y, brow[ti].z, brow[ti].w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * ti + 4 * g + r;
-      sm.Af[row][col] = (col < row) ? sm.bet[row] * __builtin_amdgcn_exp2f(sm.g2[row] - gc) * acc[r] : 0.f;
+      const float val = br[r] * __builtin_amdgcn_exp2f(gr[r] - gcol[tj]) * acc[r];
+      sm.Af[row][col] = (ti > tj || col < row) ? val : 0.f;
     }
   }
   __syncthreads();
 
-  // diagonal 16x16 blocks by forward substitution (lane -> block g, column l16)
+  // diagonal 16x16 blocks by forward substitution (lane -> block g, column
+  // l16), the block's rows of A read into registers first
   {
     const int blk = g, j = l16;
+    float a[16][16];
+#pragma unroll
+    for (int t = 1; t < 16; ++t)
+#pragma unroll
+      for (int q = 0; q < (t + 3) / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(&sm.Af[16 * blk + t][16 * blk + 4 * q]);
+        a[t][4 * q] = v.x; a[t][4 * q + 1] = v.y; a[t][4 * q + 2] = v.z; a[t][4 * q + 3] = v.w;
+      }
     float x[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const float* arow = &sm.Af[16 * blk + t][16 * blk];
-      float s0 = 0.f, s1 = 0.f;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i + 1 < t; i += 2) {
-        s0 = fmaf(arow[i], x[i], s0);
-        s1 = fmaf(arow[i + 1], x[i + 1], s1);
-      }
-      if (t & 1) s0 = fmaf(arow[t - 1], x[t - 1], s0);
-      x[t] = ((t == j) ? 1.f : 0.f) - (s0 + s1);
+      for (int i = 0; i < t; ++i) s4[i % 4] = fmaf(a[t][i], x[i], s4[i % 4]);
+      x[t] = ((t == j) ? 1.f : 0.f) - ((s4[0] + s4[1]) + (s4[2] + s4[3]));
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) sm.Tb[16 * blk + t][16 * blk + j] = bf16_bits(x[t]);
@@ -237,41 +264,40 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
   __syncthreads();
 
   // T_{h1,h0} = -T_{h1,h1} A_{h1,h0} T_{h0,h0} for the two 32x32 halves
-  // (K = 16 padded to 32: slots 8g + r <-> k = 4g + r, slots 8g+4.. are zero)
+  // (K = 16 padded to 32: slots 8g + r <-> k = 4g + r, slots 8g+4.. are zero);
+  // the columns of T_{h0,h0} come from transposed reads (4 rows each)
+  f32x4 t10[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int h0 = 2 * half, h1 = 2 * half + 1;
-    const float* arow = &sm.Af[16 * h1 + l16][16 * h0 + 4 * g];
-    const bf16x8 a = to_bf16x8(arow[0], arow[1], arow[2], arow[3], 0.f, 0.f, 0.f, 0.f);
-    const int col = 16 * h0 + l16;
-    const int r0 = 16 * h0 + 4 * g;
-    const uint2 lo = make_uint2(sm.Tb[r0][col] | ((uint32_t)sm.Tb[r0 + 1][col] << 16),
-                                sm.Tb[r0 + 2][col] | ((uint32_t)sm.Tb[r0 + 3][col] << 16));
+    const float4 av = *reinterpret_cast<const float4*>(&sm.Af[16 * h1 + l16][16 * h0 + 4 * g]);
+    const bf16x8 a = to_bf16x8(av.x, av.y, av.z, av.w, 0.f, 0.f, 0.f, 0.f);
+    const uint2 lo = lds_read_tr(&sm.Tb[16 * h0 + 4 * g + l16 / 4][16 * h0 + 4 * (l16 % 4)]);
     const f32x4 z = mfma16x16x32(a, as_bf16x8(lo, make_uint2(0, 0)), zero4());
     const uint2 tlo = *reinterpret_cast<const uint2*>(&sm.Tb[16 * h1 + l16][16 * h1 + 4 * g]);
-    const f32x4 t10 = mfma16x16x32(as_bf16x8(tlo, make_uint2(0, 0)),
-                                   to_bf16x8(z[0], z[1], z[2], z[3], 0.f, 0.f, 0.f, 0.f), zero4());
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Tb[16 * h1 + 4 * g + r][16 * h0 + l16] = bf16_bits(-t10[r]);
+    t10[half] = mfma16x16x32(as_bf16x8(tlo, make_uint2(0, 0)),
+                             to_bf16x8(z[0], z[1], z[2], z[3], 0.f, 0.f, 0.f, 0.f), zero4());
   }
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.Tb[32 * half + 16 + 4 * g + r][32 * half + l16] = bf16_bits(-t10[half][r]);
   __syncthreads();
 
-  // lower-left 32x32 block: T_LL = -T_H A_HL T_L (column tile tj)
+  // lower-left 32x32 block: T_LL = -T_H A_HL T_L (column tile tj); rows
+  // 8g .. 8g+7 of a column of T_L from two transposed reads
   f32x4 tll[2][2];
 #pragma unroll
   for (int tj = 0; tj < 2; ++tj) {
+    const uint2 b0 = lds_read_tr(&sm.Tb[8 * g + l16 / 4][16 * tj + 4 * (l16 % 4)]);
+    const uint2 b1 = lds_read_tr(&sm.Tb[8 * g + 4 + l16 / 4][16 * tj + 4 * (l16 % 4)]);
     f32x4 z[2];
 #pragma unroll
     for (int zi = 0; zi < 2; ++zi) {
-      const float* arow = &sm.Af[32 + 16 * zi + l16][8 * g];
-      const bf16x8 a = to_bf16x8(arow[0], arow[1], arow[2], arow[3], arow[4], arow[5], arow[6], arow[7]);
-      const int col = 16 * tj + l16;
-      const int r0 = 8 * g;
-      const uint4 bw = make_uint4(sm.Tb[r0][col] | ((uint32_t)sm.Tb[r0 + 1][col] << 16),
-                                  sm.Tb[r0 + 2][col] | ((uint32_t)sm.Tb[r0 + 3][col] << 16),
-                                  sm.Tb[r0 + 4][col] | ((uint32_t)sm.Tb[r0 + 5][col] << 16),
-                                  sm.Tb[r0 + 6][col] | ((uint32_t)sm.Tb[r0 + 7][col] << 16));
-      z[zi] = mfma16x16x32(a, as_bf16x8(bw), zero4());
+      const float4 a0 = *reinterpret_cast<const float4*>(&sm.Af[32 + 16 * zi + l16][8 * g]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&sm.Af[32 + 16 * zi + l16][8 * g + 4]);
+      const bf16x8 a = to_bf16x8(a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w);
+      z[zi] = mfma16x16x32(a, as_bf16x8(b0, b1), zero4());
     }
     const bf16x8 zb = regs_operand(z[0], z[1]);
 #pragma unroll
@@ -331,20 +357,9 @@ __device__ __forceinline__ int s_feature(int dt, int g) {   // cb(dt, g)
   return 32 * (dt / 2) + 8 * g + 4 * (dt % 2);
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
-// 4j + i/4, j = 0..3.  With lane s addressing row k0 + s/4, columns
-// c(s % 4) .. c(s % 4) + 3, lane i receives column c(i/4) + i%4 of rows
-// k0 .. k0 + 3.
-__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (s16x4 __attribute__((address_space(3)))*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
 
 __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
@@ -354,6 +369,13 @@ __device__ __forceinline__ void buf_to_lds4(__amdgpu_buffer_rsrc_t r, void* lds,
 }
 __device__ __forceinline__ void buf_store8(uint2 x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, 0);
+}
+// An element offset the compiler must treat as unknown.  LDS-DMA targets
+// written as a constant offset into a __shared__ array become a constant
+// expression whose generic-to-LDS cast this compiler fails to lower.
+__device__ __forceinline__ int opaque_offset(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 // until at most N vector memory operations of this wave are outstanding
@@ -422,19 +444,22 @@ struct ScanCtx {
 // Per-lane byte offsets of the loader wave's loads inside a chunk: load m of
 // a tile fills 16-byte units 64 m .. 64 m + 63 (row = unit / units per row).
 // Each of the NW loader waves issues loads m = lw, lw + NW, ... of each tile.
-template <int D, int NW>
+// The loader index is a compile-time constant, so that every load of a
+// wave is unconditional and the compiler's waits for LDS data written by
+// these loads count exactly the loads issued after them.
+template <int D, int NW, int LW>
 struct ScanLoadOffs {
+  static constexpr int lw = LW;      // loader index 0 .. NW-1
   static constexpr int KJ = (ScanGeom<D, NW>::KU + NW - 1) / NW;
   static constexpr int VJ = (ScanGeom<D, NW>::VU + NW - 1) / NW;
   static constexpr int TJ = (ScanGeom<D, NW>::TU + NW - 1) / NW;
   uint32_t kq[KJ];
   uint32_t v[VJ];
   uint32_t t[TJ];
-  int lw;            // loader index 0 .. NW-1
   // loads m = lw, lw + NW, ... < U of a tile of U loads
-  static constexpr int share(int U, int lw) { return U > lw ? (U - 1 - lw) / NW + 1 : 0; }
-  static constexpr int qvt_loads(int lw) {
-    return share(ScanGeom<D, NW>::KU, lw) + share(ScanGeom<D, NW>::VU, lw) + share(ScanGeom<D, NW>::TU, lw);
+  static constexpr int share(int U) { return U > LW ? (U - 1 - LW) / NW + 1 : 0; }
+  static constexpr int qvt_loads() {
+    return share(ScanGeom<D, NW>::KU) + share(ScanGeom<D, NW>::VU) + share(ScanGeom<D, NW>::TU);
   }
 };
 
@@ -443,15 +468,15 @@ struct ScanLoadOffs {
 // (needed through the whole chunk), and Q, V, T (read before the middle of
 // the chunk, so they are fetched one chunk earlier into the buffer that the
 // chunk two steps back has released).
-template <int D, int NW>
-__device__ __forceinline__ void scan_issue_k(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
+template <int D, int NW, int LW>
+__device__ __forceinline__ void scan_issue_k(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW, LW>& lo,
                                              const ScanBuf& bf, int c) {
   using G = ScanGeom<D, NW>;
-  using L = ScanLoadOffs<D, NW>;
+  using L = ScanLoadOffs<D, NW, LW>;
   const int lane = threadIdx.x % 64;
   const size_t e0 = x.head0 + (size_t)c * x.chunk_elems;
   const auto rk = buf_rsrc(x.k + e0, chunk_bytes(x.T, c, x.tok_bytes, D));
-  if (lo.lw == 0) {
+  if constexpr (LW == 0) {
     const int valid = min(CH, x.T - c * CH);
     const auto rg = buf_rsrc(x.g_in + (x.tg0 + c) * CH, CH * 4);
     const auto rb = buf_rsrc(x.beta + x.beta0 + (size_t)c * CH * x.H, (uint32_t)((valid - 1) * x.H + 1) * 4);
@@ -460,16 +485,16 @@ __device__ __forceinline__ void scan_issue_k(const ScanCtx<D, NW>& x, const Scan
   }
 #pragma unroll
   for (int j = 0; j < L::KJ; ++j) {
-    const int m = lo.lw + NW * j;
-    if (m < G::KU) buf_to_lds16(rk, bf.K + 512 * m, lo.kq[j]);
+    const int m = LW + NW * j;
+    if (m < G::KU) buf_to_lds16(rk, bf.K + opaque_offset(512 * m), lo.kq[j]);
   }
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void scan_issue_qvt(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
+template <int D, int NW, int LW>
+__device__ __forceinline__ void scan_issue_qvt(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW, LW>& lo,
                                                const ScanBuf& bf, int c) {
   using G = ScanGeom<D, NW>;
-  using L = ScanLoadOffs<D, NW>;
+  using L = ScanLoadOffs<D, NW, LW>;
   const size_t e0 = x.head0 + (size_t)c * x.chunk_elems;
   const uint32_t nrec = chunk_bytes(x.T, c, x.tok_bytes, D);
   const auto rq = buf_rsrc(x.q + e0, nrec);
@@ -477,30 +502,19 @@ __device__ __forceinline__ void scan_issue_qvt(const ScanCtx<D, NW>& x, const Sc
   const auto rt = buf_rsrc(x.t_in + (x.tg0 + c) * CH * CH, CH * CH * 2);
 #pragma unroll
   for (int j = 0; j < L::TJ; ++j) {
-    const int m = lo.lw + NW * j;
-    if (m < G::TU) buf_to_lds16(rt, bf.T + 512 * m, lo.t[j]);
+    const int m = LW + NW * j;
+    if (m < G::TU) buf_to_lds16(rt, bf.T + opaque_offset(512 * m), lo.t[j]);
   }
 #pragma unroll
   for (int j = 0; j < L::VJ; ++j) {
-    const int m = lo.lw + NW * j;
-    if (m < G::VU) buf_to_lds16(rv, bf.V + 512 * m, lo.v[j]);
+    const int m = LW + NW * j;
+    if (m < G::VU) buf_to_lds16(rv, bf.V + opaque_offset(512 * m), lo.v[j]);
   }
 #pragma unroll
   for (int j = 0; j < L::KJ; ++j) {
-    const int m = lo.lw + NW * j;
-    if (m < G::KU) buf_to_lds16(rq, bf.Q + 512 * m, lo.kq[j]);
+    const int m = LW + NW * j;
+    if (m < G::KU) buf_to_lds16(rq, bf.Q + opaque_offset(512 * m), lo.kq[j]);
   }
-}
-
-// Wait until this loader wave's Q/V/T batch (the most recent one) is the
-// only one still in flight.
-template <int D, int NW>
-__device__ __forceinline__ void wait_all_but_qvt(int lw) {
-  using L = ScanLoadOffs<D, NW>;
-  if (lw == 0) wait_vmem_le<L::qvt_loads(0)>();
-  else if (lw == 1) wait_vmem_le<L::qvt_loads(1)>();
-  else if (lw == 2) wait_vmem_le<L::qvt_loads(2)>();
-  else wait_vmem_le<L::qvt_loads(3)>();
 }
 
 // 2^{g} and 2^{g_C - g} of a staged chunk (wave 0, after its loads landed)
@@ -742,28 +756,69 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
 }
 
 // Loader wave, one chunk c (buffer cb; nb is the other buffer): K, g, b of
+// Loader wave, one chunk c (buffer cb; nb is the other buffer): K, g, b of
 // chunk c+1 into nb; after the middle barrier, when chunk c no longer reads
 // its Q, V, T, the Q/V/T batch of chunk c+2 into cb; 2^{g} and 2^{g_C - g}
 // of chunk c+1.  Before the end barrier everything but the newest batch has
 // landed.  Two barriers per chunk, as in the compute waves.
-template <int D, int NW>
-__device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW>& lo,
+template <int D, int NW, int LW>
+__device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW, LW>& lo,
                                                 const ScanBuf& cb, const ScanBuf& nb, int c) {
-  using L = ScanLoadOffs<D, NW>;
+  using L = ScanLoadOffs<D, NW, LW>;
   const bool more1 = c + 1 < x.nchunks, more2 = c + 2 < x.nchunks;
-  if (more1) scan_issue_k<D, NW>(x, lo, nb, c + 1);
+  if (more1) scan_issue_k<D, NW, LW>(x, lo, nb, c + 1);
   lds_barrier();
-  if (more1 && lo.lw == 0) {
-    wait_vmem_le<L::share(ScanGeom<D, NW>::KU, 0)>();      // g and b of chunk c+1
-    scan_decays(nb);
+  if constexpr (LW == 0) {
+    if (more1) {
+      wait_vmem_le<L::share(ScanGeom<D, NW>::KU)>();      // g and b of chunk c+1
+      scan_decays(nb);
+    }
   }
   if (more2) {
-    scan_issue_qvt<D, NW>(x, lo, cb, c + 2);
-    wait_all_but_qvt<D, NW>(lo.lw);
+    scan_issue_qvt<D, NW, LW>(x, lo, cb, c + 2);
+    wait_vmem_le<L::qvt_loads()>();                         // all but the batch just issued
   } else {
     wait_vmem();
   }
   lds_barrier();
+}
+
+// One loader wave: its load offsets, the first two chunks, then one
+// scan_load_chunk per chunk.
+template <int D, int NW, int LW>
+__device__ __forceinline__ void scan_loader(const ScanCtx<D, NW>& x, const ScanBuf& B0, const ScanBuf& B1) {
+  using G = ScanGeom<D, NW>;
+  using L = ScanLoadOffs<D, NW, LW>;
+  constexpr int NR = G::NR;
+  const int lane = threadIdx.x % 64;
+  L lo;
+#pragma unroll
+  for (int j = 0; j < L::KJ; ++j) {
+    const int U = 64 * (LW + NW * j) + lane;
+    lo.kq[j] = (uint32_t)row_token(U / G::KU) * x.tok_bytes + (U % G::KU) % (D / 8) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < L::VJ; ++j) {
+    const int U = 64 * (LW + NW * j) + lane;
+    lo.v[j] = (uint32_t)row_token(U / G::VU) * x.tok_bytes + (U % G::VU) % (NR / 8) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < L::TJ; ++j) {
+    const int U = 64 * (LW + NW * j) + lane;
+    lo.t[j] = (uint32_t)row_token(U / G::TU) * (CH * 2) + (U % G::TU) % 8 * 16;
+  }
+  if (x.nchunks > 0) {
+    scan_issue_k<D, NW, LW>(x, lo, B0, 0);
+    scan_issue_qvt<D, NW, LW>(x, lo, B0, 0);
+    if (x.nchunks > 1) scan_issue_qvt<D, NW, LW>(x, lo, B1, 1);
+    wait_vmem();
+    if constexpr (LW == 0) scan_decays(B0);
+  }
+  lds_barrier();
+  for (int c = 0; c < x.nchunks; c += 2) {
+    scan_load_chunk<D, NW, LW>(x, lo, B0, B1, c);
+    if (c + 1 < x.nchunks) scan_load_chunk<D, NW, LW>(x, lo, B1, B0, c + 1);
+  }
 }
 
 // Workgroup: NW compute waves (16 rows of S each) and NW loader waves that
@@ -809,35 +864,16 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
   x.beta0 = (size_t)b * T * H + h;
 
   if (wave >= NW) {                   // ---- loader waves
-    using L = ScanLoadOffs<D, NW>;
-    L lo;
-    lo.lw = wave - NW;
-#pragma unroll
-    for (int j = 0; j < L::KJ; ++j) {
-      const int U = 64 * (lo.lw + NW * j) + lane;
-      lo.kq[j] = (uint32_t)row_token(U / G::KU) * x.tok_bytes + (U % G::KU) % (D / 8) * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < L::VJ; ++j) {
-      const int U = 64 * (lo.lw + NW * j) + lane;
-      lo.v[j] = (uint32_t)row_token(U / G::VU) * x.tok_bytes + (U % G::VU) % (NR / 8) * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < L::TJ; ++j) {
-      const int U = 64 * (lo.lw + NW * j) + lane;
-      lo.t[j] = (uint32_t)row_token(U / G::TU) * (CH * 2) + (U % G::TU) % 8 * 16;
-    }
-    if (x.nchunks > 0) {
-      scan_issue_k<D, NW>(x, lo, B0, 0);
-      scan_issue_qvt<D, NW>(x, lo, B0, 0);
-      if (x.nchunks > 1) scan_issue_qvt<D, NW>(x, lo, B1, 1);
-      wait_vmem();
-      if (lo.lw == 0) scan_decays(B0);
-    }
-    lds_barrier();
-    for (int c = 0; c < x.nchunks; c += 2) {
-      scan_load_chunk<D, NW>(x, lo, B0, B1, c);
-      if (c + 1 < x.nchunks) scan_load_chunk<D, NW>(x, lo, B1, B0, c + 1);
+    const int lw = wave - NW;
+    if (lw == 0) {
+      scan_loader<D, NW, 0>(x, B0, B1);
+    } else if constexpr (NW > 1) {
+      if (lw == 1) {
+        scan_loader<D, NW, 1>(x, B0, B1);
+      } else if constexpr (NW > 2) {
+        if (lw == 2) scan_loader<D, NW, 2>(x, B0, B1);
+        else scan_loader<D, NW, 3>(x, B0, B1);
+      }
     }
     return;
   }
