@@ -358,6 +358,7 @@ __device__ __forceinline__ int s_feature(int dt, int g) {   // cb(dt, g)
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 
@@ -395,7 +396,8 @@ template <int D, int NW>
 struct ScanGeom {
   static constexpr int NR = 16 * NW;                               // S rows per workgroup
   static constexpr int KST = D + 16;                               // K, Q row stride
-  static constexpr int VST = (NR % 32 == 0) ? NR + 16 : NR + 32;   // V slice row stride
+  static constexpr int VST = NR;                                   // V slice row stride
+  static constexpr int OST = NR + 8;                               // O staging row stride
   static constexpr int TST = CH + 16;                              // T, P row stride
   static constexpr int KU = KST / 8, VU = VST / 8, TU = TST / 8;   // 16-byte units per row
   // a tile of 64 rows x U units is exactly U loads of 64 lanes
@@ -438,7 +440,6 @@ struct ScanCtx {
   size_t beta0;          // element offset of (b, t = 0, h) in beta
   int T, H, nchunks, n_base, wave;
   uint32_t tok_bytes;
-  uint32_t o_off[4];
 };
 
 // Per-lane byte offsets of the loader wave's loads inside a chunk: load m of
@@ -526,24 +527,40 @@ __device__ __forceinline__ void scan_decays(const ScanBuf& bf) {
   bf.wts[lane] = __builtin_amdgcn_exp2f(gl - gv);
 }
 
-template <int D, int NW>
-__device__ __forceinline__ void scan_store_o(const ScanCtx<D, NW>& x, const uint2 (&o)[4], int c) {
-  const auto ro = buf_rsrc(x.out + x.head0 + (size_t)c * x.chunk_elems, chunk_bytes(x.T, c, x.tok_bytes, D));
+// O of chunk c from the staging tile (token-natural rows, this workgroup's
+// NR columns) to HBM: 2 stores of 16 bytes per lane per loader wave.  With
+// store = false the stores go to an empty range (nothing is written), so
+// that every chunk issues the same number of memory operations.
+template <int D, int NW, int LW>
+__device__ __forceinline__ void scan_store_o(const ScanCtx<D, NW>& x, const uint16_t* Os, int c, bool store) {
+  using G = ScanGeom<D, NW>;
+  constexpr int UPR = G::NR / 8;            // 16-byte units per row
+  const int lane = threadIdx.x % 64;
+  uint4 d[2];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) buf_store8(o[tt], ro, x.o_off[tt]);
+  for (int j = 0; j < 2; ++j) {
+    const int U = 64 * (LW + NW * j) + lane;
+    d[j] = *reinterpret_cast<const uint4*>(Os + (U / UPR) * G::OST + (U % UPR) * 8);
+  }
+  const auto ro = buf_rsrc(x.out + x.head0 + (size_t)c * x.chunk_elems + x.n_base,
+                           store ? chunk_bytes(x.T, c, x.tok_bytes, G::NR) : 0u);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int U = 64 * (LW + NW * j) + lane;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, d[j]), ro,
+                                           (uint32_t)(U / UPR) * x.tok_bytes + (U % UPR) * 16, 0, 0);
+  }
 }
 
 // One chunk of a compute wave: reads buffer cb.
 template <int D, int NW>
 __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBuf& cb,
-                                           uint16_t* Pb, f32x4 (&S)[D / 16], uint2 (&o_prev)[4], int c) {
+                                           uint16_t* Pb, uint16_t* Os, f32x4 (&S)[D / 16], int c) {
   using G = ScanGeom<D, NW>;
   constexpr int DT = D / 16, DS = D / 32;
   constexpr int KST = G::KST, VST = G::VST, TST = G::TST;
   const int lane = threadIdx.x % 64, l16 = lane % 16, g = lane / 16;
   const int wave = x.wave;
-
-  if (c > 0) scan_store_o<D, NW>(x, o_prev, c - 1);
 
   // LDS reads run ahead of the products that consume them: each step issues
   // the next step's reads before its own products (rings of two register
@@ -736,7 +753,8 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
       f32x4 o = f32x4{gmo[tt] * Y[tt][0], gmo[tt] * Y[tt][1], gmo[tt] * Y[tt][2], gmo[tt] * Y[tt][3]};
       o = mfma16x16x32(Eop0, as_bf16x8(po[tt]), o);
       if (tt >= 2) o = mfma16x16x32(Eop1, as_bf16x8(po[tt + 2]), o);
-      o_prev[tt] = pack_bf16x4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint2*>(Os + row_token(16 * tt + l16) * G::OST + 16 * wave + 4 * g) =
+          pack_bf16x4(o[0], o[1], o[2], o[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -756,21 +774,24 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
 }
 
 // Loader wave, one chunk c (buffer cb; nb is the other buffer): K, g, b of
-// Loader wave, one chunk c (buffer cb; nb is the other buffer): K, g, b of
-// chunk c+1 into nb; after the middle barrier, when chunk c no longer reads
-// its Q, V, T, the Q/V/T batch of chunk c+2 into cb; 2^{g} and 2^{g_C - g}
-// of chunk c+1.  Before the end barrier everything but the newest batch has
-// landed.  Two barriers per chunk, as in the compute waves.
+// chunk c+1 into nb, then O of chunk c-1 from the staging tile to HBM (the
+// compute waves overwrite it after the middle barrier); after that barrier,
+// when chunk c no longer reads its Q, V, T, the Q/V/T batch of chunk c+2 into
+// cb; 2^{g} and 2^{g_C - g} of chunk c+1.  Before the end barrier everything
+// but the newest batch has landed.  Two barriers per chunk, as in the compute
+// waves.
 template <int D, int NW, int LW>
 __device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW, LW>& lo,
-                                                const ScanBuf& cb, const ScanBuf& nb, int c) {
+                                                const ScanBuf& cb, const ScanBuf& nb, const uint16_t* Os,
+                                                int c) {
   using L = ScanLoadOffs<D, NW, LW>;
   const bool more1 = c + 1 < x.nchunks, more2 = c + 2 < x.nchunks;
   if (more1) scan_issue_k<D, NW, LW>(x, lo, nb, c + 1);
+  scan_store_o<D, NW, LW>(x, Os, c - 1, c > 0);
   lds_barrier();
   if constexpr (LW == 0) {
     if (more1) {
-      wait_vmem_le<L::share(ScanGeom<D, NW>::KU)>();      // g and b of chunk c+1
+      wait_vmem_le<L::share(ScanGeom<D, NW>::KU) + 2>();   // g and b of chunk c+1
       scan_decays(nb);
     }
   }
@@ -786,7 +807,8 @@ __device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const S
 // One loader wave: its load offsets, the first two chunks, then one
 // scan_load_chunk per chunk.
 template <int D, int NW, int LW>
-__device__ __forceinline__ void scan_loader(const ScanCtx<D, NW>& x, const ScanBuf& B0, const ScanBuf& B1) {
+__device__ __forceinline__ void scan_loader(const ScanCtx<D, NW>& x, const ScanBuf& B0, const ScanBuf& B1,
+                                            const uint16_t* Os) {
   using G = ScanGeom<D, NW>;
   using L = ScanLoadOffs<D, NW, LW>;
   constexpr int NR = G::NR;
@@ -816,9 +838,10 @@ __device__ __forceinline__ void scan_loader(const ScanCtx<D, NW>& x, const ScanB
   }
   lds_barrier();
   for (int c = 0; c < x.nchunks; c += 2) {
-    scan_load_chunk<D, NW, LW>(x, lo, B0, B1, c);
-    if (c + 1 < x.nchunks) scan_load_chunk<D, NW, LW>(x, lo, B1, B0, c + 1);
+    scan_load_chunk<D, NW, LW>(x, lo, B0, B1, Os, c);
+    if (c + 1 < x.nchunks) scan_load_chunk<D, NW, LW>(x, lo, B1, B0, Os, c + 1);
   }
+  if (x.nchunks > 0) scan_store_o<D, NW, LW>(x, Os, x.nchunks - 1, true);
 }
 
 // Workgroup: NW compute waves (16 rows of S each) and NW loader waves that
@@ -838,6 +861,7 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t V0[CH * G::VST], V1[CH * G::VST];
   __shared__ __attribute__((aligned(16))) uint16_t T0[CH * G::TST], T1[CH * G::TST];
   __shared__ __attribute__((aligned(16))) uint16_t Pb[CH * G::TST];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[CH * G::OST];
   __shared__ __attribute__((aligned(16))) float g0[CH], g1[CH], gam0[CH], gam1[CH];
   __shared__ __attribute__((aligned(16))) float w0[CH], w1[CH], b0[CH], b1[CH];
   const ScanBuf B0{K0, Q0, V0, T0, g0, gam0, w0, b0};
@@ -866,13 +890,13 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
   if (wave >= NW) {                   // ---- loader waves
     const int lw = wave - NW;
     if (lw == 0) {
-      scan_loader<D, NW, 0>(x, B0, B1);
+      scan_loader<D, NW, 0>(x, B0, B1, Os);
     } else if constexpr (NW > 1) {
       if (lw == 1) {
-        scan_loader<D, NW, 1>(x, B0, B1);
+        scan_loader<D, NW, 1>(x, B0, B1, Os);
       } else if constexpr (NW > 2) {
-        if (lw == 2) scan_loader<D, NW, 2>(x, B0, B1);
-        else scan_loader<D, NW, 3>(x, B0, B1);
+        if (lw == 2) scan_loader<D, NW, 2>(x, B0, B1, Os);
+        else scan_loader<D, NW, 3>(x, B0, B1, Os);
       }
     }
     return;
@@ -880,9 +904,6 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
 
   // ---- compute waves
   const int n_w = x.n_base + 16 * wave;     // first S row of this wave
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-    x.o_off[tt] = (uint32_t)row_token(16 * tt + l16) * x.tok_bytes + (uint32_t)(n_w + 4 * g) * 2;
 
   f32x4 S[DT];
   if (state_in) {
@@ -898,12 +919,10 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
   }
   lds_barrier();                      // chunk 0 has landed
 
-  uint2 o_prev[4] = {make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0)};
   for (int c = 0; c < x.nchunks; c += 2) {
-    scan_chunk<D, NW>(x, B0, Pb, S, o_prev, c);
-    if (c + 1 < x.nchunks) scan_chunk<D, NW>(x, B1, Pb, S, o_prev, c + 1);
+    scan_chunk<D, NW>(x, B0, Pb, Os, S, c);
+    if (c + 1 < x.nchunks) scan_chunk<D, NW>(x, B1, Pb, Os, S, c + 1);
   }
-  if (x.nchunks > 0) scan_store_o<D, NW>(x, o_prev, x.nchunks - 1);
 
   if (state_out) {
     float* dst = state_out + ((size_t)bh * D + n_w + l16) * D;
