@@ -49,8 +49,16 @@ namespace kairos {
 constexpr int WD = 128;          // head dimension
 constexpr int BQ = 128;          // queries per workgroup
 constexpr int BK = 64;           // keys per block
-constexpr int KST = WD + 16;     // bf16 K and V LDS row stride (elements): 16 mod 32
-constexpr int K8ST = WD + 16;    // E4M3 K LDS row stride (bytes)
+constexpr int KST = WD + 16;     // bf16 K LDS row stride (elements): 16 mod 32
+constexpr int K8ST = WD;         // E4M3 K LDS row stride (bytes), 16-byte units XOR-swizzled
+constexpr int VST = 2 * WD;      // V LDS row stride (bytes), 16-byte units XOR-swizzled
+
+// Unpadded K (E4M3) and V rows in LDS: 16-byte unit u of row r is stored in
+// slot u ^ f(r).  Measured on gfx950, both keep their reads (the 32-row
+// operand reads of K, the transposed 4-row reads of V) as fast as padded rows
+// (V faster), with fewer loads per block.
+__device__ __forceinline__ constexpr int k8_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ constexpr int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 constexpr float RESCALE_SLACK = 8.f;
 
 typedef short wshort4 __attribute__((ext_vector_type(4)));
@@ -77,8 +85,8 @@ __device__ __forceinline__ void win_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0
 // unit 64 m + l).
 template <bool FP8>
 struct WinGeom {
-  static constexpr int KU = FP8 ? K8ST / 16 : KST * 2 / 16;   // units per K row (9 / 18)
-  static constexpr int VU = KST * 2 / 16;                     // units per V row (18)
+  static constexpr int KU = FP8 ? K8ST / 16 : KST * 2 / 16;   // units per K row (8 / 18)
+  static constexpr int VU = VST / 16;                         // units per V row (16)
   static constexpr int KBYTES = BK * KU * 16;
   static constexpr int VBYTES = BK * VU * 16;
   static constexpr int NLOAD = KU + VU + (FP8 ? 1 : 0);       // loads per block (all waves)
@@ -137,6 +145,8 @@ __device__ __forceinline__ constexpr int key_of(int kt, int r, int g) {
 struct QueryCtx {
   int b, h, mq, mw_lo, mw_hi, krow, ql, g, wave;
   float cq;
+  int k8o[2][2];   // E4M3 K: byte offset of this lane's operand halves (step s, half) in a 32-row tile
+  int vo[4][2];    // V: byte offset of this lane's transposed reads (feature tile dt, rows +0 / +4)
 };
 
 // One LDS buffer of a key block (pointers into separate __shared__ variables).
@@ -175,9 +185,9 @@ __device__ __forceinline__ void win_load_setup(WinLoads<FP8>& ld, int wave, int 
     else if (e < G::KU + G::VU) { U = 64 * (e - G::KU) + lane; upr = G::VU; }
     else { U = lane; upr = 1; }                      // scales: one per key
     ld.row[j] = U / upr;
-    const int u = U % upr;
-    if (e < G::KU) ld.col[j] = FP8 ? (u % 8) * 16 : (u % 16) * 16;     // padding units copy a real unit
-    else if (e < G::KU + G::VU) ld.col[j] = (u % 16) * 16;
+    const int u = U % upr;                           // LDS slot of the row
+    if (e < G::KU) ld.col[j] = FP8 ? (u ^ k8_swz(ld.row[j])) * 16 : (u % 16) * 16;   // bf16: padding copies a unit
+    else if (e < G::KU + G::VU) ld.col[j] = (u ^ v_swz(ld.row[j])) * 16;
     else ld.col[j] = 0;
   }
 }
@@ -259,11 +269,11 @@ __device__ __forceinline__ void win_block(const WinArgs& a, const WinBuf& cb, co
       for (int s = 0; s < 8; ++s)
         S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * qc.g)), qf[s], S[kt]);
     } else {
-      const uint8_t* K8 = cb.K + (32 * kt + qc.krow) * K8ST;
+      const uint8_t* K8 = cb.K + 32 * kt * K8ST;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g);
-        const uint4 hi = *reinterpret_cast<const uint4*>(K8 + 64 * s + 32 * qc.g + 16);
+        const uint4 lo = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][0]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][1]);
         const i32x8 ka = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         S[kt] = mfma32x32x64_fp8(ka, q8f[s], S[kt]);
@@ -326,17 +336,17 @@ __device__ __forceinline__ void win_block(const WinArgs& a, const WinBuf& cb, co
   }
   // ---- O^T += V^T P^T   (lane: O^T[32dt + 8(r/4) + 4g + r%4][query ql]); the
   //      V^T operand of (kt, j): features 32 dt + lane%32, keys 32 kt + 16 j + 8 g + 0..7
-  const int lane = threadIdx.x % 64;
-  const int G16 = lane / 16, s16 = lane % 16;
-  const uint16_t* vbase = cb.V + (8 * (G16 / 2) + s16 / 4) * KST + 16 * (G16 % 2) + 4 * (s16 % 4);
+  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(cb.V);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint16_t* vp = vbase + (32 * kt + 16 * j) * KST + 32 * dt;
-        O[dt] = mfma32x32x16(as_bf16x8(win_read_tr(vp), win_read_tr(vp + 4 * KST)), P[kt][j], O[dt]);
+        const uint8_t* vp = Vb + (32 * kt + 16 * j) * VST;
+        O[dt] = mfma32x32x16(as_bf16x8(win_read_tr(reinterpret_cast<const uint16_t*>(vp + qc.vo[dt][0])),
+                                       win_read_tr(reinterpret_cast<const uint16_t*>(vp + qc.vo[dt][1]))),
+                             P[kt][j], O[dt]);
       }
 }
 
@@ -422,6 +432,26 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   qc.mw_hi = min(m0 + 32 * wave + 31, m_last_wg);
   // score row of this lane's A operand: key pi(ql) of each 32-key tile
   qc.krow = 16 * (qc.ql / 16) + 8 * ((qc.ql / 4) & 1) + 4 * ((qc.ql / 8) & 1) + (qc.ql & 3);
+  // E4M3 K operand: row krow (+32 kt, which leaves the swizzle unchanged),
+  // bytes 64 s + 32 g + 16 half
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      qc.k8o[s2][hh] = qc.krow * K8ST + 16 * ((4 * s2 + 2 * qc.g + hh) ^ k8_swz(qc.krow));
+  // V^T operand of feature tile dt: rows 8 (G16/2) + s16/4 (+4), features
+  // 32 dt + 16 (G16 % 2) + 4 (s16 % 4) .. +3 (+32 kt + 16 j rows leave the swizzle unchanged)
+  {
+    const int G16 = lane / 16, s16 = lane % 16;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 8 * (G16 / 2) + s16 / 4 + 4 * e;
+        const int cb = 2 * (32 * dt + 16 * (G16 % 2) + 4 * (s16 % 4));
+        qc.vo[dt][e] = r * VST + 16 * ((cb / 16) ^ v_swz(r)) + (cb & 15);
+      }
+  }
   const int b = qc.b, h = qc.h, g = qc.g;
 
   WinLoads<FP8> ld;
