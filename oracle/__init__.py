@@ -19,7 +19,10 @@ Physical AI" (arXiv 2606.16533, HTML v3):
                rearrange-then-SWA form of Eq. 8, and a scalar brute force;
 * ``fp8``    -- an OCP FP8 E4M3 quantiser with per-64-token-block absmax
                scales, written from the format definition;
-* ``hlta``   -- the gated combination of the three branches.
+* ``hlta``   -- the gated combination of the three branches;
+* ``prologue`` -- the inputs of the gated delta rule from raw keys and gate
+               logits (L2 normalisation, sigmoids of Eq. 1 and Eq. 4, and the
+               rescaling that turns the printed Eq. 6 into the canonical form).
 
 Readings of points the paper leaves open are listed in each function's
 docstring.  Every function is pinned by tests against closed forms,
@@ -31,11 +34,12 @@ from .window import (windowed_attention, windowed_attention_rows, window_brutefo
                      dswa_reshape, frame_index_maps)
 from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, fp8_quantize_blocks, E4M3_MAX
 from .hlta import hlta, hlta_rows, sigmoid
+from .prologue import l2_normalize, gdn_prologue
 
 __all__ = [
     "gdn_recurrent", "gdn_literal_eq6", "gdn_chunked",
     "windowed_attention", "windowed_attention_rows", "window_bruteforce", "dswa_reshape",
     "frame_index_maps",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "fp8_quantize_blocks", "E4M3_MAX",
-    "hlta", "hlta_rows", "sigmoid",
+    "hlta", "hlta_rows", "sigmoid", "l2_normalize", "gdn_prologue",
 ]
