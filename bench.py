@@ -120,6 +120,8 @@ class StageTimer:
 
     def run(self, name, fn, reps):
         torch = self.torch
+        fn()                                        # untimed: first launch loads the kernel
+        torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         for a, b in ev:
@@ -213,6 +215,26 @@ def main():
         codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
         k_scales=sk, out=bufs["out"], workspace=yws), reps)
 
+    # input prologue of the gated delta rule on the same shape: raw keys and
+    # gate logits -> unit keys and gates ("k": the canonical inputs), and with
+    # query normalisation and the printed-Eq.-6 rescaling ("qk_literal": every
+    # stream the kernel can move)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 7)
+    za = 4.0 - torch.randn((w.B, w.T, w.H), generator=gen, device=dev)
+    zb = torch.randn((w.B, w.T, w.H), generator=gen, device=dev)
+    p_k, p_q, p_v = (torch.empty_like(d["v"]) for _ in range(3))
+    p_a, p_b = torch.empty_like(za), torch.empty_like(zb)
+    t_pro_k = st.run("gdn_prologue_k", lambda: K.kairos_gdn_prologue(
+        d["q"], za, zb, k_out=p_k, alpha_out=p_a, beta_out=p_b), reps)
+    t_pro_all = st.run("gdn_prologue_qk_literal", lambda: K.kairos_gdn_prologue(
+        d["q"], za, zb, q=d["k"], v=d["v"], literal=True, k_out=p_k, alpha_out=p_a, beta_out=p_b,
+        q_out=p_q, v_out=p_v), reps)
+    rows = w.B * w.T * w.H
+    pro_bytes = {"gdn_prologue_k": rows * (2 * w.d * 2 + 16),
+                 "gdn_prologue_qk_literal": rows * (6 * w.d * 2 + 16)}
+    del p_k, p_q, p_v, p_a, p_b, za, zb
+
     pairs = window_pairs(w.T, w.L, w.window, 1) + window_pairs(w.T, w.L, w.window, w.dilation)
     win_flops = pairs * 4 * w.d * w.B * w.H          # QK^T 2d + PV 2d per (query, key) pair
     if fp8:
@@ -229,14 +251,16 @@ def main():
     # HBM traffic of the kernel from the committed counter summary, valid only
     # while the kernel's sources are the ones the counters were taken on
     cpath = os.path.join(ROOT, "profiles", "hlta_fp8_B4H24F16L3600_hbm_counters.txt")
+    cnt = {}
     if fp8 and os.path.exists(cpath):
-        cnt = {}
         for line in open(cpath):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 cnt[key.strip()] = val.strip()
-        if cnt.get("win_attn_kernel.source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
-            roofline["traffic"] = float(cnt["win_attn_kernel.traffic_bytes_per_launch"])
+    if cnt.get("win_attn_kernel.source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
+        roofline["traffic"] = float(cnt["win_attn_kernel.traffic_bytes_per_launch"])
+    pro_fresh = cnt.get("gdn_prologue_kernel.source_sha") == src_sha("prologue.hip", "common.hpp",
+                                                                    "launch.hpp")
 
     gdn_tok_heads = w.B * w.T * w.H
     gdn_bytes = gdn_tok_heads * GDN_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * w.d * w.d * 4
@@ -252,6 +276,13 @@ def main():
         },
         "window_stage": {"ms": round(t_win, 4), "alg_TFLOP_per_s": round(achieved, 1),
                          "pairs_per_bh": pairs},
+        "gdn_prologue": {
+            name: {"ms": round(t, 4), "alg_bytes": pro_bytes[name],
+                   "alg_GB_per_s": round(pro_bytes[name] / (t / 1e3) / 1e9, 1),
+                   "hbm_frac": round(pro_bytes[name] / (t / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "traffic": (float(cnt[name + ".traffic_bytes_per_launch"])
+                               if pro_fresh and name + ".traffic_bytes_per_launch" in cnt else None)}
+            for name, t in (("gdn_prologue_k", t_pro_k), ("gdn_prologue_qk_literal", t_pro_all))},
     }
     del codes_q, codes_k, o_gdn, d, bufs
     torch.cuda.empty_cache()

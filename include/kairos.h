@@ -6,7 +6,8 @@
  *
  * Source of the operations: "Kairos: A Regret-Aware Native World-Action
  * Model Stack for Physical AI" (arXiv 2606.16533, HTML v3):
- *   Sec. 2.2.1, Eq. 1-6 and step 4    gated delta rule, read-out o_t = S_t q_t
+ *   Sec. 2.2.1, Eq. 1-6 and step 4    gated delta rule, read-out o_t = S_t q_t;
+ *                                     its inputs: sigmoid gates (Eq. 1, 4), unit keys
  *   Sec. 2.2.2, Eq. 7                 sliding-window attention, w = L x window_size
  *   Sec. 2.2.2, Eq. 8                 dilated SWA on the frame-rearranged sequence
  *   Sec. 2.2.2, "Long-Horizon Generation"  recurrent state passing, constant memory per step
@@ -116,7 +117,9 @@ int kairos_hlta_ring_frames_required(const kairos_hlta_desc* desc, int32_t* fram
 
 /* Gated delta rule forward (Sec. 2.2.1, Eq. 1-6 canonical form, step 4).
  *   q, k, v      [B][T][H][d]  io type; k L2-normalised per (token, head)
- *   alpha, beta  [B][T][H]     fp32, alpha in (0, 1], beta in [0, 1]
+ *   alpha, beta  [B][T][H]     fp32, alpha in (0, 1], beta >= 0 (beta <= 1 for the
+ *                canonical form; the printed Eq. 6 form of kairos_gdn_prologue
+ *                passes beta / alpha, which may exceed 1)
  *   state_in     [B][H][d][d]  fp32 initial memory; NULL means zero
  *   out          [B][T][H][d]  io type, o_t = S_t q_t; must not overlap inputs
  *   state_out    [B][H][d][d]  fp32 final memory; NULL discards it; may equal
@@ -170,6 +173,44 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
                            const void* o_gdn, const float* gate_logits, const void* k_ring,
                            const void* v_ring, void* out, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* Flags of kairos_gdn_prologue. */
+typedef enum {
+  KAIROS_PROLOGUE_NORMALIZE_Q = 1,   /* also L2-normalise q                          */
+  KAIROS_PROLOGUE_LITERAL_EQ6 = 2    /* emit the inputs of the printed Eq. 6 form    */
+} kairos_prologue_flags;
+
+/* Input prologue of the gated delta rule: turns raw per-token keys and gate
+ * logits into the inputs kairos_gdn_fwd / kairos_hlta_fwd take (Sec. 2.2.1:
+ * Eq. 1 beta = sig(z_beta); Eq. 4 alpha = sig(z_alpha); Eq. 2-3 take unit
+ * keys).  Per (token, head) row:
+ *   k_out     = k_in / ||k_in||_2                  (a zero row stays zero)
+ *   q_out     = q_in / ||q_in||_2                  with KAIROS_PROLOGUE_NORMALIZE_Q
+ *   alpha_out = sig(alpha_logits)
+ *   beta_out  = sig(beta_logits)
+ * With KAIROS_PROLOGUE_LITERAL_EQ6 the outputs make the canonical recurrence
+ * equal to Eq. 6 as printed (erasing with the un-decayed retrieval
+ * S_{t-1} k_t): beta_out = sig(beta_logits) / sig(alpha_logits) and
+ * v_out = sig(alpha_logits) * v_in (rounded to the io type); alpha_out is
+ * unchanged.  That form needs sig(alpha_logits) > 0 in fp32: alpha_logits
+ * >= -80; below, beta_out overflows.
+ *   desc          as for kairos_gdn_fwd (io KAIROS_F32 or KAIROS_BF16); only
+ *                 B, T, H, dk and io are used; chunk must still be 64
+ *   k_in, k_out   [B][T][H][d] io type
+ *   alpha_logits, beta_logits, alpha_out, beta_out   [B][T][H] fp32
+ *   q_in, q_out   [B][T][H][d] io type with KAIROS_PROLOGUE_NORMALIZE_Q, else NULL
+ *   v_in, v_out   [B][T][H][d] io type with KAIROS_PROLOGUE_LITERAL_EQ6, else NULL
+ * Arithmetic is fp32 (the norm after an exact power-of-two rescaling of each
+ * row by its largest magnitude, so tiny or huge rows still normalise);
+ * bf16 outputs are rounded to nearest even.  Inputs must be finite.  Each
+ * output may be the same buffer as its own input (in place: k_out == k_in,
+ * alpha_out == alpha_logits, ...); any other overlap is KAIROS_ERR_ALIAS.
+ * A pointer given for a tensor its flag does not ask for is
+ * KAIROS_ERR_UNSUPPORTED, as is an unknown flag bit.  T == 0 does nothing. */
+int kairos_gdn_prologue(const kairos_gdn_desc* desc, int32_t flags, const void* k_in,
+                        const float* alpha_logits, const float* beta_logits, const void* q_in,
+                        const void* v_in, void* k_out, float* alpha_out, float* beta_out,
+                        void* q_out, void* v_out, void* stream);
 
 /* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block):
  * s = amax / 448 (fp32; 1 when amax == 0), code = E4M3(x / s) with an IEEE

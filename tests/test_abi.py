@@ -159,6 +159,37 @@ def test_window_and_quantiser_validation():
     assert L.kairos_fp8_quantize(None, None, None, 1, 0, 2, 128, None) == OK   # empty: nothing to do
 
 
+@host_only
+def test_prologue_validation():
+    L = K.lib()
+    cv = lambda x: None if x is None else ctypes.c_void_p(x)
+    d = K.gdn_desc(2, 100, 3, 128)
+    nx = 2 * 100 * 3 * 128 * 2
+
+    def call(flags=0, k=1 * G, za=2 * G, zb=3 * G, q=None, v=None, ko=4 * G, ao=5 * G, bo=6 * G,
+             qo=None, vo=None, desc=d):
+        return L.kairos_gdn_prologue(ctypes.byref(desc), flags, cv(k), cv(za), cv(zb), cv(q), cv(v),
+                                     cv(ko), cv(ao), cv(bo), cv(qo), cv(vo), None)
+
+    assert call(flags=4) == UNSUP                           # unknown flag bit
+    assert call(q=7 * G) == UNSUP                           # q without its flag
+    assert call(v=7 * G, vo=8 * G) == UNSUP                 # v without the literal flag
+    assert call(flags=K.PROLOGUE_NORMALIZE_Q) == NULL       # q pointers missing
+    assert call(flags=K.PROLOGUE_LITERAL_EQ6, v=7 * G) == NULL
+    assert call(k=None) == NULL
+    assert call(bo=None) == NULL
+    assert call(k=1 * G + 8) == ALIGN
+    assert call(za=2 * G + 2) == ALIGN
+    assert call(ko=1 * G + nx // 2) == ALIAS                # partial overlap with its own input
+    assert call(ko=2 * G) == ALIAS                          # k_out over the decay logits
+    assert call(ao=6 * G) == ALIAS                          # two outputs on one buffer
+    assert call(flags=K.PROLOGUE_LITERAL_EQ6, v=7 * G, vo=4 * G) == ALIAS
+    assert call(desc=K.gdn_desc(1, 64, 2, 96)) == SHAPE
+    assert call(desc=K.gdn_desc(1, 64, 2, 128, io=K.FP8_E4M3)) == DTYPE
+    assert call(desc=K.gdn_desc(1, 0, 2, 128), k=None, za=None, zb=None, ko=None, ao=None,
+                bo=None) == OK                             # empty: nothing to do
+
+
 def test_binding_rejects_bad_tensors_on_cpu():
     import torch
     q = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)

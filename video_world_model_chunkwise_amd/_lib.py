@@ -6,6 +6,7 @@ import os
 from ctypes import POINTER, byref, c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
+PROLOGUE_NORMALIZE_Q, PROLOGUE_LITERAL_EQ6 = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libkairos.so")
@@ -15,6 +16,7 @@ symbols = (
     "kairos_status_string", "kairos_version", "kairos_gdn_workspace_size",
     "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
     "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
+    "kairos_gdn_prologue",
 )
 
 
@@ -57,6 +59,7 @@ def lib():
         L.kairos_window_fwd.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 9
         L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p]
         L.kairos_hlta_window_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_size_t, c_void_p]
+        L.kairos_gdn_prologue.argtypes = [POINTER(GdnDesc), c_int32] + [c_void_p] * 11
         L.kairos_fp8_quantize.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                           c_int32, c_void_p]
         for name in symbols:
@@ -299,3 +302,50 @@ def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, fra
                                       _ptr(v_ring), _ptr(out), _ptr(ws), nws, _stream(stream))
     _check(st, "kairos_hlta_window_fwd")
     return out
+
+
+def kairos_gdn_prologue(k, alpha_logits, beta_logits, q=None, v=None, literal=False,
+                        k_out=None, alpha_out=None, beta_out=None, q_out=None, v_out=None,
+                        stream=None):
+    """Inputs of the gated delta rule from raw keys and gate logits.  k (and q
+    when given) [B, T, H, d] bf16 or fp32 are L2-normalised per row;
+    alpha = sigmoid(alpha_logits), beta = sigmoid(beta_logits) ([B, T, H]
+    fp32).  literal=True (needs v) returns beta / alpha and alpha * v instead,
+    the inputs under which the canonical recurrence is Eq. 6 as printed.
+    Outputs may be passed in, also as the inputs themselves (in place).
+    Returns (k_out, alpha_out, beta_out, q_out or None, v_out or None)."""
+    torch = _torch()
+    B, T, H, d = k.shape
+    dev = k.device
+    io = F32 if k.dtype == torch.float32 else BF16
+    _need(k, "k", k.dtype, (B, T, H, d), dev)
+    _need(alpha_logits, "alpha_logits", torch.float32, (B, T, H), dev)
+    _need(beta_logits, "beta_logits", torch.float32, (B, T, H), dev)
+    if q is not None:
+        _need(q, "q", k.dtype, (B, T, H, d), dev)
+    if literal:
+        _need(v, "v", k.dtype, (B, T, H, d), dev)
+    elif v is not None or v_out is not None:
+        raise ValueError("v is rescaled only in the literal form")
+    if q is None and q_out is not None:
+        raise ValueError("q_out given without q")
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    alpha_out = torch.empty_like(alpha_logits) if alpha_out is None else alpha_out
+    beta_out = torch.empty_like(beta_logits) if beta_out is None else beta_out
+    _need(k_out, "k_out", k.dtype, (B, T, H, d), dev)
+    _need(alpha_out, "alpha_out", torch.float32, (B, T, H), dev)
+    _need(beta_out, "beta_out", torch.float32, (B, T, H), dev)
+    if q is not None:
+        q_out = torch.empty_like(q) if q_out is None else q_out
+        _need(q_out, "q_out", k.dtype, (B, T, H, d), dev)
+    if literal:
+        v_out = torch.empty_like(v) if v_out is None else v_out
+        _need(v_out, "v_out", k.dtype, (B, T, H, d), dev)
+    flags = (PROLOGUE_NORMALIZE_Q if q is not None else 0) | (PROLOGUE_LITERAL_EQ6 if literal else 0)
+    desc = gdn_desc(B, T, H, d, io)
+    st = lib().kairos_gdn_prologue(byref(desc), flags, _ptr(k), _ptr(alpha_logits),
+                                   _ptr(beta_logits), _ptr(q), _ptr(v if literal else None),
+                                   _ptr(k_out), _ptr(alpha_out), _ptr(beta_out), _ptr(q_out),
+                                   _ptr(v_out), _stream(stream))
+    _check(st, "kairos_gdn_prologue")
+    return k_out, alpha_out, beta_out, q_out, v_out

@@ -359,6 +359,60 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   return KAIROS_OK;
 }
 
+int kairos_gdn_prologue(const kairos_gdn_desc* desc, int32_t flags, const void* k_in,
+                        const float* alpha_logits, const float* beta_logits, const void* q_in,
+                        const void* v_in, void* k_out, float* alpha_out, float* beta_out,
+                        void* q_out, void* v_out, void* stream) {
+  int st = check_gdn_desc(desc);
+  if (st != KAIROS_OK) return st;
+  if (flags & ~(KAIROS_PROLOGUE_NORMALIZE_Q | KAIROS_PROLOGUE_LITERAL_EQ6))
+    return KAIROS_ERR_UNSUPPORTED;
+  const bool nq = (flags & KAIROS_PROLOGUE_NORMALIZE_Q) != 0;
+  const bool lit = (flags & KAIROS_PROLOGUE_LITERAL_EQ6) != 0;
+  if (!nq && (q_in || q_out)) return KAIROS_ERR_UNSUPPORTED;
+  if (!lit && (v_in || v_out)) return KAIROS_ERR_UNSUPPORTED;
+  if (desc->T == 0) return KAIROS_OK;
+  if (!k_in || !k_out || !alpha_logits || !beta_logits || !alpha_out || !beta_out)
+    return KAIROS_ERR_NULL;
+  if (nq && (!q_in || !q_out)) return KAIROS_ERR_NULL;
+  if (lit && (!v_in || !v_out)) return KAIROS_ERR_NULL;
+  if (!aligned16(k_in) || !aligned16(k_out) || !aligned16(q_in) || !aligned16(q_out) ||
+      !aligned16(v_in) || !aligned16(v_out))
+    return KAIROS_ERR_ALIGN;
+  if (((uintptr_t)alpha_logits | (uintptr_t)beta_logits | (uintptr_t)alpha_out |
+       (uintptr_t)beta_out) & 3u)
+    return KAIROS_ERR_ALIGN;
+  const long rows = (long)desc->B * desc->T * desc->H;
+  const size_t nx = (size_t)rows * desc->dk * (desc->io == KAIROS_F32 ? 4 : 2);
+  const size_t ng = (size_t)rows * 4;
+  // outputs[i] may coincide exactly with inputs[i] and overlap nothing else
+  const void* ins[5] = {k_in, alpha_logits, beta_logits, q_in, v_in};
+  const void* outs[5] = {k_out, alpha_out, beta_out, q_out, v_out};
+  const size_t sz[5] = {nx, ng, ng, nx, nx};
+  for (int i = 0; i < 5; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 5; ++j) {
+      if (j != i && overlaps(outs[i], sz[i], ins[j], sz[j])) return KAIROS_ERR_ALIAS;
+      if (j != i && overlaps(outs[i], sz[i], outs[j], sz[j])) return KAIROS_ERR_ALIAS;
+    }
+    if (outs[i] != ins[i] && overlaps(outs[i], sz[i], ins[i], sz[i])) return KAIROS_ERR_ALIAS;
+  }
+  PrologueArgs a;
+  a.k_in = k_in;
+  a.q_in = q_in;
+  a.v_in = v_in;
+  a.za = alpha_logits;
+  a.zb = beta_logits;
+  a.k_out = k_out;
+  a.q_out = q_out;
+  a.v_out = v_out;
+  a.alpha = alpha_out;
+  a.beta = beta_out;
+  a.rows = rows;
+  return hip_status(launch_gdn_prologue(a, desc->dk, desc->io == KAIROS_F32, nq, lit,
+                                        (hipStream_t)stream));
+}
+
 int kairos_fp8_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
                         int32_t H, int32_t d, void* stream) {
   if (B < 1 || H < 1 || T < 0) return KAIROS_ERR_SHAPE;

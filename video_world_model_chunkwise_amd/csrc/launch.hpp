@@ -24,6 +24,25 @@ struct WinArgs {
   long frame_offset;
 };
 
+// Arguments of the gated-delta-rule input prologue (one row = one (token, head)).
+struct PrologueArgs {
+  const void* k_in;         // [rows][D] io type
+  const void* q_in;         // [rows][D] or null (query not normalised)
+  const void* v_in;         // [rows][D] or null (canonical form)
+  const float* za;          // [rows] decay logits
+  const float* zb;          // [rows] write-strength logits
+  void* k_out;
+  void* q_out;
+  void* v_out;
+  float* alpha;             // [rows]
+  float* beta;              // [rows]
+  long rows;
+};
+
+// fp32 io when f32, else bf16; D in {32, 64, 128}
+hipError_t launch_gdn_prologue(const PrologueArgs& args, int D, bool f32, bool normalize_q,
+                               bool literal, hipStream_t stream);
+
 hipError_t launch_gdn_f32(const float* q, const float* k, const float* v, const float* alpha,
                           const float* beta, const float* state_in, float* out, float* state_out,
                           int B, int T, int H, int D, hipStream_t stream);

@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "workload", "make_inputs", "make_custom",
+    "Workload", "WORKLOADS", "workload", "make_inputs", "make_custom", "make_raw",
     "to_bf16_bits", "bf16_bits_to_f32", "round_bf16",
 ]
 
@@ -183,6 +183,39 @@ def make_custom(B: int, T: int, H: int, d: int, io: str = "bf16", seed: int = 0,
         out.update(q=q, k=k, v=v)
     else:
         raise ValueError(io)
+    return out
+
+
+def make_raw(B: int, T: int, H: int, d: int, io: str = "bf16", seed: int = 0) -> dict:
+    """Raw per-token inputs of the gated delta rule's input prologue.
+
+    q, k, v standard normal fp32 ``[B, T, H, d]`` (keys NOT normalised),
+    decay logits ``za = -x`` with x ~ N(-4, 1) (so sigmoid(za) is the
+    softplus workloads' decay exp(-softplus(x))), write-strength logits
+    ``zb`` ~ N(0, 1), both fp32 ``[B, T, H]``.  Seeded like make_custom
+    (SeedSequence(seed) spawned into five streams: q, k, v, za, zb).  For
+    ``io == "bf16"`` q, k, v are rounded to bf16 and ``*_bits`` hold the
+    patterns.
+    """
+    import concurrent.futures as cf
+    sq, sk, sv, sa, sb = np.random.SeedSequence(seed).spawn(5)
+    shape = (B, T, H, d)
+    with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as pool:
+        q = _normal_chunked(sq, shape, pool)
+        k = _normal_chunked(sk, shape, pool)
+        v = _normal_chunked(sv, shape, pool)
+    ra, rb = (np.random.Generator(np.random.PCG64(x)) for x in (sa, sb))
+    za = -(ra.standard_normal((B, T, H), dtype=np.float32) - np.float32(4.0))
+    zb = rb.standard_normal((B, T, H), dtype=np.float32)
+    out = dict(za=za, zb=zb)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if io == "bf16":
+            out[name + "_bits"] = to_bf16_bits(x)
+            out[name] = bf16_bits_to_f32(out[name + "_bits"])
+        elif io == "f32":
+            out[name] = x
+        else:
+            raise ValueError(io)
     return out
 
 
