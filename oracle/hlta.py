@@ -16,6 +16,8 @@ Readings:
   (per-64-token-block absmax e4m3); the GDN branch uses the unquantised q, k.
 * A streamed rollout (frames fed call by call, state carried) is defined to
   equal one call over the whole sequence; the oracle is that single call.
+* ``centered=True`` gives both windowed branches Eq. 7's centred band (see
+  ``window``); such a layer sees future frames and has no streamed form.
 """
 from __future__ import annotations
 
@@ -40,7 +42,7 @@ def _window_inputs(q, k, window_qk):
 
 
 def hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, rows, frame_offset=0,
-              state_in=None, window_qk="bf16", o_gdn=None):
+              state_in=None, window_qk="bf16", o_gdn=None, centered=False):
     """Layer output for the query tokens ``rows`` (all heads) and final state.
 
     The GDN branch needs every token before the last requested row; it is
@@ -51,8 +53,8 @@ def hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, rows, frame_offset=0,
     if o_gdn is None:
         o_gdn, S = gdn_recurrent(q, k, v, alpha, beta, state_in)
     qw, kw = _window_inputs(q, k, window_qk)
-    o_swa = windowed_attention_rows(qw, kw, v, rows, L, w, 1, frame_offset)
-    o_dswa = windowed_attention_rows(qw, kw, v, rows, L, w, dil, frame_offset)
+    o_swa = windowed_attention_rows(qw, kw, v, rows, L, w, 1, frame_offset, centered)
+    o_dswa = windowed_attention_rows(qw, kw, v, rows, L, w, dil, frame_offset, centered)
     g = sigmoid(gates)                                        # [3, H]
     y = g[0][None, None, :, None] * o_swa + g[1][None, None, :, None] * o_dswa \
         + g[2][None, None, :, None] * np.asarray(o_gdn, np.float64)[:, rows]
@@ -60,8 +62,8 @@ def hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, rows, frame_offset=0,
 
 
 def hlta(q, k, v, alpha, beta, gates, L, w, dil, frame_offset=0, state_in=None,
-         window_qk="bf16"):
+         window_qk="bf16", centered=False):
     """Layer output for every token ``[B, T, H, d]`` and the final GDN state."""
     T = np.asarray(q).shape[1]
     return hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, np.arange(T), frame_offset,
-                     state_in, window_qk)
+                     state_in, window_qk, centered=centered)

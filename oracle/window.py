@@ -7,9 +7,13 @@ rearranged from (B, F*L, D) to (B*d, F/d*L, D)).
 
 Readings (the paper is ambiguous or silent on these):
 
-* Causal windows.  Eq. 7 prints a centred band; the workloads here are
-  causal, and streaming needs causality.  Query i sees the w keys
+* Causal windows by default.  Eq. 7 prints a centred band; the workloads
+  here are causal, and streaming needs causality.  Query i sees the w keys
   ``i - w < j <= i`` (itself included).
+* Centred windows (``centered=True``): Eq. 7's band ``[i - w/2, i + w/2]``
+  read with the radius rounded down, r = floor(w / 2), both ends included:
+  query i sees ``|j - i| <= r`` (2r + 1 keys away from the sequence ends;
+  w + 1 for even w, w for odd w).  Keys exist only inside the call.
 * Dilation groups frames by residue: frame f belongs to group f mod d (the
   rearrange keeps the frame's tokens contiguous and strides frames by d).
   Frames are counted from an absolute index ``frame_offset`` of the first
@@ -27,7 +31,9 @@ p(t) = (f(t) // dil) * L + t mod L, the key set is
     J(i) = { j : r(j) = r(i) and p(i) - w < p(j) <= p(i) }
 
 and the output is sum_{j in J(i)} softmax_j(q_i . k_j / sqrt(d)) v_j.  With
-dil = 1 this is exactly SWA's set {i - w < j <= i}.
+dil = 1 this is exactly SWA's set {i - w < j <= i}.  Centred windows use
+
+    J(i) = { j : r(j) = r(i) and |p(j) - p(i)| <= floor(w / 2) }.
 """
 from __future__ import annotations
 
@@ -63,7 +69,14 @@ def _candidate_keys(i_lo, i_hi, T, L, w, dil, frame_offset):
     return idx[idx <= i_hi]
 
 
-def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0):
+def _in_window(p_key, p_query, w, centered):
+    """Window test on sub-sequence positions (broadcasting)."""
+    if centered:
+        return np.abs(p_key - p_query) <= w // 2
+    return (p_key > p_query - w) & (p_key <= p_query)
+
+
+def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0, centered=False):
     """Outputs of the windowed branch for the query tokens ``rows`` only.
 
     q, k, v: ``[B, T, H, d]``.  Returns ``[B, len(rows), H, d]`` fp64.
@@ -89,10 +102,14 @@ def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0):
         while end < len(srt) and srt[end] // Lf == fr and end - start < 256:
             end += 1
         qi = srt[start:end]
-        cand = _candidate_keys(qi[0], qi[-1], T, Lf, w, dil, frame_offset)
+        if centered:
+            # every token of the rows' group within reach of the rows' positions
+            rad = w // 2
+            cand = np.nonzero((r == r[qi[0]]) & (p >= p[qi].min() - rad) & (p <= p[qi].max() + rad))[0]
+        else:
+            cand = _candidate_keys(qi[0], qi[-1], T, Lf, w, dil, frame_offset)
         mask = (r[cand][None, :] == r[qi][:, None]) \
-            & (p[cand][None, :] > p[qi][:, None] - w) \
-            & (p[cand][None, :] <= p[qi][:, None])
+            & _in_window(p[cand][None, :], p[qi][:, None], w, centered)
         for b in range(B):
             for h in range(H):
                 s = (q[b, qi, h] @ k[b, cand, h].T) * scale
@@ -105,13 +122,13 @@ def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0):
     return out
 
 
-def windowed_attention(q, k, v, L, w, dil=1, frame_offset=0):
+def windowed_attention(q, k, v, L, w, dil=1, frame_offset=0, centered=False):
     """Windowed branch for every query token: ``[B, T, H, d]`` fp64."""
     T = np.asarray(q).shape[1]
-    return windowed_attention_rows(q, k, v, np.arange(T), L, w, dil, frame_offset)
+    return windowed_attention_rows(q, k, v, np.arange(T), L, w, dil, frame_offset, centered)
 
 
-def window_bruteforce(q, k, v, L, w, dil=1, frame_offset=0):
+def window_bruteforce(q, k, v, L, w, dil=1, frame_offset=0, centered=False):
     """Scalar loops straight from the key-set definition; tiny inputs only."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -128,7 +145,11 @@ def window_bruteforce(q, k, v, L, w, dil=1, frame_offset=0):
                 for j in range(T):
                     fj = j // Lf + frame_offset
                     pj = (fj // dil) * Lf + j % Lf
-                    if fj % dil == fi % dil and pi - w < pj <= pi:
+                    if centered:
+                        inside = abs(pj - pi) <= w // 2
+                    else:
+                        inside = pi - w < pj <= pi
+                    if fj % dil == fi % dil and inside:
                         keys.append(j)
                 sc = [sum(q[b, i, h, c] * k[b, j, h, c] for c in range(d)) / math.sqrt(d)
                       for j in keys]
@@ -140,18 +161,18 @@ def window_bruteforce(q, k, v, L, w, dil=1, frame_offset=0):
     return out
 
 
-def dswa_reshape(q, k, v, L, w, dil, frame_offset=0, swa=None):
+def dswa_reshape(q, k, v, L, w, dil, frame_offset=0, swa=None, centered=False):
     """Eq. 8 taken literally: gather each residue group's frames into one
-    contiguous sub-sequence (the rearrange), run causal SWA with window w on
-    it, and scatter the outputs back to their tokens.  ``swa`` is the SWA
-    routine to use (defaults to ``windowed_attention`` with dil = 1)."""
+    contiguous sub-sequence (the rearrange), run SWA with window w (causal or
+    centred) on it, and scatter the outputs back to their tokens.  ``swa`` is
+    the SWA routine to use (defaults to ``windowed_attention`` with dil = 1)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     B, T, H, d = q.shape
     if swa is None:
         def swa(qq, kk, vv):
-            return windowed_attention(qq, kk, vv, L, w, 1, 0)
+            return windowed_attention(qq, kk, vv, L, w, 1, 0, centered)
     out = np.empty_like(v)
     F = -(-T // L)
     for res in range(dil):
