@@ -40,8 +40,9 @@ def gdn_flops_per_token_head(d=128, C=CHUNK):
     return (2 * (5 * C * C * d + 3 * C * d * d) + C ** 3 / 3) / C
 
 
-def window_pairs(T, L, w, dil, frame_offset=0):
-    """Exact (query, key) pair count of one causal windowed branch (all groups)."""
+def window_pairs(T, L, w, dil, frame_offset=0, centered=False):
+    """Exact (query, key) pair count of one windowed branch (all groups):
+    causal (i - w, i], or centred |j - i| <= floor(w / 2)."""
     F = -(-T // L)
     total = 0
     for r in range(dil):
@@ -49,8 +50,13 @@ def window_pairs(T, L, w, dil, frame_offset=0):
         for f in range(F):
             if (f + frame_offset) % dil == r:
                 n += min(L, T - f * L)
-        m = min(n, w)
-        total += m * (m + 1) // 2 + (n - m) * w
+        if centered:
+            rad = w // 2
+            side = n * (n - 1) // 2 if n <= rad + 1 else rad * (rad + 1) // 2 + (n - rad - 1) * rad
+            total += n + 2 * side
+        else:
+            m = min(n, w)
+            total += m * (m + 1) // 2 + (n - m) * w
     return total
 
 
@@ -214,6 +220,10 @@ def main():
     t_win = st.run("window_hybrid", lambda: K.kairos_hlta_window_fwd(
         codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
         k_scales=sk, out=bufs["out"], workspace=yws), reps)
+    # the same stage with centred windows (Eq. 7 as printed) and the pages' DSWA dilation 6
+    t_win_c = st.run("window_hybrid_centered_dil6", lambda: K.kairos_hlta_window_fwd(
+        codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, 6, q_scales=sq,
+        k_scales=sk, out=bufs["out"], workspace=yws, centered=True), reps)
 
     # input prologue of the gated delta rule on the same shape: raw keys and
     # gate logits -> unit keys and gates ("k": the canonical inputs), and with
@@ -237,6 +247,9 @@ def main():
 
     pairs = window_pairs(w.T, w.L, w.window, 1) + window_pairs(w.T, w.L, w.window, w.dilation)
     win_flops = pairs * 4 * w.d * w.B * w.H          # QK^T 2d + PV 2d per (query, key) pair
+    pairs_c = window_pairs(w.T, w.L, w.window, 1, centered=True) + \
+        window_pairs(w.T, w.L, w.window, 6, centered=True)
+    win_flops_c = pairs_c * 4 * w.d * w.B * w.H
     if fp8:
         # QK^T at the fp8 peak, PV at the bf16 peak: time-weighted (blended) peak
         peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
@@ -276,6 +289,10 @@ def main():
         },
         "window_stage": {"ms": round(t_win, 4), "alg_TFLOP_per_s": round(achieved, 1),
                          "pairs_per_bh": pairs},
+        "window_stage_centered_dil6": {
+            "ms": round(t_win_c, 4), "pairs_per_bh": pairs_c,
+            "alg_TFLOP_per_s": round(win_flops_c / (t_win_c / 1e3) / 1e12, 1),
+            "mfma_frac": round(win_flops_c / (t_win_c / 1e3) / 1e12 / peak, 4)},
         "gdn_prologue": {
             name: {"ms": round(t, 4), "alg_bytes": pro_bytes[name],
                    "alg_GB_per_s": round(pro_bytes[name] / (t / 1e3) / 1e9, 1),

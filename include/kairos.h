@@ -25,9 +25,10 @@
  *   fp8 codes          [B][T][H][d]      uint8 OCP E4M3; scales [B][H][ceil(T/64)] fp32
  * The gated delta rule is the canonical form
  *   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t,
- * keys arrive L2-normalised (nothing renormalises them).  Windows are causal:
- * query i sees keys i-w < j <= i (SWA); DSWA groups frames by absolute frame
- * index mod dilation and applies the same window to positions inside a group.
+ * keys arrive L2-normalised (nothing renormalises them).  Windows are causal
+ * by default: query i sees keys i-w < j <= i (SWA), or centred on request
+ * (|j - i| <= floor(w/2)); DSWA groups frames by absolute frame index mod
+ * dilation and applies the same window to positions inside a group.
  * The softmax scale is 1/sqrt(d).
  *
  * Ownership and streams: the caller owns every buffer (device memory unless
@@ -67,6 +68,12 @@ typedef enum {
 
 typedef enum { KAIROS_F32 = 0, KAIROS_BF16 = 1, KAIROS_FP8_E4M3 = 2 } kairos_dtype;
 
+/* Window form of the SWA / DSWA branches (Sec. 2.2.2, Eq. 7).
+ *   KAIROS_WINDOW_CAUSAL    query i sees keys i - w < j <= i (w keys with itself)
+ *   KAIROS_WINDOW_CENTERED  Eq. 7's centred band as printed: |j - i| <= floor(w / 2)
+ *                           (keys on both sides, itself included; no streaming) */
+typedef enum { KAIROS_WINDOW_CAUSAL = 0, KAIROS_WINDOW_CENTERED = 1 } kairos_window_kind;
+
 /* Gated delta rule problem.  dk == dv == d with d in {32, 64, 128};
  * chunk must be 64 (the chunkwise evaluation's block length; any chunk size
  * gives the same result up to rounding).  io: KAIROS_F32 (q, k, v, out fp32,
@@ -88,7 +95,10 @@ typedef struct {
  * ring_frames R: 0 for a self-contained call (no keys before token 0);
  * otherwise the call continues a rollout: frames frame_offset-R ..
  * frame_offset-1 (those >= 0) are read from the ring, T must be a multiple of
- * L, and R must be >= kairos_hlta_ring_frames_required(). */
+ * L, and R must be >= kairos_hlta_ring_frames_required().  window_kind
+ * (kairos_window_kind) applies to both windowed branches; a centred window
+ * sees later frames, so it needs ring_frames == 0 (else
+ * KAIROS_ERR_UNSUPPORTED); frame_offset still sets the DSWA residue groups. */
 typedef struct {
   kairos_gdn_desc g;
   int32_t L;
@@ -97,7 +107,7 @@ typedef struct {
   int32_t window_qk;           /* kairos_dtype */
   int64_t frame_offset;
   int32_t ring_frames;
-  int32_t reserved;            /* must be 0 */
+  int32_t window_kind;         /* kairos_window_kind */
 } kairos_hlta_desc;
 
 /* Human-readable name of a status code (static storage). */
@@ -111,7 +121,7 @@ int kairos_version(void);
 int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes);
 int kairos_hlta_workspace_size(const kairos_hlta_desc* desc, size_t* bytes);
 
-/* Ring frames a streamed call needs: dilation * ceil((window - 1) / L)
+/* Ring frames a streamed (causal) call needs: dilation * ceil((window - 1) / L)
  * (frames whose keys a query can still see), written to *frames. */
 int kairos_hlta_ring_frames_required(const kairos_hlta_desc* desc, int32_t* frames);
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert K.version() == 100
+    assert K.version() == 101
     assert K.status_string(0) == "ok"
     assert "align" in K.status_string(ALIGN)
     assert K.status_string(12345) == "unknown status"
@@ -128,8 +128,11 @@ def test_hlta_validation():
     assert _hlta_call(K.hlta_desc(**base, ring_frames=4)) == NULL          # ring pointers missing
     assert _hlta_call(K.hlta_desc(**base, ring_frames=4, window_qk=K.FP8_E4M3)) == UNSUP
     d2 = K.hlta_desc(**base)
-    d2.reserved = 1
+    d2.window_kind = 2
     assert _hlta_call(d2) == SHAPE
+    # a centred window sees later frames: no ring
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, centered=True)) == UNSUP
+    assert _hlta_call(K.hlta_desc(**base, centered=True)) == WS       # otherwise valid
     nws = K.kairos_hlta_workspace_size(d)
     assert _hlta_call(d, ws=8 * G, nws=nws - 256) == WS
     # workspace overlapping the output

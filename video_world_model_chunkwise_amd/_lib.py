@@ -6,6 +6,7 @@ import os
 from ctypes import POINTER, byref, c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
+WINDOW_CAUSAL, WINDOW_CENTERED = 0, 1
 PROLOGUE_NORMALIZE_Q, PROLOGUE_LITERAL_EQ6 = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,7 @@ class GdnDesc(ctypes.Structure):
 class HltaDesc(ctypes.Structure):
     _fields_ = [("g", GdnDesc), ("L", c_int32), ("window", c_int32), ("dilation", c_int32),
                 ("window_qk", c_int32), ("frame_offset", c_int64), ("ring_frames", c_int32),
-                ("reserved", c_int32)]
+                ("window_kind", c_int32)]
 
 
 _lib = None
@@ -86,9 +87,9 @@ def gdn_desc(B, T, H, d, io=BF16, chunk=64) -> GdnDesc:
 
 
 def hlta_desc(B, T, H, d, L, window, dilation, frame_offset=0, ring_frames=0,
-              window_qk=BF16, io=BF16) -> HltaDesc:
+              window_qk=BF16, io=BF16, centered=False) -> HltaDesc:
     return HltaDesc(gdn_desc(B, T, H, d, io), L, window, dilation, window_qk, frame_offset,
-                    ring_frames, 0)
+                    ring_frames, WINDOW_CENTERED if centered else WINDOW_CAUSAL)
 
 
 # ------------------------------------------------------------------ torch marshalling
@@ -201,9 +202,10 @@ def kairos_fp8_quantize(x, codes=None, scales=None, stream=None):
 
 def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=0,
                       k_ring=None, v_ring=None, q_scales=None, k_scales=None, out=None,
-                      stream=None):
-    """One windowed branch (SWA if dilation == 1, else DSWA).  q, k bf16, or
-    uint8 E4M3 codes with q_scales/k_scales; v bf16 [B, T, H, 128]."""
+                      stream=None, centered=False):
+    """One windowed branch (SWA if dilation == 1, else DSWA), causal or
+    centred.  q, k bf16, or uint8 E4M3 codes with q_scales/k_scales; v bf16
+    [B, T, H, 128]."""
     torch = _torch()
     B, T, H, d = v.shape
     dev = v.device
@@ -223,7 +225,7 @@ def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=
         out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
     desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames,
-                     FP8_E4M3 if fp8 else BF16)
+                     FP8_E4M3 if fp8 else BF16, centered=centered)
     st = lib().kairos_window_fwd(byref(desc), dilation, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scales),
                                  _ptr(k_scales), _ptr(k_ring), _ptr(v_ring), _ptr(out),
                                  _stream(stream))
@@ -233,7 +235,8 @@ def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=
 
 def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, frame_offset=0,
                     state_in=None, ring_frames=0, k_ring=None, v_ring=None, window_qk=BF16,
-                    out=None, state_out=None, keep_state=True, workspace=None, stream=None):
+                    out=None, state_out=None, keep_state=True, workspace=None, stream=None,
+                    centered=False):
     """Hybrid layer forward.  q, k, v: [B, T, H, 128] bf16; alpha, beta
     [B, T, H] fp32; gate_logits [3, H] fp32.  Returns (out, state_out)."""
     torch = _torch()
@@ -254,7 +257,8 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
     if state_out is None and keep_state:
         state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, window_qk)
+    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, window_qk,
+                     centered=centered)
     nws = kairos_hlta_workspace_size(desc)
     ws = workspace if workspace is not None else _workspace(nws, dev)
     if ws is not None and ws.numel() < nws:
@@ -268,7 +272,7 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
 
 def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, frame_offset=0,
                            ring_frames=0, k_ring=None, v_ring=None, q_scales=None, k_scales=None,
-                           out=None, workspace=None, stream=None):
+                           out=None, workspace=None, stream=None, centered=False):
     """Windowed stage of the hybrid layer: SWA + DSWA + gated combination with
     o_gdn.  q, k bf16 or uint8 E4M3 codes (with scales); v, o_gdn bf16."""
     torch = _torch()
@@ -292,7 +296,7 @@ def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, fra
         out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
     desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames,
-                     FP8_E4M3 if fp8 else BF16)
+                     FP8_E4M3 if fp8 else BF16, centered=centered)
     nws = 4 * B * T * H * d
     ws = workspace if workspace is not None else _workspace(nws, dev)
     if ws.numel() < nws:

@@ -46,9 +46,11 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
   if (st != KAIROS_OK) return st;
   if (d->g.io != KAIROS_BF16) return KAIROS_ERR_DTYPE;
   if (d->g.dk != 128) return KAIROS_ERR_UNSUPPORTED;
-  if (d->L < 1 || d->window < 1 || d->dilation < 1 || d->frame_offset < 0 || d->ring_frames < 0 ||
-      d->reserved != 0)
+  if (d->L < 1 || d->window < 1 || d->dilation < 1 || d->frame_offset < 0 || d->ring_frames < 0)
     return KAIROS_ERR_SHAPE;
+  if (d->window_kind != KAIROS_WINDOW_CAUSAL && d->window_kind != KAIROS_WINDOW_CENTERED)
+    return KAIROS_ERR_SHAPE;
+  if (d->window_kind == KAIROS_WINDOW_CENTERED && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   if (d->window_qk != KAIROS_BF16 && d->window_qk != KAIROS_FP8_E4M3) return KAIROS_ERR_DTYPE;
   if (d->window_qk == KAIROS_FP8_E4M3 && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   // group positions (frame / dil) * L + L and token indices must fit in int32
@@ -134,6 +136,7 @@ void fill_win_args(WinArgs& a, const kairos_hlta_desc* d) {
   a.dil = d->dilation;
   a.R = d->ring_frames;
   a.nblk = (d->g.T + 63) / 64;
+  a.centered = d->window_kind == KAIROS_WINDOW_CENTERED ? 1 : 0;
   a.frame_offset = (long)d->frame_offset;
 }
 
@@ -156,7 +159,7 @@ const char* kairos_status_string(int status) {
   }
 }
 
-int kairos_version(void) { return 100; }
+int kairos_version(void) { return 101; }
 
 int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
   if (!bytes) return KAIROS_ERR_NULL;

@@ -21,6 +21,7 @@ struct WinArgs {
   uint16_t* out;            // bf16 [B][T][H][128]
   int B, T, H, L, F, QT;    // F frames in the call (last may be partial), QT query tiles per frame
   int w, dil, R, nblk;
+  int centered;             // 0: causal window (i - w, i]; 1: centred |j - i| <= w / 2
   long frame_offset;
 };
 

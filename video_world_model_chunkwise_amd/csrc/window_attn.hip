@@ -1,15 +1,19 @@
-// Causal sliding-window (SWA) and dilated sliding-window (DSWA) softmax
-// attention on gfx950, with the fused per-head sigmoid branch-gate epilogue of
-// the hybrid layer.
+// Sliding-window (SWA) and dilated sliding-window (DSWA) softmax attention on
+// gfx950, causal or centred, with the fused per-head sigmoid branch-gate
+// epilogue of the hybrid layer.
 //
 // Operation (Kairos paper, arXiv 2606.16533 HTML v3, Sec. 2.2.2):
 //   SWA (Eq. 7, causal reading):  o_i = sum_{i-w < j <= i} softmax_j(q_i.k_j / sqrt(d)) v_j
+//   SWA (Eq. 7 as printed, centred): keys |j - i| <= r, r = floor(w / 2)
 //   DSWA (Eq. 8): SWA over the sequence rearranged so that frames with equal
 //   (absolute frame index mod dilation) are contiguous.  Nothing is moved in
 //   memory: with f the absolute frame of a token, its group is f mod dil and
 //   its position inside the group's sequence is p = (f / dil) * L + offset;
 //   keys of query i are the tokens of its group with p_i - w < p_j <= p_i.
 //   SWA is the same map with dil = 1, so one code path serves both.
+//   Both window forms are one band [p_i - back, min(p_i + fwd, p_last)] in
+//   group positions (causal: back = w - 1, fwd = 0; centred: back = fwd = r;
+//   p_last is the group's last position that exists in the call).
 //   Hybrid epilogue: y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn.
 //
 // Work decomposition: one workgroup (4 waves) per (batch, head, frame,
@@ -114,6 +118,8 @@ struct BranchRange {
   KeyMap km;
   int pq0;      // group position of query row m = 0 of the frame
   int p_lo, p_hi, nb;
+  int back, fwd;  // reach of a query's window before / after its own position
+  int p_last;     // last group position present in the call
 };
 
 __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, int f, int m_first,
@@ -129,9 +135,16 @@ __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, i
   const int f_avail = (int)a.frame_offset - a.R > 0 ? (int)a.frame_offset - a.R : 0;
   const int f1 = f_avail + (((r.km.res - f_avail % dil) % dil) + dil) % dil;   // first frame of the group
   const int p_avail = (f1 / dil) * a.L;
-  const int lo = r.pq0 + m_first - a.w + 1;
+  // last frame of the group inside the call (only the call's last frame may be partial)
+  const int f_end = (int)a.frame_offset + a.F - 1;
+  const int f_lastg = f_end - (f_end - r.km.res) % dil;
+  const int len_last = min(a.L, a.T - (f_lastg - (int)a.frame_offset) * a.L);
+  r.p_last = (f_lastg / dil) * a.L + len_last - 1;
+  r.back = a.centered ? a.w / 2 : a.w - 1;
+  r.fwd = a.centered ? a.w / 2 : 0;
+  const int lo = r.pq0 + m_first - r.back;
   r.p_lo = lo > p_avail ? lo : p_avail;
-  r.p_hi = r.pq0 + m_last;
+  r.p_hi = min(r.pq0 + m_last + r.fwd, r.p_last);
   r.nb = (r.p_hi - r.p_lo + BK) / BK;
   return r;
 }
@@ -254,10 +267,12 @@ __device__ __forceinline__ void win_issue(const WinLoads<FP8>& ld, const WinBuf&
 }
 
 // One key block of a branch: scores from buffer cb, online softmax, O update.
+// The lane's query sees the keys at group positions [hi - wl + 1, hi].
 template <bool FP8>
-__device__ __forceinline__ void win_block(const WinArgs& a, const WinBuf& cb, const QueryCtx& qc, int pq,
-                                          int pb, bool full, const bf16x8 (&qf)[8], const i32x8 (&q8f)[2],
-                                          f32x16 (&O)[4], float& m_run, float& l_run) {
+__device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
+                                          bool full, const bf16x8 (&qf)[8],
+                                          const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
+                                          float& l_run) {
   // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
   f32x16 S[2];
 #pragma unroll
@@ -294,13 +309,13 @@ __device__ __forceinline__ void win_block(const WinArgs& a, const WinBuf& cb, co
       }
   }
   if (!full) {
-    // valid iff pq - w < pk <= pq, i.e. (unsigned)(pq - pk) < w
-    const int base = pq - pb;
+    // valid iff hi - wl < pk <= hi, i.e. (unsigned)(hi - pk) < wl
+    const int base = hi - pb;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)a.w) S[kt][r] = -INFINITY;
+        if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)wl) S[kt][r] = -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -365,6 +380,10 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   win_wait_vmem();
   lds_barrier();
   const int pq = br.pq0 + qc.mq;                         // this lane's query position
+  const int hi = min(pq + br.fwd, br.p_last);            // its window's last key position
+  const int wl = hi - (pq - br.back) + 1;                // and the window's length
+  const int full_lo = br.pq0 + qc.mw_hi - br.back;       // blocks inside every window of the wave
+  const int full_hi = min(br.pq0 + qc.mw_lo + br.fwd, br.p_last);
   for (int jb = 0; jb < br.nb; jb += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -388,8 +407,8 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
         }
         win_issue<FP8>(ld, nb, qc.wave);
       }
-      const bool full = (pb > br.pq0 + qc.mw_hi - a.w) && (pb + BK - 1 <= br.pq0 + qc.mw_lo);
-      win_block<FP8>(a, cb, qc, pq, pb, full, qf, q8f, O, m_run, l_run);
+      const bool full = pb >= full_lo && pb + BK - 1 <= full_hi;
+      win_block<FP8>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
       win_wait_vmem();
       lds_barrier();
       n0 = n1;
