@@ -20,6 +20,8 @@ Physical AI" (arXiv 2606.16533, HTML v3):
 * ``fp8``    -- an OCP FP8 E4M3 quantiser with per-64-token-block absmax
                scales, written from the format definition;
 * ``hlta``   -- the gated combination of the three branches;
+* ``rope``   -- rotary position embedding of the windowed branches' q and k
+               at each branch's (group) positions;
 * ``prologue`` -- the inputs of the gated delta rule from raw keys and gate
                logits (L2 normalisation, sigmoids of Eq. 1 and Eq. 4, and the
                rescaling that turns the printed Eq. 6 into the canonical form).
@@ -35,6 +37,7 @@ from .window import (windowed_attention, windowed_attention_rows, window_brutefo
 from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, fp8_quantize_blocks, E4M3_MAX
 from .hlta import hlta, hlta_rows, sigmoid
 from .prologue import l2_normalize, gdn_prologue
+from .rope import rope, rope_angles, branch_positions
 
 __all__ = [
     "gdn_recurrent", "gdn_literal_eq6", "gdn_chunked",
@@ -42,4 +45,5 @@ __all__ = [
     "frame_index_maps",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "fp8_quantize_blocks", "E4M3_MAX",
     "hlta", "hlta_rows", "sigmoid", "l2_normalize", "gdn_prologue",
+    "rope", "rope_angles", "branch_positions",
 ]

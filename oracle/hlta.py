@@ -18,6 +18,8 @@ Readings:
   equal one call over the whole sequence; the oracle is that single call.
 * ``centered=True`` gives both windowed branches Eq. 7's centred band (see
   ``window``); such a layer sees future frames and has no streamed form.
+* ``rope_base``: RoPE (``rope``) on each windowed branch's q and k at that
+  branch's positions, before the FP8 quantisation when there is one.
 """
 from __future__ import annotations
 
@@ -26,11 +28,22 @@ import numpy as np
 from .gdn import gdn_recurrent
 from .window import windowed_attention_rows
 from .fp8 import fp8_quantize_blocks
+from .rope import rope, branch_positions
 
 
 def sigmoid(z):
     z = np.asarray(z, dtype=np.float64)
     return 1.0 / (1.0 + np.exp(-z))
+
+
+def _branch_inputs(q, k, L, dil, frame_offset, window_qk, rope_base):
+    """q, k as one windowed branch consumes them: rotated (RoPE at the
+    branch's positions) when rope_base is given, then quantised for FP8."""
+    if rope_base:
+        T = np.asarray(q).shape[1]
+        pos = branch_positions(T, L, dil, frame_offset)
+        q, k = rope(q, pos, rope_base), rope(k, pos, rope_base)
+    return _window_inputs(q, k, window_qk)
 
 
 def _window_inputs(q, k, window_qk):
@@ -42,7 +55,7 @@ def _window_inputs(q, k, window_qk):
 
 
 def hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, rows, frame_offset=0,
-              state_in=None, window_qk="bf16", o_gdn=None, centered=False):
+              state_in=None, window_qk="bf16", o_gdn=None, centered=False, rope_base=None):
     """Layer output for the query tokens ``rows`` (all heads) and final state.
 
     The GDN branch needs every token before the last requested row; it is
@@ -52,8 +65,9 @@ def hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, rows, frame_offset=0,
     S = None
     if o_gdn is None:
         o_gdn, S = gdn_recurrent(q, k, v, alpha, beta, state_in)
-    qw, kw = _window_inputs(q, k, window_qk)
+    qw, kw = _branch_inputs(q, k, L, 1, frame_offset, window_qk, rope_base)
     o_swa = windowed_attention_rows(qw, kw, v, rows, L, w, 1, frame_offset, centered)
+    qw, kw = _branch_inputs(q, k, L, dil, frame_offset, window_qk, rope_base)
     o_dswa = windowed_attention_rows(qw, kw, v, rows, L, w, dil, frame_offset, centered)
     g = sigmoid(gates)                                        # [3, H]
     y = g[0][None, None, :, None] * o_swa + g[1][None, None, :, None] * o_dswa \
@@ -62,8 +76,8 @@ def hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, rows, frame_offset=0,
 
 
 def hlta(q, k, v, alpha, beta, gates, L, w, dil, frame_offset=0, state_in=None,
-         window_qk="bf16", centered=False):
+         window_qk="bf16", centered=False, rope_base=None):
     """Layer output for every token ``[B, T, H, d]`` and the final GDN state."""
     T = np.asarray(q).shape[1]
     return hlta_rows(q, k, v, alpha, beta, gates, L, w, dil, np.arange(T), frame_offset,
-                     state_in, window_qk, centered=centered)
+                     state_in, window_qk, centered=centered, rope_base=rope_base)

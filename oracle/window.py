@@ -76,8 +76,12 @@ def _in_window(p_key, p_query, w, centered):
     return (p_key > p_query - w) & (p_key <= p_query)
 
 
-def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0, centered=False):
+def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0, centered=False,
+                            rope_base=None):
     """Outputs of the windowed branch for the query tokens ``rows`` only.
+
+    ``rope_base``: when given, q and k are first rotated by RoPE at the
+    branch's positions (``oracle.rope``: group positions of this dilation).
 
     q, k, v: ``[B, T, H, d]``.  Returns ``[B, len(rows), H, d]`` fp64.
     Naive masked softmax: scores materialised, max subtracted, exponentiated,
@@ -87,6 +91,10 @@ def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0, centered
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     B, T, H, d = q.shape
+    if rope_base:
+        from .rope import rope, branch_positions
+        pos = branch_positions(T, L if L else T, dil, frame_offset)
+        q, k = rope(q, pos, rope_base), rope(k, pos, rope_base)
     rows = np.asarray(rows, dtype=np.int64)
     out = np.empty((B, len(rows), H, v.shape[-1]))
     f, r, p = frame_index_maps(T, L if L else T, dil, frame_offset)
@@ -122,10 +130,11 @@ def windowed_attention_rows(q, k, v, rows, L, w, dil=1, frame_offset=0, centered
     return out
 
 
-def windowed_attention(q, k, v, L, w, dil=1, frame_offset=0, centered=False):
+def windowed_attention(q, k, v, L, w, dil=1, frame_offset=0, centered=False, rope_base=None):
     """Windowed branch for every query token: ``[B, T, H, d]`` fp64."""
     T = np.asarray(q).shape[1]
-    return windowed_attention_rows(q, k, v, np.arange(T), L, w, dil, frame_offset, centered)
+    return windowed_attention_rows(q, k, v, np.arange(T), L, w, dil, frame_offset, centered,
+                                   rope_base)
 
 
 def window_bruteforce(q, k, v, L, w, dil=1, frame_offset=0, centered=False):
