@@ -240,6 +240,19 @@ def main():
     t_pro_all = st.run("gdn_prologue_qk_literal", lambda: K.kairos_gdn_prologue(
         d["q"], za, zb, q=d["k"], v=d["v"], literal=True, k_out=p_k, alpha_out=p_a, beta_out=p_b,
         q_out=p_q, v_out=p_v), reps)
+    # RoPE fused with the E4M3 quantiser (one tensor, DSWA positions), and the
+    # whole layer with RoPE on both windowed branches
+    t_rope = st.run("rope_fp8_q", lambda: K.kairos_rope(d["q"], w.L, w.dilation, 1e4, fp8=True,
+                                                        out=codes_q, scales=sq), reps)
+    rope_bytes = d["q"].numel() * 3 + sq.numel() * 4          # bf16 in, codes + scales out
+    desc_r = K.hlta_desc(w.B, w.T, w.H, w.d, w.L, w.window, w.dilation,
+                         window_qk=K.FP8_E4M3 if fp8 else K.BF16, rope_base=1e4)
+    ws_r = torch.empty(K.kairos_hlta_workspace_size(desc_r), dtype=torch.uint8, device=dev)
+    t_layer_rope = st.run("layer_rope", lambda: K.kairos_hlta_fwd(
+        d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["gates"], w.L, w.window, w.dilation,
+        window_qk=K.FP8_E4M3 if fp8 else K.BF16, out=bufs["out"], state_out=bufs["state"],
+        workspace=ws_r, rope_base=1e4), reps)
+    del ws_r
     rows = w.B * w.T * w.H
     pro_bytes = {"gdn_prologue_k": rows * (2 * w.d * 2 + 16),
                  "gdn_prologue_qk_literal": rows * (6 * w.d * 2 + 16)}
@@ -293,6 +306,13 @@ def main():
             "ms": round(t_win_c, 4), "pairs_per_bh": pairs_c,
             "alg_TFLOP_per_s": round(win_flops_c / (t_win_c / 1e3) / 1e12, 1),
             "mfma_frac": round(win_flops_c / (t_win_c / 1e3) / 1e12 / peak, 4)},
+        "rope": {
+            "rope_fp8_q": {"ms": round(t_rope, 4), "alg_bytes": rope_bytes,
+                           "alg_GB_per_s": round(rope_bytes / (t_rope / 1e3) / 1e9, 1),
+                           "hbm_frac": round(rope_bytes / (t_rope / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "layer_rope": {"ms": round(t_layer_rope, 4),
+                           "tokens_per_s": round(tokens / (t_layer_rope / 1e3))},
+        },
         "gdn_prologue": {
             name: {"ms": round(t, 4), "alg_bytes": pro_bytes[name],
                    "alg_GB_per_s": round(pro_bytes[name] / (t / 1e3) / 1e9, 1),

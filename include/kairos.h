@@ -98,7 +98,15 @@ typedef struct {
  * L, and R must be >= kairos_hlta_ring_frames_required().  window_kind
  * (kairos_window_kind) applies to both windowed branches; a centred window
  * sees later frames, so it needs ring_frames == 0 (else
- * KAIROS_ERR_UNSUPPORTED); frame_offset still sets the DSWA residue groups. */
+ * KAIROS_ERR_UNSUPPORTED); frame_offset still sets the DSWA residue groups.
+ * rope_base: 0 for none, else RoPE (Sec. 2.2.2: every sliding-window block
+ * uses rotary relative position encoding; RoFormer's definition: feature
+ * pairs (2i, 2i+1) rotated by p * base^(-2i/d)) on the windowed branches' q
+ * and k at each branch's positions p = (f div dil) * L + (t mod L), f the
+ * absolute frame (SWA: the absolute token index; DSWA: the position in the
+ * residue group's sub-sequence); applied before the FP8 quantisation; not on
+ * the gated delta rule.  Not with a ring (KAIROS_ERR_UNSUPPORTED).
+ * reserved must be 0. */
 typedef struct {
   kairos_gdn_desc g;
   int32_t L;
@@ -108,6 +116,8 @@ typedef struct {
   int64_t frame_offset;
   int32_t ring_frames;
   int32_t window_kind;         /* kairos_window_kind */
+  float rope_base;             /* 0: no RoPE; else > 0, finite (10000 is RoFormer's) */
+  int32_t reserved;            /* must be 0 */
 } kairos_hlta_desc;
 
 /* Human-readable name of a status code (static storage). */
@@ -149,7 +159,8 @@ int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, co
  * KAIROS_FP8_E4M3, q and k are the E4M3 codes and q_scales / k_scales the
  * per-64-token-block scales written by kairos_fp8_quantize; otherwise q, k are
  * bf16 and the scale pointers must be NULL.  out [B][T][H][d] bf16.  The ring
- * is read, never written. */
+ * is read, never written.  q and k are used as given: desc->rope_base must be
+ * 0 (apply kairos_rope with the branch's dilation first). */
 int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void* q, const void* k,
                       const void* v, const float* q_scales, const float* k_scales,
                       const void* k_ring, const void* v_ring, void* out, void* stream);
@@ -177,7 +188,9 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
  *   workspace  >= 4*B*T*H*128 bytes, 256-byte aligned (fp32 partial result of
  *              the first branch, one row per query)
  * kairos_hlta_fwd = [kairos_fp8_quantize x2] + kairos_gdn_fwd + this call
- * [+ the ring update]; the stages are exposed for timing and composition. */
+ * [+ the ring update]; the stages are exposed for timing and composition.
+ * Both branches share q and k, so desc->rope_base must be 0 here (with RoPE
+ * the branches need differently rotated q, k: use kairos_hlta_fwd). */
 int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const void* k,
                            const void* v, const float* q_scales, const float* k_scales,
                            const void* o_gdn, const float* gate_logits, const void* k_ring,
@@ -221,6 +234,22 @@ int kairos_gdn_prologue(const kairos_gdn_desc* desc, int32_t flags, const void* 
                         const float* alpha_logits, const float* beta_logits, const void* q_in,
                         const void* v_in, void* k_out, float* alpha_out, float* beta_out,
                         void* q_out, void* v_out, void* stream);
+
+/* RoPE of one windowed branch's q or k (Sec. 2.2.2; definition as for
+ * kairos_hlta_desc.rope_base) at the positions of the branch with the given
+ * dilation (1: SWA, the absolute token index; > 1: DSWA, the position in the
+ * residue group's sub-sequence), using desc->{g.B, g.T, g.H, g.dk, L,
+ * frame_offset, rope_base (> 0), window_qk}.
+ *   x       [B][T][H][d] bf16
+ *   out     window_qk == KAIROS_BF16: [B][T][H][d] bf16, may be x itself (in
+ *           place); KAIROS_FP8_E4M3: E4M3 codes [B][T][H][d] uint8 of the
+ *           rotated values, quantised as kairos_fp8_quantize does
+ *   scales  FP8: [B][H][ceil(T/64)] fp32; bf16: must be NULL
+ * Angles are reduced in fp64, cos/sin in fp32, the rotation in fp32; bf16
+ * output rounds to nearest even.  kairos_rope + kairos_window_fwd per branch
+ * equals the windowed branches of kairos_hlta_fwd with RoPE. */
+int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, void* out,
+                float* scales, void* stream);
 
 /* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block):
  * s = amax / 448 (fp32; 1 when amax == 0), code = E4M3(x / s) with an IEEE

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert K.version() == 101
+    assert K.version() == 102
     assert K.status_string(0) == "ok"
     assert "align" in K.status_string(ALIGN)
     assert K.status_string(12345) == "unknown status"
@@ -130,6 +130,15 @@ def test_hlta_validation():
     d2 = K.hlta_desc(**base)
     d2.window_kind = 2
     assert _hlta_call(d2) == SHAPE
+    # RoPE: base must be finite and >= 0; not with a ring; reserved must be 0
+    assert _hlta_call(K.hlta_desc(**base, rope_base=-1.0)) == SHAPE
+    assert _hlta_call(K.hlta_desc(**base, rope_base=float("nan"))) == SHAPE
+    assert _hlta_call(K.hlta_desc(**base, rope_base=float("inf"))) == SHAPE
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, rope_base=1e4)) == UNSUP
+    assert _hlta_call(K.hlta_desc(**base, rope_base=1e4)) == WS
+    d3 = K.hlta_desc(**base)
+    d3.reserved = 1
+    assert _hlta_call(d3) == SHAPE
     # a centred window sees later frames: no ring
     assert _hlta_call(K.hlta_desc(**base, ring_frames=4, centered=True)) == UNSUP
     assert _hlta_call(K.hlta_desc(**base, centered=True)) == WS       # otherwise valid
@@ -191,6 +200,41 @@ def test_prologue_validation():
     assert call(desc=K.gdn_desc(1, 64, 2, 128, io=K.FP8_E4M3)) == DTYPE
     assert call(desc=K.gdn_desc(1, 0, 2, 128), k=None, za=None, zb=None, ko=None, ao=None,
                 bo=None) == OK                             # empty: nothing to do
+
+
+@host_only
+def test_rope_validation():
+    L = K.lib()
+    cv = lambda x: None if x is None else ctypes.c_void_p(x)
+    d = K.hlta_desc(1, 1000, 2, 128, 100, 1, 1, rope_base=1e4)
+    d8 = K.hlta_desc(1, 1000, 2, 128, 100, 1, 1, window_qk=K.FP8_E4M3, rope_base=1e4)
+    n = 1000 * 2 * 128
+    call = lambda desc, dil=1, x=1 * G, out=2 * G, sc=None: L.kairos_rope(
+        ctypes.byref(desc), dil, cv(x), cv(out), cv(sc), None)
+    assert call(K.hlta_desc(1, 1000, 2, 128, 100, 1, 1)) == SHAPE          # base 0
+    assert call(d, dil=0) == SHAPE
+    assert call(d, sc=3 * G) == UNSUP                                      # bf16 takes no scales
+    assert call(d8) == NULL                                                # fp8 needs scales
+    assert call(d, x=None) == NULL
+    assert call(d, x=1 * G + 8) == ALIGN
+    assert call(d, out=1 * G + n) == ALIAS                                 # partial overlap
+    assert call(d8, out=1 * G, sc=3 * G) == ALIAS                          # codes over the input
+    # windowed stages take q, k as given: no RoPE there
+    assert L.kairos_window_fwd(ctypes.byref(d), 1, cv(G), cv(2 * G), cv(3 * G), None, None, None,
+                               None, cv(4 * G), None) == UNSUP
+
+
+def test_workspace_grows_with_rope():
+    base = dict(B=1, T=4096, H=2, d=128, L=1024, window=1024, dilation=4)
+    n = 4096 * 2 * 128
+    plain = K.kairos_hlta_workspace_size(K.hlta_desc(**base))
+    rope = K.kairos_hlta_workspace_size(K.hlta_desc(**base, rope_base=1e4))
+    assert rope - plain == 4 * n * 2                                       # two bf16 q, k pairs
+    rope1 = K.kairos_hlta_workspace_size(K.hlta_desc(**{**base, "dilation": 1}, rope_base=1e4))
+    assert rope1 - plain == 2 * n * 2                                      # dilation 1: one pair
+    f8 = K.kairos_hlta_workspace_size(K.hlta_desc(**base, window_qk=K.FP8_E4M3))
+    f8r = K.kairos_hlta_workspace_size(K.hlta_desc(**base, window_qk=K.FP8_E4M3, rope_base=1e4))
+    assert f8r - f8 == 2 * n + 2 * 256 * ((2 * 64 * 4 + 255) // 256)      # codes + scales, 2nd branch
 
 
 def test_binding_rejects_bad_tensors_on_cpu():

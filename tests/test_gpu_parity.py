@@ -109,6 +109,49 @@ def test_fp8_quantize_bit_exact(T):
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_fp8_quantize_wide_range(d):
+    """Values spread over 2^-20 .. 2^10 (non-power-of-two scales, many
+    quotients in the E4M3 subnormal range and below), every head size, a
+    ragged last block: bit-exact against the oracle."""
+    from workloads import to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(d)
+    T = 64 * 5 + 23
+    x = rng.standard_normal((2, T, 5, d)) * np.exp2(rng.uniform(-20, 10, size=(2, T, 5, d)))
+    xb = to_bf16_bits(x.astype(np.float32))
+    codes, scales = K.kairos_fp8_quantize(dev_bf16(xb))
+    torch.cuda.synchronize()
+    c_ref, s_ref, _ = oracle.fp8_quantize_blocks(bf16_bits_to_f32(xb))
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
+def test_fp8_quantize_every_bf16_value():
+    """Every finite bf16 value of magnitude <= 448 (both signs, both zeros,
+    subnormals), placed in blocks whose maximum is 448 so that s = 1 and the
+    quotient is the value itself: the codes match the oracle bit for bit.
+    This covers every E4M3 rounding tie, the subnormal range and the
+    saturation edge of the encoding."""
+    from workloads import bf16_bits_to_f32
+    top = 0x43E0                                   # bf16 pattern of 448
+    mags = np.arange(0, top + 1, dtype=np.uint16)
+    vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+    per_block = 64 * 128 - 1
+    nblk = -(-len(vals) // per_block)
+    blocks = np.zeros((nblk, 64 * 128), dtype=np.uint16)
+    blocks[:, 0] = top
+    flat = blocks[:, 1:].reshape(-1)
+    flat[:len(vals)] = vals
+    blocks[:, 1:] = flat.reshape(nblk, per_block)
+    xb = blocks.reshape(1, nblk * 64, 1, 128)     # [B, T, H, d]: block = 64 tokens x 128
+    codes, scales = K.kairos_fp8_quantize(dev_bf16(xb))
+    torch.cuda.synchronize()
+    c_ref, s_ref, _ = oracle.fp8_quantize_blocks(bf16_bits_to_f32(xb))
+    assert np.all(s_ref == 1.0)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
 # ------------------------------------------------------------------ windowed branches
 
 WIN_CASES = [

@@ -3,7 +3,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, byref, c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import POINTER, byref, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 WINDOW_CAUSAL, WINDOW_CENTERED = 0, 1
@@ -17,7 +17,7 @@ symbols = (
     "kairos_status_string", "kairos_version", "kairos_gdn_workspace_size",
     "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
     "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
-    "kairos_gdn_prologue",
+    "kairos_gdn_prologue", "kairos_rope",
 )
 
 
@@ -35,7 +35,7 @@ class GdnDesc(ctypes.Structure):
 class HltaDesc(ctypes.Structure):
     _fields_ = [("g", GdnDesc), ("L", c_int32), ("window", c_int32), ("dilation", c_int32),
                 ("window_qk", c_int32), ("frame_offset", c_int64), ("ring_frames", c_int32),
-                ("window_kind", c_int32)]
+                ("window_kind", c_int32), ("rope_base", c_float), ("reserved", c_int32)]
 
 
 _lib = None
@@ -61,6 +61,7 @@ def lib():
         L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p]
         L.kairos_hlta_window_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_size_t, c_void_p]
         L.kairos_gdn_prologue.argtypes = [POINTER(GdnDesc), c_int32] + [c_void_p] * 11
+        L.kairos_rope.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 4
         L.kairos_fp8_quantize.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                           c_int32, c_void_p]
         for name in symbols:
@@ -87,9 +88,9 @@ def gdn_desc(B, T, H, d, io=BF16, chunk=64) -> GdnDesc:
 
 
 def hlta_desc(B, T, H, d, L, window, dilation, frame_offset=0, ring_frames=0,
-              window_qk=BF16, io=BF16, centered=False) -> HltaDesc:
+              window_qk=BF16, io=BF16, centered=False, rope_base=0.0) -> HltaDesc:
     return HltaDesc(gdn_desc(B, T, H, d, io), L, window, dilation, window_qk, frame_offset,
-                    ring_frames, WINDOW_CENTERED if centered else WINDOW_CAUSAL)
+                    ring_frames, WINDOW_CENTERED if centered else WINDOW_CAUSAL, rope_base, 0)
 
 
 # ------------------------------------------------------------------ torch marshalling
@@ -236,7 +237,7 @@ def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=
 def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, frame_offset=0,
                     state_in=None, ring_frames=0, k_ring=None, v_ring=None, window_qk=BF16,
                     out=None, state_out=None, keep_state=True, workspace=None, stream=None,
-                    centered=False):
+                    centered=False, rope_base=0.0):
     """Hybrid layer forward.  q, k, v: [B, T, H, 128] bf16; alpha, beta
     [B, T, H] fp32; gate_logits [3, H] fp32.  Returns (out, state_out)."""
     torch = _torch()
@@ -258,7 +259,7 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
     if state_out is None and keep_state:
         state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, window_qk,
-                     centered=centered)
+                     centered=centered, rope_base=rope_base)
     nws = kairos_hlta_workspace_size(desc)
     ws = workspace if workspace is not None else _workspace(nws, dev)
     if ws is not None and ws.numel() < nws:
@@ -353,3 +354,30 @@ def kairos_gdn_prologue(k, alpha_logits, beta_logits, q=None, v=None, literal=Fa
                                    _ptr(v_out), _stream(stream))
     _check(st, "kairos_gdn_prologue")
     return k_out, alpha_out, beta_out, q_out, v_out
+
+
+def kairos_rope(x, L, dilation, rope_base, frame_offset=0, fp8=False, out=None, scales=None,
+                stream=None):
+    """RoPE of one windowed branch's q or k (bf16 [B, T, H, 128]) at the
+    positions of the branch with this dilation (1: SWA).  Returns the rotated
+    bf16 tensor, or with fp8=True (E4M3 codes, scales) of the rotated values.
+    out may be x itself for bf16 (in place)."""
+    torch = _torch()
+    B, T, H, d = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (B, T, H, d), dev)
+    if fp8:
+        out = torch.empty((B, T, H, d), dtype=torch.uint8, device=dev) if out is None else out
+        nb = (T + 63) // 64
+        scales = torch.empty((B, H, nb), dtype=torch.float32, device=dev) if scales is None else scales
+        _need(out, "out", torch.uint8, (B, T, H, d), dev)
+        _need(scales, "scales", torch.float32, (B, H, nb), dev)
+    else:
+        out = torch.empty_like(x) if out is None else out
+        _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
+    desc = hlta_desc(B, T, H, d, L, 1, 1, frame_offset, 0, FP8_E4M3 if fp8 else BF16,
+                     rope_base=rope_base)
+    st = lib().kairos_rope(byref(desc), dilation, _ptr(x), _ptr(out), _ptr(scales if fp8 else None),
+                           _stream(stream))
+    _check(st, "kairos_rope")
+    return (out, scales) if fp8 else out

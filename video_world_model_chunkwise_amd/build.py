@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkairos.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn.hip", "window_attn.hip", "fp8_ring.hip", "prologue.hip", "kairos_abi.hip"]
+SOURCES = ["gdn.hip", "window_attn.hip", "operands.hip", "ring.hip", "prologue.hip", "kairos_abi.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -51,6 +51,8 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
   if (d->window_kind != KAIROS_WINDOW_CAUSAL && d->window_kind != KAIROS_WINDOW_CENTERED)
     return KAIROS_ERR_SHAPE;
   if (d->window_kind == KAIROS_WINDOW_CENTERED && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
+  if (!(d->rope_base >= 0.f) || !(d->rope_base < 3.0e38f) || d->reserved != 0) return KAIROS_ERR_SHAPE;
+  if (d->rope_base > 0.f && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   if (d->window_qk != KAIROS_BF16 && d->window_qk != KAIROS_FP8_E4M3) return KAIROS_ERR_DTYPE;
   if (d->window_qk == KAIROS_FP8_E4M3 && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   // group positions (frame / dil) * L + L and token indices must fit in int32
@@ -66,8 +68,15 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
   return KAIROS_OK;
 }
 
+// Layer workspace: GDN chunk data, o_gdn, the parked first branch, and the
+// windowed operands of each branch (E4M3 codes + scales, or with RoPE the
+// rotated q, k; the second set only when RoPE gives DSWA its own operands).
 struct HltaWs {
-  size_t gdn, o_gdn, ypart, q8, k8, qs, ks, total;
+  size_t gdn, o_gdn, ypart;
+  size_t q1, k1, qs1, ks1;   // first-branch operands (fp8 codes / rotated bf16), scales (fp8)
+  size_t q2, k2, qs2, ks2;   // second-branch operands (RoPE with dilation > 1)
+  bool has1, has2;
+  size_t total;
 };
 
 size_t gdn_ws_bytes(const kairos_gdn_desc* d) {
@@ -78,6 +87,10 @@ HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
   HltaWs w{};
   const size_t n = (size_t)d->g.B * d->g.T * d->g.H * d->g.dk;
   const size_t nblk = (size_t)(d->g.T + 63) / 64;
+  const bool fp8 = d->window_qk == KAIROS_FP8_E4M3;
+  const bool rope = d->rope_base > 0.f;
+  const size_t esz = fp8 ? 1 : 2;
+  const size_t nsc = fp8 ? (size_t)d->g.B * d->g.H * nblk * 4 : 0;
   size_t off = 0;
   w.gdn = off;
   off += align_up(gdn_ws_bytes(&d->g));
@@ -85,18 +98,47 @@ HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
   off += align_up(n * 2);
   w.ypart = off;
   off += align_up(n * 4);
-  if (d->window_qk == KAIROS_FP8_E4M3) {
-    w.q8 = off;
-    off += align_up(n);
-    w.k8 = off;
-    off += align_up(n);
-    w.qs = off;
-    off += align_up((size_t)d->g.B * d->g.H * nblk * 4);
-    w.ks = off;
-    off += align_up((size_t)d->g.B * d->g.H * nblk * 4);
+  w.has1 = fp8 || rope;
+  w.has2 = rope && d->dilation > 1;
+  for (int set = 0; set < 2; ++set) {
+    if (!(set == 0 ? w.has1 : w.has2)) continue;
+    size_t* q = set == 0 ? &w.q1 : &w.q2;
+    size_t* k = set == 0 ? &w.k1 : &w.k2;
+    size_t* qs = set == 0 ? &w.qs1 : &w.qs2;
+    size_t* ks = set == 0 ? &w.ks1 : &w.ks2;
+    *q = off;
+    off += align_up(n * esz);
+    *k = off;
+    off += align_up(n * esz);
+    *qs = off;
+    off += align_up(nsc);
+    *ks = off;
+    off += align_up(nsc);
   }
   w.total = off;
   return w;
+}
+
+// RoPE of q and k of one branch into the workspace (bf16 or E4M3 + scales).
+hipError_t rope_branch(const kairos_hlta_desc* d, int dil, const void* q, const void* k, void* qo,
+                       void* ko, float* qs, float* ks, hipStream_t s) {
+  OperandArgs r;
+  memset(&r, 0, sizeof(r));
+  r.x[0] = (const uint16_t*)q;
+  r.x[1] = (const uint16_t*)k;
+  r.out[0] = qo;
+  r.out[1] = ko;
+  r.scales[0] = qs;
+  r.scales[1] = ks;
+  r.nt = 2;
+  r.B = d->g.B;
+  r.T = d->g.T;
+  r.H = d->g.H;
+  r.L = d->L;
+  r.dil = dil;
+  r.nblk = (d->g.T + 63) / 64;
+  r.frame_offset = (long)d->frame_offset;
+  return launch_rope(r, d->g.dk, (double)d->rope_base, d->window_qk == KAIROS_FP8_E4M3, s);
 }
 
 int check_gdn_ptrs(const kairos_gdn_desc* d, const void* q, const void* k, const void* v,
@@ -159,7 +201,7 @@ const char* kairos_status_string(int status) {
   }
 }
 
-int kairos_version(void) { return 101; }
+int kairos_version(void) { return 102; }
 
 int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
   if (!bytes) return KAIROS_ERR_NULL;
@@ -220,6 +262,7 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
     if (desc->ring_frames < need) return KAIROS_ERR_SHAPE;
   }
   const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  if (desc->rope_base != 0.f) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!q || !k || !v || !out) return KAIROS_ERR_NULL;
   if (fp8 && (!q_scales || !k_scales)) return KAIROS_ERR_NULL;
@@ -257,6 +300,7 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
   if (st != KAIROS_OK) return st;
   const size_t nws = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk * 4;
   const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  if (desc->rope_base != 0.f) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!q || !k || !v || !o_gdn || !gate_logits || !out) return KAIROS_ERR_NULL;
   if (fp8 && (!q_scales || !k_scales)) return KAIROS_ERR_NULL;
@@ -334,22 +378,37 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   a.ypart = (float*)(wsb + ws.ypart);
   a.out = (uint16_t*)out;
   const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
-  if (fp8) {
-    uint8_t* q8 = wsb + ws.q8;
-    uint8_t* k8 = wsb + ws.k8;
-    float* qs = (float*)(wsb + ws.qs);
-    float* ks = (float*)(wsb + ws.ks);
-    e = launch_fp8_quant((const uint16_t*)q, q8, qs, B, T, H, D, s);
+  const bool rope = desc->rope_base > 0.f;
+  a.q = q;
+  a.k = k;
+  if (ws.has1) {
+    void* q1 = wsb + ws.q1;
+    void* k1 = wsb + ws.k1;
+    float* qs1 = fp8 ? (float*)(wsb + ws.qs1) : nullptr;
+    float* ks1 = fp8 ? (float*)(wsb + ws.ks1) : nullptr;
+    if (rope) {
+      e = rope_branch(desc, 1, q, k, q1, k1, qs1, ks1, s);
+    } else {
+      e = launch_fp8_quant((const uint16_t*)q, (uint8_t*)q1, qs1, B, T, H, D, s);
+      if (e == hipSuccess) e = launch_fp8_quant((const uint16_t*)k, (uint8_t*)k1, ks1, B, T, H, D, s);
+    }
     if (e != hipSuccess) return KAIROS_ERR_HIP;
-    e = launch_fp8_quant((const uint16_t*)k, k8, ks, B, T, H, D, s);
+    a.q = q1;
+    a.k = k1;
+    a.q_scales = qs1;
+    a.k_scales = ks1;
+  }
+  if (ws.has2) {
+    void* q2 = wsb + ws.q2;
+    void* k2 = wsb + ws.k2;
+    float* qs2 = fp8 ? (float*)(wsb + ws.qs2) : nullptr;
+    float* ks2 = fp8 ? (float*)(wsb + ws.ks2) : nullptr;
+    e = rope_branch(desc, desc->dilation, q, k, q2, k2, qs2, ks2, s);
     if (e != hipSuccess) return KAIROS_ERR_HIP;
-    a.q = q8;
-    a.k = k8;
-    a.q_scales = qs;
-    a.k_scales = ks;
-  } else {
-    a.q = q;
-    a.k = k;
+    a.q2 = q2;
+    a.k2 = k2;
+    a.q_scales2 = qs2;
+    a.k_scales2 = ks2;
   }
   e = launch_window(a, fp8, true, s);
   if (e != hipSuccess) return KAIROS_ERR_HIP;
@@ -414,6 +473,38 @@ int kairos_gdn_prologue(const kairos_gdn_desc* desc, int32_t flags, const void* 
   a.rows = rows;
   return hip_status(launch_gdn_prologue(a, desc->dk, desc->io == KAIROS_F32, nq, lit,
                                         (hipStream_t)stream));
+}
+
+int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, void* out,
+                float* scales, void* stream) {
+  int st = check_hlta_desc(desc, false);
+  if (st != KAIROS_OK) return st;
+  if (!(desc->rope_base > 0.f) || dilation < 1) return KAIROS_ERR_SHAPE;
+  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  if (!fp8 && scales) return KAIROS_ERR_UNSUPPORTED;
+  if (desc->g.T == 0) return KAIROS_OK;
+  if (!x || !out || (fp8 && !scales)) return KAIROS_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out) || ((uintptr_t)scales & 3u)) return KAIROS_ERR_ALIGN;
+  const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
+  const size_t ns = (size_t)desc->g.B * desc->g.H * ((desc->g.T + 63) / 64) * 4;
+  if (fp8 ? overlaps(out, n, x, 2 * n) : (out != x && overlaps(out, 2 * n, x, 2 * n)))
+    return KAIROS_ERR_ALIAS;
+  if (overlaps(scales, ns, x, 2 * n) || overlaps(scales, ns, out, fp8 ? n : 2 * n))
+    return KAIROS_ERR_ALIAS;
+  OperandArgs r;
+  memset(&r, 0, sizeof(r));
+  r.x[0] = (const uint16_t*)x;
+  r.out[0] = out;
+  r.scales[0] = scales;
+  r.nt = 1;
+  r.B = desc->g.B;
+  r.T = desc->g.T;
+  r.H = desc->g.H;
+  r.L = desc->L;
+  r.dil = dilation;
+  r.nblk = (desc->g.T + 63) / 64;
+  r.frame_offset = (long)desc->frame_offset;
+  return hip_status(launch_rope(r, desc->g.dk, (double)desc->rope_base, fp8, (hipStream_t)stream));
 }
 
 int kairos_fp8_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,

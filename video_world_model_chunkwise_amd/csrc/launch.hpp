@@ -13,6 +13,13 @@ struct WinArgs {
   const uint16_t* v;        // bf16 [B][T][H][128]
   const float* q_scales;    // [B][H][nblk] (FP8 only)
   const float* k_scales;
+  // second (DSWA) branch of the hybrid kernel: its own q, k (and scales) when
+  // they differ from the first branch's (RoPE at the group positions); null
+  // means the first branch's
+  const void* q2;
+  const void* k2;
+  const float* q_scales2;
+  const float* k_scales2;
   const uint16_t* k_ring;   // [B][R][L][H][128] bf16 or null
   const uint16_t* v_ring;
   const uint16_t* o_gdn;    // bf16 [B][T][H][128] (hybrid only)
@@ -39,6 +46,21 @@ struct PrologueArgs {
   float* beta;              // [rows]
   long rows;
 };
+
+// Windowed-branch operands: E4M3 quantisation and/or RoPE of q and/or k
+// ([B][T][H][D] bf16) at a branch's positions (frame_offset, L, dil), written
+// as bf16 or as E4M3 codes with per-(b, h, 64-token block) scales.
+struct OperandArgs {
+  const uint16_t* x[2];     // nt tensors sharing positions (q and k of one branch)
+  void* out[2];
+  float* scales[2];         // FP8 only: [B][H][nblk]
+  int nt, B, T, H, L, dil, nblk;
+  long frame_offset;
+};
+struct RopeFreqs {
+  double theta[64];         // base^(-2i/D), i < D/2
+};
+hipError_t launch_rope(const OperandArgs& args, int D, double base, bool fp8, hipStream_t stream);
 
 // fp32 io when f32, else bf16; D in {32, 64, 128}
 hipError_t launch_gdn_prologue(const PrologueArgs& args, int D, bool f32, bool normalize_q,

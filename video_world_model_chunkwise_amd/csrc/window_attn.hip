@@ -120,6 +120,7 @@ struct BranchRange {
   int p_lo, p_hi, nb;
   int back, fwd;  // reach of a query's window before / after its own position
   int p_last;     // last group position present in the call
+  bool own_k;     // keys from the second-branch operands (a.k2, a.k_scales2)
 };
 
 __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, int f, int m_first,
@@ -146,6 +147,7 @@ __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, i
   r.p_lo = lo > p_avail ? lo : p_avail;
   r.p_hi = min(r.pq0 + m_last + r.fwd, r.p_last);
   r.nb = (r.p_hi - r.p_lo + BK) / BK;
+  r.own_k = false;
   return r;
 }
 
@@ -209,12 +211,13 @@ __device__ __forceinline__ void win_load_setup(WinLoads<FP8>& ld, int wave, int 
 // m0): positions past p_hi clamp to p_hi (masked out; clamping keeps loads in
 // bounds and values finite).
 template <bool FP8, bool SHORTL>
-__device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs& a, const KeyMap& km,
-                                                int b, int h, int wave, int pb, int n0, int m0,
-                                                int p_hi) {
+__device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs& a, const BranchRange& br,
+                                                int b, int h, int wave, int pb, int n0, int m0) {
   using G = WinGeom<FP8>;
   constexpr int KESZ = FP8 ? 1 : 2;
-  const uint8_t* kx = reinterpret_cast<const uint8_t*>(a.k);
+  const KeyMap& km = br.km;
+  const int p_hi = br.p_hi;
+  const uint8_t* kx = reinterpret_cast<const uint8_t*>(br.own_k ? a.k2 : a.k);
   const uint8_t* kring = reinterpret_cast<const uint8_t*>(a.k_ring);
   const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
   const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
@@ -249,7 +252,8 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs
     } else {
       // E4M3 calls have no ring: rows are tokens of the call
       const int tok = (n * km.dil + km.res - km.frame_offset) * L + mm;
-      ld.src[j] = reinterpret_cast<const uint8_t*>(a.k_scales + ((size_t)b * a.H + h) * a.nblk + tok / 64);
+      const float* ksc = br.own_k ? a.k_scales2 : a.k_scales;
+      ld.src[j] = reinterpret_cast<const uint8_t*>(ksc + ((size_t)b * a.H + h) * a.nblk + tok / 64);
     }
   }
 }
@@ -375,7 +379,7 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
                                            float& l_run) {
   const int L = a.L;
   int n0 = br.p_lo / L, m0 = br.p_lo - (br.p_lo / L) * L;
-  win_block_addrs<FP8, SHORTL>(ld, a, br.km, qc.b, qc.h, qc.wave, br.p_lo, n0, m0, br.p_hi);
+  win_block_addrs<FP8, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, br.p_lo, n0, m0);
   win_issue<FP8>(ld, B0, qc.wave);
   win_wait_vmem();
   lds_barrier();
@@ -403,7 +407,7 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
 #pragma unroll
           for (int j = 0; j < WinGeom<FP8>::NJ; ++j) ld.src[j] += ld.inc[j];
         } else {
-          win_block_addrs<FP8, SHORTL>(ld, a, br.km, qc.b, qc.h, qc.wave, pb + BK, n1, m1, br.p_hi);
+          win_block_addrs<FP8, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, pb + BK, n1, m1);
         }
         win_issue<FP8>(ld, nb, qc.wave);
       }
@@ -476,28 +480,31 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   WinLoads<FP8> ld;
   win_load_setup<FP8>(ld, wave, a.H);
 
-  // ---- Q operand registers (B operand of S^T = K Q^T)
+  // ---- Q operand registers (B operand of S^T = K Q^T) of a branch
   bf16x8 qf[8];
   i32x8 q8f[2];
-  float qscale = 1.f;
-  if (!FP8) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.T + tq) * tok_stride +
-                         (size_t)h * WD;
+  auto load_q = [&](const void* qsrc, const float* qscales) {
+    float qscale = 1.f;
+    if (!FP8) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(qsrc) + ((size_t)b * a.T + tq) * tok_stride +
+                           (size_t)h * WD;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s + 8 * g));
-  } else {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)b * a.T + tq) * tok_stride +
-                        (size_t)h * WD;
+      for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s + 8 * g));
+    } else {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(qsrc) + ((size_t)b * a.T + tq) * tok_stride +
+                          (size_t)h * WD;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g);
-      const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g + 16);
-      q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int s = 0; s < 2; ++s) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g);
+        const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g + 16);
+        q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      qscale = qscales[((size_t)b * a.H + h) * a.nblk + tq / 64];
     }
-    qscale = a.q_scales[((size_t)b * a.H + h) * a.nblk + tq / 64];
-  }
-  // log2(e) / sqrt(d) (x the query's block scale): scores in exp2 units
-  qc.cq = 1.4426950408889634f * 0.08838834764831845f * qscale;
+    // log2(e) / sqrt(d) (x the query's block scale): scores in exp2 units
+    qc.cq = 1.4426950408889634f * 0.08838834764831845f * qscale;
+  };
+  load_q(a.q, a.q_scales);
 
   const size_t rowoff = ((size_t)b * a.T + tq) * tok_stride + (size_t)h * WD;
   f32x16 O[4];
@@ -527,7 +534,11 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
     for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
     m_run = -1e30f;
     l_run = 0.f;
-    const BranchRange b1 = branch_range(a, a.dil, f, m0, m_last_wg);
+    BranchRange b1 = branch_range(a, a.dil, f, m0, m_last_wg);
+    if (a.q2) {                                      // the branch has its own q, k (RoPE)
+      load_q(a.q2, a.q_scales2);
+      b1.own_k = true;
+    }
     run_branch<FP8, SHORTL>(a, B0, B1, b1, qc, qf, q8f, ld, O, m_run, l_run);
     fac = 1.f / (l_run + __shfl_xor(l_run, 32, 64)) / (1.f + __expf(-a.gates[a.H + h]));
   }
