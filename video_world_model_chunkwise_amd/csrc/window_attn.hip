@@ -279,25 +279,33 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
                                           float& l_run) {
   // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
   f32x16 S[2];
+  S[0] = f32x16{};
+  S[1] = f32x16{};
+  if (!FP8) {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    S[kt] = f32x16{};
-    if (!FP8) {
+    for (int kt = 0; kt < 2; ++kt) {
       const uint16_t* Ks = reinterpret_cast<const uint16_t*>(cb.K) + (32 * kt + qc.krow) * KST;
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * qc.g)), qf[s], S[kt]);
-    } else {
-      const uint8_t* K8 = cb.K + 32 * kt * K8ST;
+    }
+  } else {
+    // all four E4M3 operands are read before the first product; the products
+    // alternate between the two score tiles
+    i32x8 ka[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
+        const uint8_t* K8 = cb.K + 32 * kt * K8ST;
         const uint4 lo = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][0]);
         const uint4 hi = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][1]);
-        const i32x8 ka = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        S[kt] = mfma32x32x64_fp8(ka, q8f[s], S[kt]);
+        ka[kt][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) S[kt] = mfma32x32x64_fp8(ka[kt][s], q8f[s], S[kt]);
   }
   // ---- key scales, mask, block maximum (before the positive factor cq)
   if (FP8) {
@@ -338,35 +346,51 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
     m_run = m_new;
   }
   // ---- probabilities -> bf16 operands: registers 8j..8j+7 of a tile are keys
-  //      32 kt + 16 j + 8 g + 0..7
+  //      32 kt + 16 j + 8 g + 0..7.  The row sum adds the bf16-rounded
+  //      probabilities (the weights the P V product uses), two per instruction.
   bf16x8 P[2][2];
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], qc.cq, -m_run));
-      l_run += p[r];
-    }
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], qc.cq, -m_run));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
       P[kt][j] = to_bf16x8(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3], p[8 * j + 4],
                            p[8 * j + 5], p[8 * j + 6], p[8 * j + 7]);
+      const uint4 pw = __builtin_bit_cast(uint4, P[kt][j]);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones, l_run, false);
+    }
   }
   // ---- O^T += V^T P^T   (lane: O^T[32dt + 8(r/4) + 4g + r%4][query ql]); the
-  //      V^T operand of (kt, j): features 32 dt + lane%32, keys 32 kt + 16 j + 8 g + 0..7
+  //      V^T operand of (kt, j, dt): features 32 dt + lane%32, keys
+  //      32 kt + 16 j + 8 g + 0..7.  Products in the order (kt, j) outer, dt
+  //      inner: consecutive products accumulate into different tiles and share
+  //      the P operand; every operand is read before the products start.
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(cb.V);
+  bf16x8 vop[16];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int idx = 0; idx < 16; ++idx) {
+    const int dt = idx & 3, j = (idx >> 2) & 1, kt = idx >> 3;
+    const uint8_t* vp = Vb + (32 * kt + 16 * j) * VST;
+    vop[idx] = as_bf16x8(win_read_tr(reinterpret_cast<const uint16_t*>(vp + qc.vo[dt][0])),
+                         win_read_tr(reinterpret_cast<const uint16_t*>(vp + qc.vo[dt][1])));
+  }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+  for (int idx = 0; idx < 16; ++idx) O[idx & 3] = mfma32x32x16(vop[idx], P[idx >> 3][(idx >> 2) & 1], O[idx & 3]);
+  // operands four products ahead of their use, then two reads per product
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint8_t* vp = Vb + (32 * kt + 16 * j) * VST;
-        O[dt] = mfma32x32x16(as_bf16x8(win_read_tr(reinterpret_cast<const uint16_t*>(vp + qc.vo[dt][0])),
-                                       win_read_tr(reinterpret_cast<const uint16_t*>(vp + qc.vo[dt][1]))),
-                             P[kt][j], O[dt]);
-      }
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
 // One windowed branch over its key blocks: online softmax into O (unnormalised)
