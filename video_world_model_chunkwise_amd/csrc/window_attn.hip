@@ -151,6 +151,18 @@ __device__ __forceinline__ BranchRange branch_range(const WinArgs& a, int dil, i
   return r;
 }
 
+// Combine a value with the one of lane ^ 32: the two halves of the wave swap
+// registers inside the vector unit (no LDS round trip); each lane receives
+// its own value and its partner's, in some order.
+__device__ __forceinline__ float max_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // key offset inside a 64-key block of score register r of tile kt (lane group g)
 __device__ __forceinline__ constexpr int key_of(int kt, int r, int g) {
   return 32 * kt + 16 * (r / 8) + 8 * g + 4 * ((r / 4) & 1) + (r & 3);
@@ -309,16 +321,25 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
   }
   // ---- key scales, mask, block maximum (before the positive factor cq)
   if (FP8) {
+    float4 s4[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        s4[kt][rr] = *reinterpret_cast<const float4*>(cb.sk + key_of(kt, 4 * rr, qc.g));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const float4 s4 = *reinterpret_cast<const float4*>(cb.sk + key_of(kt, 4 * rr, qc.g));
-        S[kt][4 * rr] *= s4.x;
-        S[kt][4 * rr + 1] *= s4.y;
-        S[kt][4 * rr + 2] *= s4.z;
-        S[kt][4 * rr + 3] *= s4.w;
+        S[kt][4 * rr] *= s4[kt][rr].x;
+        S[kt][4 * rr + 1] *= s4[kt][rr].y;
+        S[kt][4 * rr + 2] *= s4[kt][rr].z;
+        S[kt][4 * rr + 3] *= s4[kt][rr].w;
       }
+    // every LDS read of the stage (operands, then scales) before the four
+    // products, which alternate between the two score tiles
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   }
   if (!full) {
     // valid iff hi - wl < pk <= hi, i.e. (unsigned)(hi - pk) < wl
@@ -334,7 +355,7 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qc.cq;
+  mx = max_with_partner(mx) * qc.cq;
   if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
     const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -539,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   // ---- first branch: SWA (or the single requested branch)
   const BranchRange b0 = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
   run_branch<FP8, SHORTL>(a, B0, B1, b0, qc, qf, q8f, ld, O, m_run, l_run);
-  float fac = 1.f / (l_run + __shfl_xor(l_run, 32, 64));
+  float fac = 1.f / (sum_with_partner(l_run));
   if (HYBRID) {
     fac *= 1.f / (1.f + __expf(-a.gates[h]));
     // park sig(z_swa) o_swa (fp32) in this query's workspace row
@@ -564,7 +585,7 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
       b1.own_k = true;
     }
     run_branch<FP8, SHORTL>(a, B0, B1, b1, qc, qf, q8f, ld, O, m_run, l_run);
-    fac = 1.f / (l_run + __shfl_xor(l_run, 32, 64)) / (1.f + __expf(-a.gates[a.H + h]));
+    fac = 1.f / (sum_with_partner(l_run)) / (1.f + __expf(-a.gates[a.H + h]));
   }
 
   // ---- epilogue: (+ parked first branch + gated GDN branch) -> bf16 output row
