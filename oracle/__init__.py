@@ -19,6 +19,7 @@ Physical AI" (arXiv 2606.16533, HTML v3):
                rearrange-then-SWA form of Eq. 8, and a scalar brute force;
 * ``fp8``    -- an OCP FP8 E4M3 quantiser with per-64-token-block absmax
                scales, written from the format definition;
+* ``fp4``    -- the same for the 4-bit path (OCP FP4 E2M1 codes);
 * ``hlta``   -- the gated combination of the three branches;
 * ``rope``   -- rotary position embedding of the windowed branches' q and k
                at each branch's (group) positions;
@@ -35,6 +36,8 @@ from .gdn import gdn_recurrent, gdn_literal_eq6, gdn_chunked
 from .window import (windowed_attention, windowed_attention_rows, window_bruteforce,
                      dswa_reshape, frame_index_maps)
 from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, fp8_quantize_blocks, E4M3_MAX
+from .fp4 import (e2m1_round, e2m1_encode, e2m1_decode, fp4_pack, fp4_unpack, fp4_quantize_blocks,
+                  E2M1_MAX)
 from .hlta import hlta, hlta_rows, sigmoid
 from .prologue import l2_normalize, gdn_prologue
 from .rope import rope, rope_angles, branch_positions
@@ -44,6 +47,8 @@ __all__ = [
     "windowed_attention", "windowed_attention_rows", "window_bruteforce", "dswa_reshape",
     "frame_index_maps",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "fp8_quantize_blocks", "E4M3_MAX",
+    "e2m1_round", "e2m1_encode", "e2m1_decode", "fp4_pack", "fp4_unpack", "fp4_quantize_blocks",
+    "E2M1_MAX",
     "hlta", "hlta_rows", "sigmoid", "l2_normalize", "gdn_prologue",
     "rope", "rope_angles", "branch_positions",
 ]

@@ -12,8 +12,9 @@ Readings:
   as parallel branches on one shared q, k, v and mixes them per head:
   ``y = sigmoid(z_swa) o_swa + sigmoid(z_dswa) o_dswa + sigmoid(z_gdn) o_gdn``
   with z of shape [3, H] and no normalisation of the gates.
-* With FP8 windows the SWA/DSWA branches use the dequantised q_hat, k_hat
-  (per-64-token-block absmax e4m3); the GDN branch uses the unquantised q, k.
+* With FP8 (or 4-bit) windows the SWA/DSWA branches use the dequantised
+  q_hat, k_hat (per-64-token-block absmax E4M3, or E2M1); the GDN branch uses
+  the unquantised q, k.
 * A streamed rollout (frames fed call by call, state carried) is defined to
   equal one call over the whole sequence; the oracle is that single call.
 * ``centered=True`` gives both windowed branches Eq. 7's centred band (see
@@ -28,6 +29,7 @@ import numpy as np
 from .gdn import gdn_recurrent
 from .window import windowed_attention_rows
 from .fp8 import fp8_quantize_blocks
+from .fp4 import fp4_quantize_blocks
 from .rope import rope, branch_positions
 
 
@@ -50,6 +52,10 @@ def _window_inputs(q, k, window_qk):
     if window_qk == "fp8":
         _, _, qh = fp8_quantize_blocks(q)
         _, _, kh = fp8_quantize_blocks(k)
+        return qh, kh
+    if window_qk == "fp4":
+        _, _, qh = fp4_quantize_blocks(q)
+        _, _, kh = fp4_quantize_blocks(k)
         return qh, kh
     return q, k
 
