@@ -30,6 +30,9 @@ METRIC = "GDN / hybrid temporal-attention fwd tokens/s + % roofline, H=24 d=128,
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP4_TFLOPS = 10100.0
+# QK^T at the 4-bit peak, P V at the bf16 peak (equal flops): time-weighted peak
+PEAK_FP4_BLEND_TFLOPS = 2.0 / (1.0 / PEAK_FP4_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 
 # algorithmic work per unit (derivation in the design doc)
 GDN_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 2 + 2 * 4      # q, k, v, o bf16 + alpha, beta fp32
@@ -220,6 +223,20 @@ def main():
     t_win = st.run("window_hybrid", lambda: K.kairos_hlta_window_fwd(
         codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
         k_scales=sk, out=bufs["out"], workspace=yws), reps)
+    # the same stage on 4-bit (E2M1) Q/K, and the whole layer with 4-bit windows
+    c4q = torch.empty((w.B, w.T, w.H, w.d // 2), dtype=torch.uint8, device=dev)
+    c4k = torch.empty_like(c4q)
+    t_q4 = st.run("fp4_quant_q", lambda: K.kairos_fp4_quantize(d["q"], c4q, sq), reps)
+    K.kairos_fp4_quantize(d["k"], c4k, sk)
+    t_win4 = st.run("window_hybrid_fp4", lambda: K.kairos_hlta_window_fwd(
+        c4q, c4k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
+        k_scales=sk, out=bufs["out"], workspace=yws), reps)
+    desc4 = K.hlta_desc(w.B, w.T, w.H, w.d, w.L, w.window, w.dilation, window_qk=K.FP4_E2M1)
+    ws4 = torch.empty(K.kairos_hlta_workspace_size(desc4), dtype=torch.uint8, device=dev)
+    t_layer4 = st.run("layer_fp4", lambda: K.kairos_hlta_fwd(
+        d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["gates"], w.L, w.window, w.dilation,
+        window_qk=K.FP4_E2M1, out=bufs["out"], state_out=bufs["state"], workspace=ws4), reps)
+    del ws4, c4q, c4k
     # the same stage with centred windows (Eq. 7 as printed) and the pages' DSWA dilation 6
     t_win_c = st.run("window_hybrid_centered_dil6", lambda: K.kairos_hlta_window_fwd(
         codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, 6, q_scales=sq,
@@ -271,7 +288,7 @@ def main():
     achieved = win_flops / (t_win / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": "win_attn_kernel<fp8, hybrid>",
+                "kernel": "win_attn_kernel<1 (E4M3), hybrid>",
                 "algorithmic_flops_per_launch": win_flops,
                 "avg_launch_ms": round(t_win, 4)}
     # HBM traffic of the kernel from the committed counter summary, valid only
@@ -302,6 +319,14 @@ def main():
         },
         "window_stage": {"ms": round(t_win, 4), "alg_TFLOP_per_s": round(achieved, 1),
                          "pairs_per_bh": pairs},
+        "fp4": {
+            "quant_q_ms": round(t_q4, 4),
+            "quant_alg_GB_per_s": round(d["q"].numel() * 2.5 / (t_q4 / 1e3) / 1e9, 1),
+            "window_stage_ms": round(t_win4, 4),
+            "window_alg_TFLOP_per_s": round(win_flops / (t_win4 / 1e3) / 1e12, 1),
+            "window_mfma_frac": round(win_flops / (t_win4 / 1e3) / 1e12 / PEAK_FP4_BLEND_TFLOPS, 4),
+            "layer_ms": round(t_layer4, 4), "layer_tokens_per_s": round(tokens / (t_layer4 / 1e3)),
+        },
         "window_stage_centered_dil6": {
             "ms": round(t_win_c, 4), "pairs_per_bh": pairs_c,
             "alg_TFLOP_per_s": round(win_flops_c / (t_win_c / 1e3) / 1e12, 1),

@@ -66,7 +66,12 @@ typedef enum {
   KAIROS_ERR_HIP = -8          /* a HIP launch or query failed                    */
 } kairos_status;
 
-typedef enum { KAIROS_F32 = 0, KAIROS_BF16 = 1, KAIROS_FP8_E4M3 = 2 } kairos_dtype;
+typedef enum {
+  KAIROS_F32 = 0,
+  KAIROS_BF16 = 1,
+  KAIROS_FP8_E4M3 = 2,
+  KAIROS_FP4_E2M1 = 3          /* 4-bit windowed Q/K: OCP FP4 E2M1 codes, two per byte */
+} kairos_dtype;
 
 /* Window form of the SWA / DSWA branches (Sec. 2.2.2, Eq. 7).
  *   KAIROS_WINDOW_CAUSAL    query i sees keys i - w < j <= i (w keys with itself)
@@ -90,8 +95,9 @@ typedef struct {
  * KAIROS_BF16, d == 128).  The sequence is T tokens of frames of L tokens
  * (the last frame may be partial when ring_frames == 0).  window w >= 1 in
  * tokens; dilation >= 1.  frame_offset is the absolute index of the call's
- * first frame.  window_qk: KAIROS_BF16, or KAIROS_FP8_E4M3 to quantise the
- * windowed branches' q and k per 64-token block (not with a ring).
+ * first frame.  window_qk: KAIROS_BF16, or KAIROS_FP8_E4M3 / KAIROS_FP4_E2M1
+ * to quantise the windowed branches' q and k per 64-token block (not with a
+ * ring).
  * ring_frames R: 0 for a self-contained call (no keys before token 0);
  * otherwise the call continues a rollout: frames frame_offset-R ..
  * frame_offset-1 (those >= 0) are read from the ring, T must be a multiple of
@@ -156,9 +162,10 @@ int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, co
  * DSWA otherwise (Eq. 8 as a frame-residue index map; nothing is rearranged
  * in memory).  Uses desc->L, window, frame_offset, ring_frames, window_qk and
  * g.{B,T,H,dk}; `dilation` overrides desc->dilation.  With window_qk ==
- * KAIROS_FP8_E4M3, q and k are the E4M3 codes and q_scales / k_scales the
- * per-64-token-block scales written by kairos_fp8_quantize; otherwise q, k are
- * bf16 and the scale pointers must be NULL.  out [B][T][H][d] bf16.  The ring
+ * KAIROS_FP8_E4M3 (KAIROS_FP4_E2M1), q and k are the codes and q_scales /
+ * k_scales the per-64-token-block scales written by kairos_fp8_quantize
+ * (kairos_fp4_quantize); otherwise q, k are bf16 and the scale pointers must
+ * be NULL.  out [B][T][H][d] bf16.  The ring
  * is read, never written.  q and k are used as given: desc->rope_base must be
  * 0 (apply kairos_rope with the branch's dilation first). */
 int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void* q, const void* k,
@@ -180,8 +187,9 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
 
 /* The windowed stage of kairos_hlta_fwd on its own: both windowed branches
  * and the gated combination with an already computed GDN branch output.
- *   q, k       bf16 [B][T][H][128], or E4M3 codes with q_scales / k_scales
- *              (window_qk == KAIROS_FP8_E4M3, as written by kairos_fp8_quantize)
+ *   q, k       bf16 [B][T][H][128], or codes with q_scales / k_scales
+ *              (window_qk == KAIROS_FP8_E4M3 / KAIROS_FP4_E2M1, as written by
+ *              kairos_fp8_quantize / kairos_fp4_quantize)
  *   v          bf16 [B][T][H][128];  o_gdn bf16 [B][T][H][128]
  *   gate_logits [3][H] fp32;  k_ring / v_ring as in kairos_hlta_fwd (read only)
  *   out        bf16 [B][T][H][128], y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn
@@ -242,14 +250,27 @@ int kairos_gdn_prologue(const kairos_gdn_desc* desc, int32_t flags, const void* 
  * frame_offset, rope_base (> 0), window_qk}.
  *   x       [B][T][H][d] bf16
  *   out     window_qk == KAIROS_BF16: [B][T][H][d] bf16, may be x itself (in
- *           place); KAIROS_FP8_E4M3: E4M3 codes [B][T][H][d] uint8 of the
+ *           place); KAIROS_FP4_E2M1: E2M1 codes [B][T][H][d/2] bytes of the
+ *           rotated values, quantised as kairos_fp4_quantize does;
+ *           KAIROS_FP8_E4M3: E4M3 codes [B][T][H][d] uint8 of the
  *           rotated values, quantised as kairos_fp8_quantize does
- *   scales  FP8: [B][H][ceil(T/64)] fp32; bf16: must be NULL
+ *   scales  FP8 / FP4: [B][H][ceil(T/64)] fp32; bf16: must be NULL
  * Angles are reduced in fp64, cos/sin in fp32, the rotation in fp32; bf16
  * output rounds to nearest even.  kairos_rope + kairos_window_fwd per branch
  * equals the windowed branches of kairos_hlta_fwd with RoPE. */
 int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, void* out,
                 float* scales, void* stream);
+
+/* 4-bit quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block), the
+ * 4-bit attention quantisation of the project page (TL;DR / Q3) as OCP FP4
+ * E2M1 codes (the matrix instructions take 4-bit floating-point operands, not
+ * 4-bit integers): s = amax / 6 (fp32; 1 when amax == 0), code = E2M1 of the
+ * correctly rounded fp32 quotient x / s, round to nearest with ties to the
+ * even code, saturating at 6.  codes [B][T][H][d/2] bytes, feature 2i in the
+ * low nibble of byte i; scales [B][H][ceil(T/64)] fp32.  d in {32, 64, 128}.
+ * Errors as for kairos_fp8_quantize. */
+int kairos_fp4_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
+                        int32_t H, int32_t d, void* stream);
 
 /* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block):
  * s = amax / 448 (fp32; 1 when amax == 0), code = E4M3(x / s) with an IEEE

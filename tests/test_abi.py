@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert K.version() == 102
+    assert K.version() == 103
     assert K.status_string(0) == "ok"
     assert "align" in K.status_string(ALIGN)
     assert K.status_string(12345) == "unknown status"

@@ -12,9 +12,9 @@ from __future__ import annotations
 
 from ._lib import (  # noqa: F401
     KairosError, lib, lib_path, symbols, status_string, version,
-    GdnDesc, HltaDesc, F32, BF16, FP8_E4M3, PROLOGUE_NORMALIZE_Q, PROLOGUE_LITERAL_EQ6,
+    GdnDesc, HltaDesc, F32, BF16, FP8_E4M3, FP4_E2M1, PROLOGUE_NORMALIZE_Q, PROLOGUE_LITERAL_EQ6,
     WINDOW_CAUSAL, WINDOW_CENTERED,
-    kairos_gdn_prologue, kairos_rope, kairos_gdn_fwd, kairos_hlta_fwd, kairos_hlta_window_fwd, kairos_window_fwd, kairos_fp8_quantize,
+    kairos_gdn_prologue, kairos_rope, kairos_gdn_fwd, kairos_hlta_fwd, kairos_hlta_window_fwd, kairos_window_fwd, kairos_fp8_quantize, kairos_fp4_quantize,
     kairos_gdn_workspace_size, kairos_hlta_workspace_size, kairos_hlta_ring_frames_required,
     gdn_desc, hlta_desc,
 )

@@ -5,7 +5,7 @@ import ctypes
 import os
 from ctypes import POINTER, byref, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
 WINDOW_CAUSAL, WINDOW_CENTERED = 0, 1
 PROLOGUE_NORMALIZE_Q, PROLOGUE_LITERAL_EQ6 = 1, 2
 
@@ -17,7 +17,7 @@ symbols = (
     "kairos_status_string", "kairos_version", "kairos_gdn_workspace_size",
     "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
     "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
-    "kairos_gdn_prologue", "kairos_rope",
+    "kairos_gdn_prologue", "kairos_rope", "kairos_fp4_quantize",
 )
 
 
@@ -64,6 +64,7 @@ def lib():
         L.kairos_rope.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 4
         L.kairos_fp8_quantize.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                           c_int32, c_void_p]
+        L.kairos_fp4_quantize.argtypes = L.kairos_fp8_quantize.argtypes
         for name in symbols:
             getattr(L, name).restype = c_int if name != "kairos_status_string" else c_char_p
         _lib = L
@@ -184,6 +185,24 @@ def kairos_gdn_fwd(q, k, v, alpha, beta, state_in=None, out=None, state_out=None
     return out, state_out
 
 
+def kairos_fp4_quantize(x, codes=None, scales=None, stream=None):
+    """Per-(b, h, 64-token block) 4-bit (E2M1) quantisation of x [B, T, H, d]
+    bf16.  Returns (codes uint8 [B, T, H, d/2] (two per byte, even feature in
+    the low nibble), scales fp32 [B, H, ceil(T/64)])."""
+    torch = _torch()
+    B, T, H, d = x.shape
+    _need(x, "x", torch.bfloat16, (B, T, H, d), x.device)
+    if codes is None:
+        codes = torch.empty((B, T, H, d // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, (T + 63) // 64), dtype=torch.float32, device=x.device)
+    _need(codes, "codes", torch.uint8, (B, T, H, d // 2), x.device)
+    _need(scales, "scales", torch.float32, (B, H, (T + 63) // 64), x.device)
+    st = lib().kairos_fp4_quantize(_ptr(x), _ptr(codes), _ptr(scales), B, T, H, d, _stream(stream))
+    _check(st, "kairos_fp4_quantize")
+    return codes, scales
+
+
 def kairos_fp8_quantize(x, codes=None, scales=None, stream=None):
     """Per-(b, h, 64-token block) E4M3 quantisation of x [B, T, H, d] bf16.
     Returns (codes uint8 [B, T, H, d], scales fp32 [B, H, ceil(T/64)])."""
@@ -201,19 +220,36 @@ def kairos_fp8_quantize(x, codes=None, scales=None, stream=None):
     return codes, scales
 
 
+def _qk_format(q, d, window_qk):
+    """Windowed-operand format from the tensor: bf16, E4M3 codes [.., d] or
+    E2M1 codes [.., d/2] (uint8; window_qk picks between the byte formats when
+    the shape does not)."""
+    torch = _torch()
+    if q.dtype != torch.uint8:
+        return BF16
+    if window_qk is not None:
+        return window_qk
+    return FP4_E2M1 if q.shape[-1] * 2 == d else FP8_E4M3
+
+
+def _qk_shape(B, T, H, d, fmt):
+    return (B, T, H, d // 2 if fmt == FP4_E2M1 else d)
+
+
 def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=0,
                       k_ring=None, v_ring=None, q_scales=None, k_scales=None, out=None,
-                      stream=None, centered=False):
+                      stream=None, centered=False, window_qk=None):
     """One windowed branch (SWA if dilation == 1, else DSWA), causal or
-    centred.  q, k bf16, or uint8 E4M3 codes with q_scales/k_scales; v bf16
-    [B, T, H, 128]."""
+    centred.  q, k bf16, or uint8 codes with q_scales/k_scales (E4M3
+    [B, T, H, 128], or E2M1 [B, T, H, 64]); v bf16 [B, T, H, 128]."""
     torch = _torch()
     B, T, H, d = v.shape
     dev = v.device
-    fp8 = q.dtype == torch.uint8
+    fmt = _qk_format(q, d, window_qk)
+    fp8 = fmt != BF16
     qk_dtype = torch.uint8 if fp8 else torch.bfloat16
-    _need(q, "q", qk_dtype, (B, T, H, d), dev)
-    _need(k, "k", qk_dtype, (B, T, H, d), dev)
+    _need(q, "q", qk_dtype, _qk_shape(B, T, H, d, fmt), dev)
+    _need(k, "k", qk_dtype, _qk_shape(B, T, H, d, fmt), dev)
     _need(v, "v", torch.bfloat16, (B, T, H, d), dev)
     if fp8:
         nb = (T + 63) // 64
@@ -225,8 +261,8 @@ def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=
     if out is None:
         out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
-    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames,
-                     FP8_E4M3 if fp8 else BF16, centered=centered)
+    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, fmt,
+                     centered=centered)
     st = lib().kairos_window_fwd(byref(desc), dilation, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scales),
                                  _ptr(k_scales), _ptr(k_ring), _ptr(v_ring), _ptr(out),
                                  _stream(stream))
@@ -273,16 +309,17 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
 
 def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, frame_offset=0,
                            ring_frames=0, k_ring=None, v_ring=None, q_scales=None, k_scales=None,
-                           out=None, workspace=None, stream=None, centered=False):
+                           out=None, workspace=None, stream=None, centered=False, window_qk=None):
     """Windowed stage of the hybrid layer: SWA + DSWA + gated combination with
-    o_gdn.  q, k bf16 or uint8 E4M3 codes (with scales); v, o_gdn bf16."""
+    o_gdn.  q, k bf16 or uint8 codes (E4M3 or E2M1, with scales); v, o_gdn bf16."""
     torch = _torch()
     B, T, H, d = v.shape
     dev = v.device
-    fp8 = q.dtype == torch.uint8
+    fmt = _qk_format(q, d, window_qk)
+    fp8 = fmt != BF16
     qk_dtype = torch.uint8 if fp8 else torch.bfloat16
-    _need(q, "q", qk_dtype, (B, T, H, d), dev)
-    _need(k, "k", qk_dtype, (B, T, H, d), dev)
+    _need(q, "q", qk_dtype, _qk_shape(B, T, H, d, fmt), dev)
+    _need(k, "k", qk_dtype, _qk_shape(B, T, H, d, fmt), dev)
     _need(v, "v", torch.bfloat16, (B, T, H, d), dev)
     _need(o_gdn, "o_gdn", torch.bfloat16, (B, T, H, d), dev)
     _need(gate_logits, "gate_logits", torch.float32, (3, H), dev)
@@ -296,8 +333,8 @@ def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, fra
     if out is None:
         out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
-    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames,
-                     FP8_E4M3 if fp8 else BF16, centered=centered)
+    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, fmt,
+                     centered=centered)
     nws = 4 * B * T * H * d
     ws = workspace if workspace is not None else _workspace(nws, dev)
     if ws.numel() < nws:
@@ -357,26 +394,28 @@ def kairos_gdn_prologue(k, alpha_logits, beta_logits, q=None, v=None, literal=Fa
 
 
 def kairos_rope(x, L, dilation, rope_base, frame_offset=0, fp8=False, out=None, scales=None,
-                stream=None):
+                stream=None, window_qk=None):
     """RoPE of one windowed branch's q or k (bf16 [B, T, H, 128]) at the
     positions of the branch with this dilation (1: SWA).  Returns the rotated
-    bf16 tensor, or with fp8=True (E4M3 codes, scales) of the rotated values.
-    out may be x itself for bf16 (in place)."""
+    bf16 tensor, or with fp8=True (window_qk=FP4_E2M1: 4-bit) (codes, scales)
+    of the rotated values.  out may be x itself for bf16 (in place)."""
     torch = _torch()
     B, T, H, d = x.shape
     dev = x.device
     _need(x, "x", torch.bfloat16, (B, T, H, d), dev)
+    fmt = window_qk if window_qk is not None else (FP8_E4M3 if fp8 else BF16)
+    fp8 = fmt != BF16
     if fp8:
-        out = torch.empty((B, T, H, d), dtype=torch.uint8, device=dev) if out is None else out
+        shape = _qk_shape(B, T, H, d, fmt)
+        out = torch.empty(shape, dtype=torch.uint8, device=dev) if out is None else out
         nb = (T + 63) // 64
         scales = torch.empty((B, H, nb), dtype=torch.float32, device=dev) if scales is None else scales
-        _need(out, "out", torch.uint8, (B, T, H, d), dev)
+        _need(out, "out", torch.uint8, shape, dev)
         _need(scales, "scales", torch.float32, (B, H, nb), dev)
     else:
         out = torch.empty_like(x) if out is None else out
         _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
-    desc = hlta_desc(B, T, H, d, L, 1, 1, frame_offset, 0, FP8_E4M3 if fp8 else BF16,
-                     rope_base=rope_base)
+    desc = hlta_desc(B, T, H, d, L, 1, 1, frame_offset, 0, fmt, rope_base=rope_base)
     st = lib().kairos_rope(byref(desc), dilation, _ptr(x), _ptr(out), _ptr(scales if fp8 else None),
                            _stream(stream))
     _check(st, "kairos_rope")

@@ -73,6 +73,12 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// fp4 (OCP E2M1) x fp4 -> fp32, 32x32x64: format 4 for both operands; each
+// lane's 32 codes occupy the low four registers of the operand.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp4(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for

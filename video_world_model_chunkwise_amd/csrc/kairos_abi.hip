@@ -27,6 +27,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// operand format of the windowed branches' q and k: 0 bf16, 1 E4M3 codes,
+// 2 E2M1 codes (two per byte); the last two come with per-block scales
+int qk_format(int window_qk) {
+  return window_qk == KAIROS_FP8_E4M3 ? 1 : window_qk == KAIROS_FP4_E2M1 ? 2 : 0;
+}
+size_t qk_bytes(int qf, size_t n) { return qf == 2 ? n / 2 : qf == 1 ? n : 2 * n; }
+
 int check_gdn_desc(const kairos_gdn_desc* d) {
   if (!d) return KAIROS_ERR_NULL;
   if (d->B < 1 || d->H < 1 || d->T < 0) return KAIROS_ERR_SHAPE;
@@ -53,8 +60,9 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
   if (d->window_kind == KAIROS_WINDOW_CENTERED && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   if (!(d->rope_base >= 0.f) || !(d->rope_base < 3.0e38f) || d->reserved != 0) return KAIROS_ERR_SHAPE;
   if (d->rope_base > 0.f && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
-  if (d->window_qk != KAIROS_BF16 && d->window_qk != KAIROS_FP8_E4M3) return KAIROS_ERR_DTYPE;
-  if (d->window_qk == KAIROS_FP8_E4M3 && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
+  if (d->window_qk != KAIROS_BF16 && d->window_qk != KAIROS_FP8_E4M3 && d->window_qk != KAIROS_FP4_E2M1)
+    return KAIROS_ERR_DTYPE;
+  if (d->window_qk != KAIROS_BF16 && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   // group positions (frame / dil) * L + L and token indices must fit in int32
   const int64_t frames = (d->g.T + d->L - 1) / d->L;
   if ((d->frame_offset + frames + 1) * (int64_t)d->L >= ((int64_t)1 << 30)) return KAIROS_ERR_SHAPE;
@@ -73,7 +81,7 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
 // rotated q, k; the second set only when RoPE gives DSWA its own operands).
 struct HltaWs {
   size_t gdn, o_gdn, ypart;
-  size_t q1, k1, qs1, ks1;   // first-branch operands (fp8 codes / rotated bf16), scales (fp8)
+  size_t q1, k1, qs1, ks1;   // first-branch operands (codes / rotated bf16), scales (codes)
   size_t q2, k2, qs2, ks2;   // second-branch operands (RoPE with dilation > 1)
   bool has1, has2;
   size_t total;
@@ -87,9 +95,9 @@ HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
   HltaWs w{};
   const size_t n = (size_t)d->g.B * d->g.T * d->g.H * d->g.dk;
   const size_t nblk = (size_t)(d->g.T + 63) / 64;
-  const bool fp8 = d->window_qk == KAIROS_FP8_E4M3;
+  const int qf = qk_format(d->window_qk);
+  const bool fp8 = qf != 0;
   const bool rope = d->rope_base > 0.f;
-  const size_t esz = fp8 ? 1 : 2;
   const size_t nsc = fp8 ? (size_t)d->g.B * d->g.H * nblk * 4 : 0;
   size_t off = 0;
   w.gdn = off;
@@ -107,9 +115,9 @@ HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
     size_t* qs = set == 0 ? &w.qs1 : &w.qs2;
     size_t* ks = set == 0 ? &w.ks1 : &w.ks2;
     *q = off;
-    off += align_up(n * esz);
+    off += align_up(qk_bytes(qf, n));
     *k = off;
-    off += align_up(n * esz);
+    off += align_up(qk_bytes(qf, n));
     *qs = off;
     off += align_up(nsc);
     *ks = off;
@@ -138,7 +146,7 @@ hipError_t rope_branch(const kairos_hlta_desc* d, int dil, const void* q, const 
   r.dil = dil;
   r.nblk = (d->g.T + 63) / 64;
   r.frame_offset = (long)d->frame_offset;
-  return launch_rope(r, d->g.dk, (double)d->rope_base, d->window_qk == KAIROS_FP8_E4M3, s);
+  return launch_rope(r, d->g.dk, (double)d->rope_base, qk_format(d->window_qk), s);
 }
 
 int check_gdn_ptrs(const kairos_gdn_desc* d, const void* q, const void* k, const void* v,
@@ -201,7 +209,7 @@ const char* kairos_status_string(int status) {
   }
 }
 
-int kairos_version(void) { return 102; }
+int kairos_version(void) { return 103; }
 
 int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
   if (!bytes) return KAIROS_ERR_NULL;
@@ -261,7 +269,8 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
     const int64_t need = (int64_t)dilation * ((desc->window - 1 + desc->L - 1) / desc->L);
     if (desc->ring_frames < need) return KAIROS_ERR_SHAPE;
   }
-  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  const int qf = qk_format(desc->window_qk);
+  const bool fp8 = qf != 0;
   if (desc->rope_base != 0.f) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!q || !k || !v || !out) return KAIROS_ERR_NULL;
@@ -272,7 +281,7 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
       !aligned16(v_ring))
     return KAIROS_ERR_ALIGN;
   const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
-  const size_t nqk = fp8 ? n : 2 * n;
+  const size_t nqk = qk_bytes(qf, n);
   const size_t nring = (size_t)desc->g.B * desc->ring_frames * desc->L * desc->g.H * desc->g.dk * 2;
   if (overlaps(out, 2 * n, q, nqk) || overlaps(out, 2 * n, k, nqk) || overlaps(out, 2 * n, v, 2 * n) ||
       overlaps(out, 2 * n, k_ring, nring) || overlaps(out, 2 * n, v_ring, nring))
@@ -288,7 +297,7 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
   a.k_ring = (const uint16_t*)k_ring;
   a.v_ring = (const uint16_t*)v_ring;
   a.out = (uint16_t*)out;
-  return hip_status(launch_window(a, fp8, false, (hipStream_t)stream));
+  return hip_status(launch_window(a, qf, false, (hipStream_t)stream));
 }
 
 int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const void* k,
@@ -299,7 +308,8 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
   int st = check_hlta_desc(desc, true);
   if (st != KAIROS_OK) return st;
   const size_t nws = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk * 4;
-  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  const int qf = qk_format(desc->window_qk);
+  const bool fp8 = qf != 0;
   if (desc->rope_base != 0.f) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!q || !k || !v || !o_gdn || !gate_logits || !out) return KAIROS_ERR_NULL;
@@ -310,7 +320,7 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
       !aligned16(k_ring) || !aligned16(v_ring))
     return KAIROS_ERR_ALIGN;
   const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
-  const size_t nqk = fp8 ? n : 2 * n;
+  const size_t nqk = qk_bytes(qf, n);
   const size_t nring = (size_t)desc->g.B * desc->ring_frames * desc->L * desc->g.H * desc->g.dk * 2;
   if (overlaps(out, 2 * n, q, nqk) || overlaps(out, 2 * n, k, nqk) || overlaps(out, 2 * n, v, 2 * n) ||
       overlaps(out, 2 * n, o_gdn, 2 * n) || overlaps(out, 2 * n, k_ring, nring) ||
@@ -335,7 +345,7 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
   a.o_gdn = (const uint16_t*)o_gdn;
   a.gates = gate_logits;
   a.out = (uint16_t*)out;
-  return hip_status(launch_window(a, fp8, true, (hipStream_t)stream));
+  return hip_status(launch_window(a, qf, true, (hipStream_t)stream));
 }
 
 int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, const void* v,
@@ -377,7 +387,8 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   a.gates = gate_logits;
   a.ypart = (float*)(wsb + ws.ypart);
   a.out = (uint16_t*)out;
-  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  const int qf = qk_format(desc->window_qk);
+  const bool fp8 = qf != 0;
   const bool rope = desc->rope_base > 0.f;
   a.q = q;
   a.k = k;
@@ -389,8 +400,8 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     if (rope) {
       e = rope_branch(desc, 1, q, k, q1, k1, qs1, ks1, s);
     } else {
-      e = launch_fp8_quant((const uint16_t*)q, (uint8_t*)q1, qs1, B, T, H, D, s);
-      if (e == hipSuccess) e = launch_fp8_quant((const uint16_t*)k, (uint8_t*)k1, ks1, B, T, H, D, s);
+      e = launch_block_quant((const uint16_t*)q, (uint8_t*)q1, qs1, B, T, H, D, qf, s);
+      if (e == hipSuccess) e = launch_block_quant((const uint16_t*)k, (uint8_t*)k1, ks1, B, T, H, D, qf, s);
     }
     if (e != hipSuccess) return KAIROS_ERR_HIP;
     a.q = q1;
@@ -410,7 +421,7 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     a.q_scales2 = qs2;
     a.k_scales2 = ks2;
   }
-  e = launch_window(a, fp8, true, s);
+  e = launch_window(a, qf, true, s);
   if (e != hipSuccess) return KAIROS_ERR_HIP;
   if (desc->ring_frames > 0) {
     e = launch_ring_update((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)k_ring,
@@ -480,16 +491,17 @@ int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, v
   int st = check_hlta_desc(desc, false);
   if (st != KAIROS_OK) return st;
   if (!(desc->rope_base > 0.f) || dilation < 1) return KAIROS_ERR_SHAPE;
-  const bool fp8 = desc->window_qk == KAIROS_FP8_E4M3;
+  const int qf = qk_format(desc->window_qk);
+  const bool fp8 = qf != 0;
   if (!fp8 && scales) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!x || !out || (fp8 && !scales)) return KAIROS_ERR_NULL;
   if (!aligned16(x) || !aligned16(out) || ((uintptr_t)scales & 3u)) return KAIROS_ERR_ALIGN;
   const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
   const size_t ns = (size_t)desc->g.B * desc->g.H * ((desc->g.T + 63) / 64) * 4;
-  if (fp8 ? overlaps(out, n, x, 2 * n) : (out != x && overlaps(out, 2 * n, x, 2 * n)))
+  if (fp8 ? overlaps(out, qk_bytes(qf, n), x, 2 * n) : (out != x && overlaps(out, 2 * n, x, 2 * n)))
     return KAIROS_ERR_ALIAS;
-  if (overlaps(scales, ns, x, 2 * n) || overlaps(scales, ns, out, fp8 ? n : 2 * n))
+  if (overlaps(scales, ns, x, 2 * n) || overlaps(scales, ns, out, qk_bytes(qf, n)))
     return KAIROS_ERR_ALIAS;
   OperandArgs r;
   memset(&r, 0, sizeof(r));
@@ -504,24 +516,39 @@ int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, v
   r.dil = dilation;
   r.nblk = (desc->g.T + 63) / 64;
   r.frame_offset = (long)desc->frame_offset;
-  return hip_status(launch_rope(r, desc->g.dk, (double)desc->rope_base, fp8, (hipStream_t)stream));
+  return hip_status(launch_rope(r, desc->g.dk, (double)desc->rope_base, qf, (hipStream_t)stream));
 }
 
-int kairos_fp8_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
-                        int32_t H, int32_t d, void* stream) {
+namespace {
+
+int block_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T, int32_t H,
+                   int32_t d, int fmt, void* stream) {
   if (B < 1 || H < 1 || T < 0) return KAIROS_ERR_SHAPE;
   if (d != 32 && d != 64 && d != 128) return KAIROS_ERR_SHAPE;
-  if ((int64_t)B * T * H * d > kMaxElems) return KAIROS_ERR_SHAPE;
+  if ((int64_t)B * T * H * d > kMaxElems || B > 65535 || (H + 3) / 4 > 65535) return KAIROS_ERR_SHAPE;
   if (T == 0) return KAIROS_OK;
   if (!x_bf16 || !codes || !scales) return KAIROS_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(codes) || ((uintptr_t)scales & 3u)) return KAIROS_ERR_ALIGN;
   const size_t n = (size_t)B * T * H * d;
+  const size_t nc = qk_bytes(fmt, n);
   const size_t ns = (size_t)B * H * ((T + 63) / 64) * 4;
-  if (overlaps(codes, n, x_bf16, 2 * n) || overlaps(scales, ns, x_bf16, 2 * n) ||
-      overlaps(scales, ns, codes, n))
+  if (overlaps(codes, nc, x_bf16, 2 * n) || overlaps(scales, ns, x_bf16, 2 * n) ||
+      overlaps(scales, ns, codes, nc))
     return KAIROS_ERR_ALIAS;
-  return hip_status(launch_fp8_quant((const uint16_t*)x_bf16, codes, scales, B, T, H, d,
-                                     (hipStream_t)stream));
+  return hip_status(launch_block_quant((const uint16_t*)x_bf16, codes, scales, B, T, H, d, fmt,
+                                       (hipStream_t)stream));
+}
+
+}  // namespace
+
+int kairos_fp8_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
+                        int32_t H, int32_t d, void* stream) {
+  return block_quantize(x_bf16, codes, scales, B, T, H, d, 1, stream);
+}
+
+int kairos_fp4_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
+                        int32_t H, int32_t d, void* stream) {
+  return block_quantize(x_bf16, codes, scales, B, T, H, d, 2, stream);
 }
 
 }  // extern "C"

@@ -60,7 +60,8 @@ struct OperandArgs {
 struct RopeFreqs {
   double theta[64];         // base^(-2i/D), i < D/2
 };
-hipError_t launch_rope(const OperandArgs& args, int D, double base, bool fp8, hipStream_t stream);
+// fmt: 0 bf16 out, 1 E4M3 codes, 2 E2M1 codes (two per byte)
+hipError_t launch_rope(const OperandArgs& args, int D, double base, int fmt, hipStream_t stream);
 
 // fp32 io when f32, else bf16; D in {32, 64, 128}
 hipError_t launch_gdn_prologue(const PrologueArgs& args, int D, bool f32, bool normalize_q,
@@ -79,11 +80,14 @@ hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t
                             void* workspace, hipStream_t stream);
 int gdn_chunk_waves(int B, int H, int D);
 size_t gdn_chunk_workspace(int B, int T, int H);
-hipError_t launch_fp8_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
-                            int D, hipStream_t stream);
+// Block quantiser: fmt 1 E4M3 (codes [B][T][H][D] bytes), 2 E2M1 (codes
+// [B][T][H][D/2] bytes); scales [B][H][ceil(T/64)]
+hipError_t launch_block_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
+                              int D, int fmt, hipStream_t stream);
 hipError_t launch_ring_update(const uint16_t* k, const uint16_t* v, uint16_t* k_ring,
                               uint16_t* v_ring, int B, int F, int L, int H, int D, long frame_offset,
                               int R, hipStream_t stream);
-hipError_t launch_window(const WinArgs& args, bool fp8, bool hybrid, hipStream_t stream);
+// qf: 0 bf16 q, k; 1 E4M3 codes; 2 E2M1 codes (two per byte)
+hipError_t launch_window(const WinArgs& args, int qf, bool hybrid, hipStream_t stream);
 
 }  // namespace kairos

@@ -1,5 +1,5 @@
-// Operands of the windowed branches: the FP8 E4M3 block quantiser of Q and K,
-// RoPE of Q and K, and both fused.
+// Operands of the windowed branches: the FP8 E4M3 and the 4-bit (FP4 E2M1)
+// block quantisers of Q and K, RoPE of Q and K, and RoPE fused with either.
 //
 // Quantisation (Kairos project page, TL;DR / Q3: FP8 attention quantisation;
 // block size and scale rule as in the 64-token-block absmax workload): per
@@ -15,6 +15,13 @@
 // zero).  The sign of a zero quotient is taken from x.  The encoding is the
 // gfx950 conversion instruction (OCP E4M3, round to nearest even) on values
 // first clamped to +-448, so its saturation mode never matters.
+//
+// 4-bit codes (OCP FP4 E2M1: sign, 2 exponent bits with bias 1, 1 mantissa
+// bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): s = amax / 6, the same
+// correctly rounded quotient clamped to +-6, and the code is the number of
+// rounding thresholds the magnitude passes, each tie (0.25, 0.75, 1.25, 1.75,
+// 2.5, 3.5, 5) going to the code with mantissa bit 0; feature 2i is the low
+// nibble of byte i.
 //
 // RoPE (Kairos paper, arXiv 2606.16533 HTML v3, Sec. 2.2.2: every
 // sliding-window attention block uses RoPE-based relative positional
@@ -72,16 +79,36 @@ __device__ __forceinline__ void operand_values(uint4 v, const float2* csrow, flo
   }
 }
 
+// Correctly rounded y / s from r = RN(1 / s) (one residual step), sign of
+// zero from y.
+__device__ __forceinline__ float quotient(float y, float s, float r) {
+  const float t = y * r;
+  return copysignf(fmaf(fmaf(-t, s, y), r, t), y);
+}
+
+// E2M1 code of a quotient already clamped to +-6
+__device__ __forceinline__ uint32_t e2m1_code(float t) {
+  const float a = fabsf(t);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return ((__float_as_uint(t) >> 28) & 8u) | c;
+}
+
+// E2M1 codes of y[0..7] / s, two per byte (element 2i in the low nibble)
+__device__ __forceinline__ uint32_t e2m1_encode8(const float* y, float s, float r) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    w |= e2m1_code(__builtin_amdgcn_fmed3f(quotient(y[e], s, r), -6.f, 6.f)) << (4 * e);
+  return w;
+}
+
 // E4M3 codes of y[0..7] / s (bytes in order), r = RN(1 / s).
 __device__ __forceinline__ uint2 e4m3_encode8(const float* y, float s, float r) {
   float q[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float t = y[e] * r;
-    const float res = fmaf(-t, s, y[e]);
-    t = copysignf(fmaf(res, r, t), y[e]);
-    q[e] = __builtin_amdgcn_fmed3f(t, -448.f, 448.f);
-  }
+  for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_fmed3f(quotient(y[e], s, r), -448.f, 448.f);
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
@@ -91,8 +118,11 @@ __device__ __forceinline__ uint2 e4m3_encode8(const float* y, float s, float r) 
 
 }  // namespace
 
-template <int D, bool ROPE, bool FP8>
+// OUT: 0 bf16, 1 E4M3 codes, 2 E2M1 codes (packed two per byte)
+template <int D, bool ROPE, int OUT>
 __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreqs fr) {
+  constexpr bool FP8 = OUT != 0;               // quantised: block scales
+  constexpr float QMAX = OUT == 2 ? 6.f : 448.f;
   using G = OperandGeom<D>;
   constexpr int LPR = G::LPR, TPI = G::TPI, NI = G::NI, NP = G::NP, CST = G::CST;
   __shared__ __attribute__((aligned(16))) float2 cs[ROPE ? 64 * CST : 2];
@@ -126,7 +156,7 @@ __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreq
                      : make_uint4(0u, 0u, 0u, 0u);
     }
     auto csrow = [&](int i) { return cs + (i * TPI + tsub) * CST + 4 * sub; };
-    if (!FP8) {
+    if (OUT == 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int t = blk * 64 + i * TPI + tsub;
@@ -164,7 +194,7 @@ __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreq
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-      const float s = amax > 0.f ? amax / 448.f : 1.f;
+      const float s = amax > 0.f ? amax / QMAX : 1.f;
       const float r = 1.f / s;
       if (lane == 0) a.scales[n][((size_t)b * a.H + h) * a.nblk + blk] = s;
 #pragma unroll
@@ -172,9 +202,15 @@ __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreq
         const int t = blk * 64 + i * TPI + tsub;
         float y[8];
         operand_values<D, ROPE>(v[i], ROPE ? csrow(i) : nullptr, y);
-        const uint2 c = e4m3_encode8(y, s, r);
-        if (t < a.T)
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.out[n]) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * sub) = c;
+        if (OUT == 1) {
+          const uint2 c = e4m3_encode8(y, s, r);
+          if (t < a.T)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.out[n]) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * sub) = c;
+        } else {
+          const uint32_t c = e2m1_encode8(y, s, r);
+          if (t < a.T)
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.out[n]) + ((((size_t)b * a.T + t) * a.H + h) * D + 8 * sub) / 2) = c;
+        }
       }
     }
   }
@@ -182,18 +218,18 @@ __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreq
 
 namespace {
 
-template <int D, bool ROPE, bool FP8>
+template <int D, bool ROPE, int OUT>
 void launch_operands_t(const OperandArgs& a, const RopeFreqs& fr, hipStream_t s) {
   const dim3 grid((unsigned)a.nblk, (unsigned)((a.H + 3) / 4), (unsigned)a.B);
-  qk_operand_kernel<D, ROPE, FP8><<<grid, 256, 0, s>>>(a, fr);
+  qk_operand_kernel<D, ROPE, OUT><<<grid, 256, 0, s>>>(a, fr);
 }
 
-template <bool ROPE, bool FP8>
+template <bool ROPE, int OUT>
 hipError_t launch_operands(const OperandArgs& a, int D, const RopeFreqs& fr, hipStream_t s) {
   switch (D) {
-    case 32: launch_operands_t<32, ROPE, FP8>(a, fr, s); break;
-    case 64: launch_operands_t<64, ROPE, FP8>(a, fr, s); break;
-    case 128: launch_operands_t<128, ROPE, FP8>(a, fr, s); break;
+    case 32: launch_operands_t<32, ROPE, OUT>(a, fr, s); break;
+    case 64: launch_operands_t<64, ROPE, OUT>(a, fr, s); break;
+    case 128: launch_operands_t<128, ROPE, OUT>(a, fr, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -201,8 +237,8 @@ hipError_t launch_operands(const OperandArgs& a, int D, const RopeFreqs& fr, hip
 
 }  // namespace
 
-hipError_t launch_fp8_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
-                            int D, hipStream_t stream) {
+hipError_t launch_block_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
+                              int D, int fmt, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   OperandArgs a{};
   a.x[0] = x;
@@ -216,15 +252,19 @@ hipError_t launch_fp8_quant(const uint16_t* x, uint8_t* codes, float* scales, in
   a.dil = 1;
   a.nblk = (T + 63) / 64;
   RopeFreqs fr{};
-  return launch_operands<false, true>(a, D, fr, stream);
+  return fmt == 2 ? launch_operands<false, 2>(a, D, fr, stream) : launch_operands<false, 1>(a, D, fr, stream);
 }
 
-hipError_t launch_rope(const OperandArgs& a, int D, double base, bool fp8, hipStream_t stream) {
+hipError_t launch_rope(const OperandArgs& a, int D, double base, int fmt, hipStream_t stream) {
   if (a.T <= 0 || a.nt <= 0) return hipSuccess;
   RopeFreqs fr;
   for (int i = 0; i < 64; ++i) fr.theta[i] = i < D / 2 ? pow(base, -2.0 * i / D) : 0.0;
-  return fp8 ? launch_operands<true, true>(a, D, fr, stream)
-             : launch_operands<true, false>(a, D, fr, stream);
+  switch (fmt) {
+    case 0: return launch_operands<true, 0>(a, D, fr, stream);
+    case 1: return launch_operands<true, 1>(a, D, fr, stream);
+    case 2: return launch_operands<true, 2>(a, D, fr, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kairos

@@ -55,6 +55,14 @@ constexpr int BQ = 128;          // queries per workgroup
 constexpr int BK = 64;           // keys per block
 constexpr int KST = WD + 16;     // bf16 K LDS row stride (elements): 16 mod 32
 constexpr int K8ST = WD;         // E4M3 K LDS row stride (bytes), 16-byte units XOR-swizzled
+constexpr int K4ST = WD / 2;     // E2M1 K LDS row stride (bytes, two codes per byte), swizzled
+
+// Q/K operand formats (template parameter QF)
+constexpr int QF_BF16 = 0, QF_FP8 = 1, QF_FP4 = 2;
+// bytes of one token's row of q or k in memory
+__device__ __forceinline__ constexpr int qk_row_bytes(int qf) {
+  return qf == QF_FP4 ? WD / 2 : qf == QF_FP8 ? WD : 2 * WD;
+}
 constexpr int VST = 2 * WD;      // V LDS row stride (bytes), 16-byte units XOR-swizzled
 
 // Unpadded K (E4M3) and V rows in LDS: 16-byte unit u of row r is stored in
@@ -62,6 +70,9 @@ constexpr int VST = 2 * WD;      // V LDS row stride (bytes), 16-byte units XOR-
 // operand reads of K, the transposed 4-row reads of V) as fast as padded rows
 // (V faster), with fewer loads per block.
 __device__ __forceinline__ constexpr int k8_swz(int r) { return (r >> 1) & 7; }
+// E2M1 K rows: 4 units; a 16-lane group reads 16 rows at one unit position,
+// which land in 16 distinct 16-byte slots of 256 bytes
+__device__ __forceinline__ constexpr int k4_swz(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ constexpr int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 constexpr float RESCALE_SLACK = 8.f;
 
@@ -87,9 +98,10 @@ __device__ __forceinline__ void win_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0
 // 256 + 32), V rows (256 + 32 bytes), fp32 key scales (E4M3 only).  A block
 // of U 16-byte units per row is U loads of 64 lanes (lane l of load m fills
 // unit 64 m + l).
-template <bool FP8>
+template <int QF>
 struct WinGeom {
-  static constexpr int KU = FP8 ? K8ST / 16 : KST * 2 / 16;   // units per K row (8 / 18)
+  static constexpr bool FP8 = QF != QF_BF16;                  // block-quantised codes + key scales
+  static constexpr int KU = QF == QF_FP4 ? K4ST / 16 : QF == QF_FP8 ? K8ST / 16 : KST * 2 / 16;   // units per K row (4 / 8 / 18)
   static constexpr int VU = VST / 16;                         // units per V row (16)
   static constexpr int KBYTES = BK * KU * 16;
   static constexpr int VBYTES = BK * VU * 16;
@@ -103,14 +115,15 @@ struct KeyMap {
 };
 
 // First element of the frame at sub-frame index n of the group: a frame of
-// the call, or (frames before the call) a ring slot.
+// the call, or (frames before the call) a ring slot.  row_bytes: bytes of one
+// token's row of this head.
 __device__ __forceinline__ const uint8_t* frame_base(const KeyMap& km, const uint8_t* x,
-                                                     const uint8_t* ring, int esz, int b, int h,
-                                                     int T, int H, int n) {
+                                                     const uint8_t* ring, int row_bytes, int b,
+                                                     int h, int T, int H, int n) {
   const int f = n * km.dil + km.res;                       // absolute frame
   if (f >= km.frame_offset)
-    return x + (((size_t)b * T + (size_t)(f - km.frame_offset) * km.L) * H + h) * (size_t)WD * esz;
-  return ring + (((size_t)b * km.R + f % km.R) * km.L * (size_t)H + h) * (size_t)WD * esz;
+    return x + (((size_t)b * T + (size_t)(f - km.frame_offset) * km.L) * H + h) * (size_t)row_bytes;
+  return ring + (((size_t)b * km.R + f % km.R) * km.L * (size_t)H + h) * (size_t)row_bytes;
 }
 
 // Key range of one branch for one query tile, in group-position space.
@@ -173,6 +186,7 @@ struct QueryCtx {
   int b, h, mq, mw_lo, mw_hi, krow, ql, g, wave;
   float cq;
   int k8o[2][2];   // E4M3 K: byte offset of this lane's operand halves (step s, half) in a 32-row tile
+  int k4o[2];      // E2M1 K: byte offset of this lane's operand (step s) in a 32-row tile
   int vo[4][2];    // V: byte offset of this lane's transposed reads (feature tile dt, rows +0 / +4)
 };
 
@@ -186,22 +200,22 @@ struct WinBuf {
 // This wave's share of a block's loads: entry j is load e = wave + 4 j of
 // the block (K loads, then V loads, then the E4M3 scales); per lane the key
 // row and byte offset inside the row, and the source address.
-template <bool FP8>
+template <int QF>
 struct WinLoads {
-  const uint8_t* src[WinGeom<FP8>::NJ];
-  int row[WinGeom<FP8>::NJ];
-  int col[WinGeom<FP8>::NJ];
-  uint32_t inc[WinGeom<FP8>::NJ];   // source step of a block inside one frame (64 rows)
+  const uint8_t* src[WinGeom<QF>::NJ];
+  int row[WinGeom<QF>::NJ];
+  int col[WinGeom<QF>::NJ];
+  uint32_t inc[WinGeom<QF>::NJ];   // source step of a block inside one frame (64 rows)
 };
 
-template <bool FP8>
-__device__ __forceinline__ void win_load_setup(WinLoads<FP8>& ld, int wave, int H) {
-  using G = WinGeom<FP8>;
+template <int QF>
+__device__ __forceinline__ void win_load_setup(WinLoads<QF>& ld, int wave, int H) {
+  using G = WinGeom<QF>;
   const int lane = threadIdx.x % 64;
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
     const int e = wave + 4 * j;
-    ld.inc[j] = e < G::KU ? (uint32_t)BK * H * WD * (FP8 ? 1 : 2)
+    ld.inc[j] = e < G::KU ? (uint32_t)BK * H * qk_row_bytes(QF)
               : e < G::KU + G::VU ? (uint32_t)BK * H * WD * 2 : 4u;    // scales: next 64-token block
   }
 #pragma unroll
@@ -213,7 +227,9 @@ __device__ __forceinline__ void win_load_setup(WinLoads<FP8>& ld, int wave, int 
     else { U = lane; upr = 1; }                      // scales: one per key
     ld.row[j] = U / upr;
     const int u = U % upr;                           // LDS slot of the row
-    if (e < G::KU) ld.col[j] = FP8 ? (u ^ k8_swz(ld.row[j])) * 16 : (u % 16) * 16;   // bf16: padding copies a unit
+    if (e < G::KU)
+      ld.col[j] = QF == QF_FP4 ? (u ^ k4_swz(ld.row[j])) * 16
+                : QF == QF_FP8 ? (u ^ k8_swz(ld.row[j])) * 16 : (u % 16) * 16;   // bf16: padding copies a unit
     else if (e < G::KU + G::VU) ld.col[j] = (u ^ v_swz(ld.row[j])) * 16;
     else ld.col[j] = 0;
   }
@@ -222,11 +238,11 @@ __device__ __forceinline__ void win_load_setup(WinLoads<FP8>& ld, int wave, int 
 // Source addresses of the block at group position pb (sub-frame n0, offset
 // m0): positions past p_hi clamp to p_hi (masked out; clamping keeps loads in
 // bounds and values finite).
-template <bool FP8, bool SHORTL>
-__device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs& a, const BranchRange& br,
+template <int QF, bool SHORTL>
+__device__ __forceinline__ void win_block_addrs(WinLoads<QF>& ld, const WinArgs& a, const BranchRange& br,
                                                 int b, int h, int wave, int pb, int n0, int m0) {
-  using G = WinGeom<FP8>;
-  constexpr int KESZ = FP8 ? 1 : 2;
+  using G = WinGeom<QF>;
+  constexpr int KROW = qk_row_bytes(QF);
   const KeyMap& km = br.km;
   const int p_hi = br.p_hi;
   const uint8_t* kx = reinterpret_cast<const uint8_t*>(br.own_k ? a.k2 : a.k);
@@ -234,17 +250,17 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs
   const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
   const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
   const int L = km.L;
-  const size_t rs_k = (size_t)a.H * WD * KESZ, rs_v = (size_t)a.H * WD * 2;
+  const size_t rs_k = (size_t)a.H * KROW, rs_v = (size_t)a.H * WD * 2;
   const uint8_t* k0 = nullptr;
   const uint8_t* k1 = nullptr;
   const uint8_t* v0 = nullptr;
   const uint8_t* v1 = nullptr;
   if (!SHORTL) {
     const int n1 = min(n0 + 1, p_hi / L);
-    k0 = frame_base(km, kx, kring, KESZ, b, h, a.T, a.H, n0);
-    k1 = frame_base(km, kx, kring, KESZ, b, h, a.T, a.H, n1);
-    v0 = frame_base(km, vx, vring, 2, b, h, a.T, a.H, n0);
-    v1 = frame_base(km, vx, vring, 2, b, h, a.T, a.H, n1);
+    k0 = frame_base(km, kx, kring, KROW, b, h, a.T, a.H, n0);
+    k1 = frame_base(km, kx, kring, KROW, b, h, a.T, a.H, n1);
+    v0 = frame_base(km, vx, vring, 2 * WD, b, h, a.T, a.H, n0);
+    v1 = frame_base(km, vx, vring, 2 * WD, b, h, a.T, a.H, n1);
   }
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
@@ -256,10 +272,10 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs
     if (SHORTL) { n = n0 + m / L; mm = m - (m / L) * L; }
     else { n = n0 + (m >= L ? 1 : 0); mm = m >= L ? m - L : m; }
     if (e < G::KU) {
-      const uint8_t* base = SHORTL ? frame_base(km, kx, kring, KESZ, b, h, a.T, a.H, n) : (n == n0 ? k0 : k1);
+      const uint8_t* base = SHORTL ? frame_base(km, kx, kring, KROW, b, h, a.T, a.H, n) : (n == n0 ? k0 : k1);
       ld.src[j] = base + (size_t)mm * rs_k + ld.col[j];
     } else if (e < G::KU + G::VU) {
-      const uint8_t* base = SHORTL ? frame_base(km, vx, vring, 2, b, h, a.T, a.H, n) : (n == n0 ? v0 : v1);
+      const uint8_t* base = SHORTL ? frame_base(km, vx, vring, 2 * WD, b, h, a.T, a.H, n) : (n == n0 ? v0 : v1);
       ld.src[j] = base + (size_t)mm * rs_v + ld.col[j];
     } else {
       // E4M3 calls have no ring: rows are tokens of the call
@@ -270,9 +286,9 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<FP8>& ld, const WinArgs
   }
 }
 
-template <bool FP8>
-__device__ __forceinline__ void win_issue(const WinLoads<FP8>& ld, const WinBuf& bf, int wave) {
-  using G = WinGeom<FP8>;
+template <int QF>
+__device__ __forceinline__ void win_issue(const WinLoads<QF>& ld, const WinBuf& bf, int wave) {
+  using G = WinGeom<QF>;
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
     const int e = wave + 4 * j;
@@ -284,11 +300,12 @@ __device__ __forceinline__ void win_issue(const WinLoads<FP8>& ld, const WinBuf&
 
 // One key block of a branch: scores from buffer cb, online softmax, O update.
 // The lane's query sees the keys at group positions [hi - wl + 1, hi].
-template <bool FP8>
+template <int QF>
 __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
                                           bool full, const bf16x8 (&qf)[8],
                                           const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
                                           float& l_run) {
+  constexpr bool FP8 = QF != QF_BF16;
   // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
   f32x16 S[2];
   S[0] = f32x16{};
@@ -302,22 +319,30 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
         S[kt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(Ks + 16 * s + 8 * qc.g)), qf[s], S[kt]);
     }
   } else {
-    // all four E4M3 operands are read before the first product; the products
-    // alternate between the two score tiles
+    // all four quantised operands are read before the first product; the
+    // products alternate between the two score tiles.  E4M3: 32 codes (two
+    // 16-byte reads) per lane and step; E2M1: 32 codes in one 16-byte read
+    // (the instruction reads the low four registers of the operand).
     i32x8 ka[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const uint8_t* K8 = cb.K + 32 * kt * K8ST;
-        const uint4 lo = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][0]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][1]);
-        ka[kt][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if (QF == QF_FP4) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(cb.K + 32 * kt * K4ST + qc.k4o[s]);
+          ka[kt][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+        } else {
+          const uint8_t* K8 = cb.K + 32 * kt * K8ST;
+          const uint4 lo = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][0]);
+          const uint4 hi = *reinterpret_cast<const uint4*>(K8 + qc.k8o[s][1]);
+          ka[kt][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
       }
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) S[kt] = mfma32x32x64_fp8(ka[kt][s], q8f[s], S[kt]);
+      for (int kt = 0; kt < 2; ++kt)
+        S[kt] = QF == QF_FP4 ? mfma32x32x64_fp4(ka[kt][s], q8f[s], S[kt]) : mfma32x32x64_fp8(ka[kt][s], q8f[s], S[kt]);
   }
   // ---- key scales, mask, block maximum (before the positive factor cq)
   if (FP8) {
@@ -338,7 +363,7 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
       }
     // every LDS read of the stage (operands, then scales) before the four
     // products, which alternate between the two score tiles
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, QF == QF_FP4 ? 12 : 16, 1);
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   }
   if (!full) {
@@ -416,16 +441,16 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
 
 // One windowed branch over its key blocks: online softmax into O (unnormalised)
 // with running max m_run and lane-partial sum l_run.
-template <bool FP8, bool SHORTL>
+template <int QF, bool SHORTL>
 __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, const WinBuf& B1,
                                            const BranchRange& br, const QueryCtx& qc,
                                            const bf16x8 (&qf)[8], const i32x8 (&q8f)[2],
-                                           WinLoads<FP8>& ld, f32x16 (&O)[4], float& m_run,
+                                           WinLoads<QF>& ld, f32x16 (&O)[4], float& m_run,
                                            float& l_run) {
   const int L = a.L;
   int n0 = br.p_lo / L, m0 = br.p_lo - (br.p_lo / L) * L;
-  win_block_addrs<FP8, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, br.p_lo, n0, m0);
-  win_issue<FP8>(ld, B0, qc.wave);
+  win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, br.p_lo, n0, m0);
+  win_issue<QF>(ld, B0, qc.wave);
   win_wait_vmem();
   lds_barrier();
   const int pq = br.pq0 + qc.mq;                         // this lane's query position
@@ -450,14 +475,14 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
         const bool step = !SHORTL && m0 + BK <= L && n1 == n0 && m1 + BK <= L && pb + 2 * BK - 1 <= br.p_hi;
         if (step) {
 #pragma unroll
-          for (int j = 0; j < WinGeom<FP8>::NJ; ++j) ld.src[j] += ld.inc[j];
+          for (int j = 0; j < WinGeom<QF>::NJ; ++j) ld.src[j] += ld.inc[j];
         } else {
-          win_block_addrs<FP8, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, pb + BK, n1, m1);
+          win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, pb + BK, n1, m1);
         }
-        win_issue<FP8>(ld, nb, qc.wave);
+        win_issue<QF>(ld, nb, qc.wave);
       }
       const bool full = pb >= full_lo && pb + BK - 1 <= full_hi;
-      win_block<FP8>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
+      win_block<QF>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
       win_wait_vmem();
       lds_barrier();
       n0 = n1;
@@ -466,9 +491,10 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   }
 }
 
-template <bool FP8, bool HYBRID, bool SHORTL>
+template <int QF, bool HYBRID, bool SHORTL>
 __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
-  using G = WinGeom<FP8>;
+  using G = WinGeom<QF>;
+  constexpr bool FP8 = G::FP8;
   __shared__ __attribute__((aligned(16))) uint8_t Kb0[G::KBYTES], Kb1[G::KBYTES];
   __shared__ __attribute__((aligned(16))) uint16_t Vb0[G::VBYTES / 2], Vb1[G::VBYTES / 2];
   __shared__ __attribute__((aligned(16))) float sk0[BK], sk1[BK];
@@ -507,6 +533,9 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       qc.k8o[s2][hh] = qc.krow * K8ST + 16 * ((4 * s2 + 2 * qc.g + hh) ^ k8_swz(qc.krow));
+  // E2M1 K operand: row krow, bytes 32 s + 16 g (one 16-byte unit)
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) qc.k4o[s2] = qc.krow * K4ST + 16 * ((2 * s2 + qc.g) ^ k4_swz(qc.krow));
   // V^T operand of feature tile dt: rows 8 (G16/2) + s16/4 (+4), features
   // 32 dt + 16 (G16 % 2) + 4 (s16 % 4) .. +3 (+32 kt + 16 j rows leave the swizzle unchanged)
   {
@@ -522,8 +551,8 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   }
   const int b = qc.b, h = qc.h, g = qc.g;
 
-  WinLoads<FP8> ld;
-  win_load_setup<FP8>(ld, wave, a.H);
+  WinLoads<QF> ld;
+  win_load_setup<QF>(ld, wave, a.H);
 
   // ---- Q operand registers (B operand of S^T = K Q^T) of a branch
   bf16x8 qf[8];
@@ -536,13 +565,18 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * s + 8 * g));
     } else {
-      const uint8_t* qp = reinterpret_cast<const uint8_t*>(qsrc) + ((size_t)b * a.T + tq) * tok_stride +
-                          (size_t)h * WD;
+      constexpr int QROW = qk_row_bytes(QF);
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(qsrc) + (((size_t)b * a.T + tq) * a.H + h) * QROW;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g);
-        const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g + 16);
-        q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if (QF == QF_FP4) {       // step s: features 64 s + 32 g .. +31 = bytes 32 s + 16 g .. +15
+          const uint4 lo = *reinterpret_cast<const uint4*>(qp + 32 * s + 16 * g);
+          q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+        } else {
+          const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g);
+          const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * s + 32 * g + 16);
+          q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
       }
       qscale = qscales[((size_t)b * a.H + h) * a.nblk + tq / 64];
     }
@@ -559,7 +593,7 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
 
   // ---- first branch: SWA (or the single requested branch)
   const BranchRange b0 = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
-  run_branch<FP8, SHORTL>(a, B0, B1, b0, qc, qf, q8f, ld, O, m_run, l_run);
+  run_branch<QF, SHORTL>(a, B0, B1, b0, qc, qf, q8f, ld, O, m_run, l_run);
   float fac = 1.f / (sum_with_partner(l_run));
   if (HYBRID) {
     fac *= 1.f / (1.f + __expf(-a.gates[h]));
@@ -584,7 +618,7 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
       load_q(a.q2, a.q_scales2);
       b1.own_k = true;
     }
-    run_branch<FP8, SHORTL>(a, B0, B1, b1, qc, qf, q8f, ld, O, m_run, l_run);
+    run_branch<QF, SHORTL>(a, B0, B1, b1, qc, qf, q8f, ld, O, m_run, l_run);
     fac = 1.f / (sum_with_partner(l_run)) / (1.f + __expf(-a.gates[a.H + h]));
   }
 
@@ -610,23 +644,24 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
     }
 }
 
-hipError_t launch_window(const WinArgs& args_in, bool fp8, bool hybrid, hipStream_t stream) {
+hipError_t launch_window(const WinArgs& args_in, int qf, bool hybrid, hipStream_t stream) {
   WinArgs a = args_in;
   a.QT = (a.L + BQ - 1) / BQ;
   const long nwg = (long)a.B * a.H * a.F * a.QT;
   if (nwg == 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (hybrid && !a.ypart) return hipErrorInvalidValue;
+  if (qf < QF_BF16 || qf > QF_FP4) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
   const bool shortl = a.L < BK;
-#define KAIROS_WIN_LAUNCH(F8, HY, SL) win_attn_kernel<F8, HY, SL><<<grid, 256, 0, stream>>>(a)
-  if (shortl) {
-    if (fp8) { if (hybrid) KAIROS_WIN_LAUNCH(true, true, true); else KAIROS_WIN_LAUNCH(true, false, true); }
-    else { if (hybrid) KAIROS_WIN_LAUNCH(false, true, true); else KAIROS_WIN_LAUNCH(false, false, true); }
-  } else {
-    if (fp8) { if (hybrid) KAIROS_WIN_LAUNCH(true, true, false); else KAIROS_WIN_LAUNCH(true, false, false); }
-    else { if (hybrid) KAIROS_WIN_LAUNCH(false, true, false); else KAIROS_WIN_LAUNCH(false, false, false); }
-  }
+#define KAIROS_WIN_LAUNCH(QQ, HY, SL) win_attn_kernel<QQ, HY, SL><<<grid, 256, 0, stream>>>(a)
+#define KAIROS_WIN_QF(QQ)                                                                  \
+  if (shortl) { if (hybrid) KAIROS_WIN_LAUNCH(QQ, true, true); else KAIROS_WIN_LAUNCH(QQ, false, true); } \
+  else { if (hybrid) KAIROS_WIN_LAUNCH(QQ, true, false); else KAIROS_WIN_LAUNCH(QQ, false, false); }
+  if (qf == QF_FP4) { KAIROS_WIN_QF(QF_FP4) }
+  else if (qf == QF_FP8) { KAIROS_WIN_QF(QF_FP8) }
+  else { KAIROS_WIN_QF(QF_BF16) }
+#undef KAIROS_WIN_QF
 #undef KAIROS_WIN_LAUNCH
   return hipGetLastError();
 }
