@@ -184,6 +184,7 @@ __device__ __forceinline__ constexpr int key_of(int kt, int r, int g) {
 // Per-lane query state shared by the branch loops.
 struct QueryCtx {
   int b, h, mq, mw_lo, mw_hi, krow, ql, g, wave;
+  bool active;     // the wave has at least one query row inside the frame
   float cq;
   int k8o[2][2];   // E4M3 K: byte offset of this lane's operand halves (step s, half) in a 32-row tile
   int k4o[2];      // E2M1 K: byte offset of this lane's operand (step s) in a 32-row tile
@@ -482,7 +483,9 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
         win_issue<QF>(ld, nb, qc.wave);
       }
       const bool full = pb >= full_lo && pb + BK - 1 <= full_hi;
-      win_block<QF>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
+      // a wave whose rows all lie past the frame's end (the last, partial
+      // query tile) only loads its share of the blocks and keeps the barriers
+      if (qc.active) win_block<QF>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
       win_wait_vmem();
       lds_barrier();
       n0 = n1;
@@ -523,6 +526,7 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   const size_t tq = (size_t)f * a.L + qc.mq;       // token index of the query
   const size_t tok_stride = (size_t)a.H * WD;
   qc.mw_lo = min(m0 + 32 * wave, m_last_wg);       // wave's query rows (clamped)
+  qc.active = m0 + 32 * wave < Lf;
   qc.mw_hi = min(m0 + 32 * wave + 31, m_last_wg);
   // score row of this lane's A operand: key pi(ql) of each 32-key tile
   qc.krow = 16 * (qc.ql / 16) + 8 * ((qc.ql / 4) & 1) + 4 * ((qc.ql / 8) & 1) + (qc.ql & 3);
