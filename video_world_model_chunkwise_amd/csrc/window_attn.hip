@@ -215,13 +215,13 @@ __device__ __forceinline__ void win_load_setup(WinLoads<QF>& ld, int wave, int H
   const int lane = threadIdx.x % 64;
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
-    const int e = wave + 4 * j;
+    const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
     ld.inc[j] = e < G::KU ? (uint32_t)BK * H * qk_row_bytes(QF)
               : e < G::KU + G::VU ? (uint32_t)BK * H * WD * 2 : 4u;    // scales: next 64-token block
   }
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
-    const int e = wave + 4 * j;
+    const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
     int U, upr;
     if (e < G::KU) { U = 64 * e + lane; upr = G::KU; }
     else if (e < G::KU + G::VU) { U = 64 * (e - G::KU) + lane; upr = G::VU; }
@@ -265,7 +265,7 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<QF>& ld, const WinArgs&
   }
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
-    const int e = wave + 4 * j;
+    const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
     if (e >= G::NLOAD) continue;
     const int d = min(pb + ld.row[j], p_hi) - pb;
     const int m = m0 + d;
@@ -292,7 +292,7 @@ __device__ __forceinline__ void win_issue(const WinLoads<QF>& ld, const WinBuf& 
   using G = WinGeom<QF>;
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
-    const int e = wave + 4 * j;
+    const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
     if (e < G::KU) to_lds16(ld.src[j], bf.K + 1024 * e);
     else if (e < G::KU + G::VU) to_lds16(ld.src[j], reinterpret_cast<uint8_t*>(bf.V) + 1024 * (e - G::KU));
     else if (e < G::NLOAD) to_lds4(ld.src[j], bf.sk);
