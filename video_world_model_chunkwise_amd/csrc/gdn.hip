@@ -977,7 +977,7 @@ static hipError_t launch_scan(const uint16_t* q, const uint16_t* k, const uint16
 hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* alpha, const float* beta, const float* state_in,
                             uint16_t* out, float* state_out, int B, int T, int H, int D, int nw,
-                            void* workspace, hipStream_t stream) {
+                            void* workspace, hipStream_t stream, hipEvent_t after_prep) {
   if (nw <= 0) nw = gdn_chunk_waves(B, H, D);
   const int nchunks = (T + CH - 1) / CH;
   const size_t nt = (size_t)B * H * nchunks;
@@ -990,6 +990,10 @@ hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t
     else if (D == 64) gdn_prep_kernel<64><<<(unsigned)nt, 64, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
     else return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (after_prep) {
+    const hipError_t e = hipEventRecord(after_prep, stream);
     if (e != hipSuccess) return e;
   }
   if (D == 128) {

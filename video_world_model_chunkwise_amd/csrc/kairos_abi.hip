@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kairos.h"
 #include "common.hpp"
 
@@ -188,6 +190,38 @@ void fill_win_args(WinArgs& a, const kairos_hlta_desc* d) {
   a.nblk = (d->g.T + 63) / 64;
   a.centered = d->window_kind == KAIROS_WINDOW_CENTERED ? 1 : 0;
   a.frame_offset = (long)d->frame_offset;
+}
+
+// Per-device side stream of a layer call: the windowed branches' operand
+// pre-passes (block quantisers, RoPE) read only q and k, so they run beside
+// the gated delta rule's scan, which leaves part of the chip idle (one
+// workgroup per (b, h, row half), latency-bound), and join before the window
+// kernel.  Created on first use and kept until the process ends; the mutex
+// orders the event record / wait pairs of concurrent callers.
+struct SideStream {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+
+// The current device's side stream, or nullptr (then the pre-passes stay on
+// the caller's stream).
+SideStream* side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& sd = g_side[dev];
+  std::lock_guard<std::mutex> lk(g_side_init);
+  if (!sd.ready) {
+    if (!sd.s && hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (!sd.fork && hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (!sd.join && hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) return nullptr;
+    sd.ready = true;
+  }
+  return &sd;
 }
 
 }  // namespace
@@ -374,10 +408,18 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   const int B = desc->g.B, T = desc->g.T, H = desc->g.H, D = desc->g.dk;
   uint8_t* wsb = (uint8_t*)workspace;
   uint16_t* o_gdn = (uint16_t*)(wsb + ws.o_gdn);
+  // operand pre-passes go to the side stream once the gated delta rule's
+  // prep kernel is done (both are bandwidth-bound; the scan is not)
+  SideStream* sd = (T > 0 && (ws.has1 || ws.has2)) ? side_stream() : nullptr;
+  std::unique_lock<std::mutex> lk;
+  if (sd) lk = std::unique_lock<std::mutex>(sd->mu);
   hipError_t e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha,
-                                  beta, state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, s);
+                                  beta, state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, s,
+                                  sd ? sd->fork : nullptr);
   if (e != hipSuccess) return KAIROS_ERR_HIP;
   if (T == 0) return KAIROS_OK;
+  const hipStream_t so = sd ? sd->s : s;
+  if (sd && hipStreamWaitEvent(so, sd->fork, 0) != hipSuccess) return KAIROS_ERR_HIP;
   WinArgs a;
   fill_win_args(a, desc);
   a.v = (const uint16_t*)v;
@@ -398,10 +440,10 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     float* qs1 = fp8 ? (float*)(wsb + ws.qs1) : nullptr;
     float* ks1 = fp8 ? (float*)(wsb + ws.ks1) : nullptr;
     if (rope) {
-      e = rope_branch(desc, 1, q, k, q1, k1, qs1, ks1, s);
+      e = rope_branch(desc, 1, q, k, q1, k1, qs1, ks1, so);
     } else {
-      e = launch_block_quant((const uint16_t*)q, (uint8_t*)q1, qs1, B, T, H, D, qf, s);
-      if (e == hipSuccess) e = launch_block_quant((const uint16_t*)k, (uint8_t*)k1, ks1, B, T, H, D, qf, s);
+      e = launch_block_quant((const uint16_t*)q, (uint8_t*)q1, qs1, B, T, H, D, qf, so);
+      if (e == hipSuccess) e = launch_block_quant((const uint16_t*)k, (uint8_t*)k1, ks1, B, T, H, D, qf, so);
     }
     if (e != hipSuccess) return KAIROS_ERR_HIP;
     a.q = q1;
@@ -414,13 +456,15 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     void* k2 = wsb + ws.k2;
     float* qs2 = fp8 ? (float*)(wsb + ws.qs2) : nullptr;
     float* ks2 = fp8 ? (float*)(wsb + ws.ks2) : nullptr;
-    e = rope_branch(desc, desc->dilation, q, k, q2, k2, qs2, ks2, s);
+    e = rope_branch(desc, desc->dilation, q, k, q2, k2, qs2, ks2, so);
     if (e != hipSuccess) return KAIROS_ERR_HIP;
     a.q2 = q2;
     a.k2 = k2;
     a.q_scales2 = qs2;
     a.k_scales2 = ks2;
   }
+  if (sd && (hipEventRecord(sd->join, so) != hipSuccess || hipStreamWaitEvent(s, sd->join, 0) != hipSuccess))
+    return KAIROS_ERR_HIP;
   e = launch_window(a, qf, true, s);
   if (e != hipSuccess) return KAIROS_ERR_HIP;
   if (desc->ring_frames > 0) {

@@ -77,7 +77,8 @@ hipError_t launch_gdn_f32(const float* q, const float* k, const float* v, const 
 hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* alpha, const float* beta, const float* state_in,
                             uint16_t* out, float* state_out, int B, int T, int H, int D, int nw,
-                            void* workspace, hipStream_t stream);
+                            void* workspace, hipStream_t stream,
+                            hipEvent_t after_prep = nullptr);
 int gdn_chunk_waves(int B, int H, int D);
 size_t gdn_chunk_workspace(int B, int T, int H);
 // Block quantiser: fmt 1 E4M3 (codes [B][T][H][D] bytes), 2 E2M1 (codes
