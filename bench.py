@@ -91,6 +91,18 @@ def cpu_baseline(w):
     t0 = time.perf_counter()
     oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
     c_gdn = (time.perf_counter() - t0) / Tg                  # s per token (all heads)
+    # the same loop on one BLAS thread, over a quarter of the tokens
+    c_gdn_1 = None
+    try:
+        from threadpoolctl import threadpool_limits
+        T1 = Tg // 4
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.gdn_recurrent(inp["q"][:, :T1], inp["k"][:, :T1], inp["v"][:, :T1],
+                                 inp["alpha"][:, :T1], inp["beta"][:, :T1])
+            c_gdn_1 = (time.perf_counter() - t0) / T1
+    except Exception:
+        pass
     # (2) windowed branches: rows of the last frame of a 2*dil+1-frame prefix, Hs heads
     Hs = 4
     F = 2 * w.dilation + 1
@@ -115,7 +127,22 @@ def cpu_baseline(w):
                    f"per-token costs summed and scaled to {w.H} heads"),
         "seconds": round(time.perf_counter() - t_all, 2),
         "per_token_s": {"gdn": c_gdn, "fp8_quant": c_quant, "windows": c_win},
+        "gdn_tokens_per_s_1_thread": (round(1.0 / c_gdn_1, 1) if c_gdn_1 else None),
+        "host": host_description(),
     }
+
+
+def host_description():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
 
 
 # ------------------------------------------------------------------ GPU timing helpers
@@ -127,13 +154,15 @@ class StageTimer:
         self.torch = torch
         self.acc = {}
 
-    def run(self, name, fn, reps):
+    def run(self, name, fn, reps, before=None):
         torch = self.torch
         fn()                                        # untimed: first launch loads the kernel
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         for a, b in ev:
+            if before is not None:
+                before()                            # untimed (e.g. a cache flush)
             a.record()
             fn()
             b.record()
@@ -223,6 +252,14 @@ def main():
     t_win = st.run("window_hybrid", lambda: K.kairos_hlta_window_fwd(
         codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
         k_scales=sk, out=bufs["out"], workspace=yws), reps)
+    # cold launches: the 256 MB Infinity Cache overwritten (a 512 MB fill) before each
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(1)
+    t_layer_warm = st.run("layer_warm", step, reps)
+    t_layer_cold = st.run("layer_cold", step, 3, before=flush)
+    t_gdn_cold = st.run("gdn_chunk_cold", lambda: K.kairos_gdn_fwd(
+        d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=o_gdn, state_out=S), 3, before=flush)
+    del flush_buf
     # the same stage on 4-bit (E2M1) Q/K, and the whole layer with 4-bit windows
     c4q = torch.empty((w.B, w.T, w.H, w.d // 2), dtype=torch.uint8, device=dev)
     c4k = torch.empty_like(c4q)
@@ -319,6 +356,9 @@ def main():
         },
         "window_stage": {"ms": round(t_win, 4), "alg_TFLOP_per_s": round(achieved, 1),
                          "pairs_per_bh": pairs},
+        "cold_vs_warm": {"layer_warm_ms": round(t_layer_warm, 4), "layer_cold_ms": round(t_layer_cold, 4),
+                         "gdn_branch_warm_ms": round(t_gdn, 4), "gdn_branch_cold_ms": round(t_gdn_cold, 4),
+                         "flush": "512 MB fill before each timed launch (Infinity Cache 256 MB)"},
         "fp4": {
             "quant_q_ms": round(t_q4, 4),
             "quant_alg_GB_per_s": round(d["q"].numel() * 2.5 / (t_q4 / 1e3) / 1e9, 1),
@@ -392,9 +432,19 @@ def workload_breakdown(K, torch, WORKLOADS, make_device_inputs, reps):
     out["gdn_B2H16T4096"] = {"ms": round(t, 4), "tokens_per_s": round(w1.B * w1.T / (t / 1e3)),
                              "alg_GB_per_s": round(th * GDN_BYTES_PER_TOKEN_HEAD / (t / 1e3) / 1e9, 1)}
     del d, o, S
-    # bf16 hybrid layer, B1 H24 21 x 1560
+    # bf16 hybrid layer, B1 H24 21 x 1560, and its gated delta rule branch alone
     w2 = WORKLOADS[2]
     d = make_device_inputs(w2, dev)
+    o = torch.empty_like(d["v"])
+    S = torch.empty((w2.B, w2.H, w2.d, w2.d), dtype=torch.float32, device=dev)
+    fn = lambda: K.kairos_gdn_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=o, state_out=S)
+    t = st.run("gdn_B1H24T32760", fn, reps)
+    th = w2.B * w2.T * w2.H
+    gb = th * GDN_BYTES_PER_TOKEN_HEAD + 2 * w2.B * w2.H * w2.d * w2.d * 4
+    out["gdn_B1H24T32760"] = {"ms": round(t, 4), "tokens_per_s": round(w2.B * w2.T / (t / 1e3)),
+                              "alg_GB_per_s": round(gb / (t / 1e3) / 1e9, 1),
+                              "hbm_frac": round(gb / (t / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del o, S
     bufs = alloc_layer(K, torch, w2, d, False)
     fn = layer_step_fn(K, d, w2, bufs, False)
     fn()
