@@ -459,6 +459,8 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   const int wl = hi - (pq - br.back) + 1;                // and the window's length
   const int full_lo = br.pq0 + qc.mw_hi - br.back;       // blocks inside every window of the wave
   const int full_hi = min(br.pq0 + qc.mw_lo + br.fwd, br.p_last);
+  const int need_lo = br.pq0 + qc.mw_lo - br.back;       // keys inside some window of the wave
+  const int need_hi = min(br.pq0 + qc.mw_hi + br.fwd, br.p_last);
   for (int jb = 0; jb < br.nb; jb += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -484,8 +486,11 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       }
       const bool full = pb >= full_lo && pb + BK - 1 <= full_hi;
       // a wave whose rows all lie past the frame's end (the last, partial
-      // query tile) only loads its share of the blocks and keeps the barriers
-      if (qc.active) win_block<QF>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
+      // query tile), or whose windows all miss this block, only loads its
+      // share of the block and keeps the barriers: a block masked for every
+      // lane adds nothing to O, l or the running maximum
+      const bool touch = pb + BK - 1 >= need_lo && pb <= need_hi;
+      if (qc.active && touch) win_block<QF>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
       win_wait_vmem();
       lds_barrier();
       n0 = n1;
