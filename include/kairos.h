@@ -180,15 +180,17 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
  *                with the call's last min(R, F) frames
  *   out          [B][T][H][d] bf16; state_out as in kairos_gdn_fwd
  *   workspace    >= kairos_hlta_workspace_size bytes
- * Streams: everything is ordered on `stream`.  When the windowed branches
- * need operand pre-passes (quantised Q/K or RoPE), those run on a side
- * stream the library creates on the device's first such call and keeps until
- * the process ends; they wait for an event recorded on `stream` and `stream`
- * waits for them before the window kernel, so the call behaves as one stream
- * and can be captured into a graph (make one call on the device before the
- * first capture, so the side stream is not created during capture).  Calls
- * from several host threads are safe; their pre-passes share the side
- * stream. */
+ * Streams: everything is ordered on `stream`.  Part of the work may run on
+ * a side stream the library creates on the device's first layer call and
+ * keeps until the process ends: the windowed branches' operand pre-passes
+ * (quantised Q/K, RoPE), or, when the window kernel and the GDN scan fit on
+ * the device together (e.g. one streamed frame), the whole GDN branch.  The
+ * side stream waits for an event recorded on `stream`, and `stream` waits
+ * for it before anything that reads its results, so the call behaves as one
+ * stream and can be captured into a graph (make one call on the device
+ * before the first capture, so the side stream is not created during
+ * capture).  Calls from several host threads are safe; their side work
+ * shares the side stream. */
 int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, const float* gate_logits,
                     const float* state_in, void* k_ring, void* v_ring, void* out,

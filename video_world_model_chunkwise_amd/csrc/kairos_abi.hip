@@ -202,7 +202,8 @@ struct SideStream {
   std::mutex mu;
   bool ready = false;
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, gdn = nullptr;
+  int cus = 0;   // compute units of the device
 };
 constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
@@ -219,9 +220,26 @@ SideStream* side_stream() {
     if (!sd.s && hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
     if (!sd.fork && hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
     if (!sd.join && hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (!sd.gdn && hipEventCreateWithFlags(&sd.gdn, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipDeviceGetAttribute(&sd.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return nullptr;
     sd.ready = true;
   }
   return &sd;
+}
+
+// Whether a layer call runs its GDN branch beside the window kernel (the
+// window epilogue then leaves the windowed sum in fp32 and a combine kernel
+// adds the gated GDN output), rather than before it: only when both grids
+// fit on the device at once (two workgroups per compute unit), i.e. when the
+// window kernel alone would leave compute units idle, as for one streamed
+// frame.  On larger calls the extra fp32 round trip and the scan's share of
+// the compute units cost more than the overlap saves (measured: one 1560-
+// token frame at H 24 -10%; 21 frames +10%; the B4 16 x 3600 FP8 layer +4%).
+bool overlap_gdn(const kairos_hlta_desc* d, const SideStream* sd) {
+  if (!sd || sd->cus <= 0 || d->g.dk != 128) return false;
+  const long win = window_workgroups(d->g.B, d->g.T, d->g.H, d->L);
+  const long gdn = (long)d->g.B * d->g.H * (d->g.dk / (16 * gdn_chunk_waves(d->g.B, d->g.H, d->g.dk)));
+  return win + gdn <= 2L * sd->cus;
 }
 
 }  // namespace
@@ -408,24 +426,40 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   const int B = desc->g.B, T = desc->g.T, H = desc->g.H, D = desc->g.dk;
   uint8_t* wsb = (uint8_t*)workspace;
   uint16_t* o_gdn = (uint16_t*)(wsb + ws.o_gdn);
-  // operand pre-passes go to the side stream once the gated delta rule's
-  // prep kernel is done (both are bandwidth-bound; the scan is not)
-  SideStream* sd = (T > 0 && (ws.has1 || ws.has2)) ? side_stream() : nullptr;
+  // Two schedules, both ordered as one stream for the caller:
+  // * overlapped: the GDN branch runs on the side stream beside the operand
+  //   pre-passes and the window kernel, whose epilogue leaves the windowed
+  //   sum in fp32; a combine kernel adds the gated GDN output;
+  // * otherwise: the GDN branch first, the operand pre-passes on the side
+  //   stream once its prep kernel is done (both are bandwidth-bound; the
+  //   scan is not), the window kernel's epilogue adds the GDN output.
+  SideStream* sd = T > 0 ? side_stream() : nullptr;
+  const bool ovl = overlap_gdn(desc, sd);
+  if (!ovl && !ws.has1 && !ws.has2) sd = nullptr;      // one stream is enough
   std::unique_lock<std::mutex> lk;
   if (sd) lk = std::unique_lock<std::mutex>(sd->mu);
-  hipError_t e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha,
-                                  beta, state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, s,
-                                  sd ? sd->fork : nullptr);
-  if (e != hipSuccess) return KAIROS_ERR_HIP;
+  hipError_t e;
+  if (ovl) {
+    if (hipEventRecord(sd->fork, s) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+      return KAIROS_ERR_HIP;
+    e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha, beta,
+                         state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, sd->s);
+    if (e != hipSuccess || hipEventRecord(sd->gdn, sd->s) != hipSuccess) return KAIROS_ERR_HIP;
+  } else {
+    e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha, beta,
+                         state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, s,
+                         sd ? sd->fork : nullptr);
+    if (e != hipSuccess) return KAIROS_ERR_HIP;
+  }
   if (T == 0) return KAIROS_OK;
-  const hipStream_t so = sd ? sd->s : s;
-  if (sd && hipStreamWaitEvent(so, sd->fork, 0) != hipSuccess) return KAIROS_ERR_HIP;
+  const hipStream_t so = (sd && !ovl) ? sd->s : s;   // stream of the operand pre-passes
+  if (so != s && hipStreamWaitEvent(so, sd->fork, 0) != hipSuccess) return KAIROS_ERR_HIP;
   WinArgs a;
   fill_win_args(a, desc);
   a.v = (const uint16_t*)v;
   a.k_ring = (const uint16_t*)k_ring;
   a.v_ring = (const uint16_t*)v_ring;
-  a.o_gdn = o_gdn;
+  a.o_gdn = ovl ? nullptr : o_gdn;
   a.gates = gate_logits;
   a.ypart = (float*)(wsb + ws.ypart);
   a.out = (uint16_t*)out;
@@ -463,10 +497,15 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     a.q_scales2 = qs2;
     a.k_scales2 = ks2;
   }
-  if (sd && (hipEventRecord(sd->join, so) != hipSuccess || hipStreamWaitEvent(s, sd->join, 0) != hipSuccess))
+  if (so != s && (hipEventRecord(sd->join, so) != hipSuccess || hipStreamWaitEvent(s, sd->join, 0) != hipSuccess))
     return KAIROS_ERR_HIP;
   e = launch_window(a, qf, true, s);
   if (e != hipSuccess) return KAIROS_ERR_HIP;
+  if (ovl) {
+    if (hipStreamWaitEvent(s, sd->gdn, 0) != hipSuccess) return KAIROS_ERR_HIP;
+    e = launch_hlta_combine(a.ypart, o_gdn, gate_logits, (uint16_t*)out, B, T, H, s);
+    if (e != hipSuccess) return KAIROS_ERR_HIP;
+  }
   if (desc->ring_frames > 0) {
     e = launch_ring_update((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)k_ring,
                            (uint16_t*)v_ring, B, T / desc->L, desc->L, H, D,

@@ -22,7 +22,9 @@ struct WinArgs {
   const float* k_scales2;
   const uint16_t* k_ring;   // [B][R][L][H][128] bf16 or null
   const uint16_t* v_ring;
-  const uint16_t* o_gdn;    // bf16 [B][T][H][128] (hybrid only)
+  const uint16_t* o_gdn;    // bf16 [B][T][H][128] (hybrid only); null: the epilogue leaves
+                            // sig(z_swa) o_swa + sig(z_dswa) o_dswa (fp32) in ypart and
+                            // launch_hlta_combine adds the gated GDN branch
   const float* gates;       // logits [3][H] (hybrid only)
   float* ypart;             // fp32 [B][T][H][128] scratch for the first branch (hybrid only)
   uint16_t* out;            // bf16 [B][T][H][128]
@@ -90,5 +92,12 @@ hipError_t launch_ring_update(const uint16_t* k, const uint16_t* v, uint16_t* k_
                               int R, hipStream_t stream);
 // qf: 0 bf16 q, k; 1 E4M3 codes; 2 E2M1 codes (two per byte)
 hipError_t launch_window(const WinArgs& args, int qf, bool hybrid, hipStream_t stream);
+// Workgroups of one window-kernel launch over B x T x H with frames of L tokens.
+long window_workgroups(int B, int T, int H, int L);
+
+// y = bf16_rne(ypart + sig(z_gdn[h]) o_gdn) over [B][T][H][128] (the hybrid
+// window kernel's epilogue when the GDN branch ran beside it).
+hipError_t launch_hlta_combine(const float* ypart, const uint16_t* o_gdn, const float* gates,
+                               uint16_t* out, int B, int T, int H, hipStream_t stream);
 
 }  // namespace kairos

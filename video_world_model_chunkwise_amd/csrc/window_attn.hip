@@ -633,6 +633,20 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
 
   // ---- epilogue: (+ parked first branch + gated GDN branch) -> bf16 output row
   if (!q_valid) return;
+  if (HYBRID && !a.o_gdn) {
+    // the GDN branch runs beside this kernel: leave both windowed branches' sum
+    float* yp = a.ypart + rowoff;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float4* p4 = reinterpret_cast<float4*>(yp + 32 * dt + 8 * rq + 4 * g);
+        const float4 y1 = *p4;
+        *p4 = make_float4(fac * O[dt][4 * rq] + y1.x, fac * O[dt][4 * rq + 1] + y1.y,
+                          fac * O[dt][4 * rq + 2] + y1.z, fac * O[dt][4 * rq + 3] + y1.w);
+      }
+    return;
+  }
   const float gg = HYBRID ? 1.f / (1.f + __expf(-a.gates[2 * a.H + h])) : 0.f;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -651,6 +665,41 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
       }
       *reinterpret_cast<uint2*>(a.out + rowoff + d0) = pack_bf16x4(y0, y1, y2, y3);
     }
+}
+
+// y = bf16_rne(ypart + sig(z_gdn[h]) o_gdn): 8 elements per thread (two
+// 16-byte fp32 loads, one 16-byte bf16 load and store).
+__global__ __launch_bounds__(256) void hlta_combine_kernel(const float* __restrict__ ypart,
+                                                           const uint16_t* __restrict__ o_gdn,
+                                                           const float* __restrict__ gates,
+                                                           uint16_t* __restrict__ out, long n8, int H) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int h = (int)((i / (WD / 8)) % H);
+  const float gg = 1.f / (1.f + __expf(-gates[2 * H + h]));
+  const float4 a = reinterpret_cast<const float4*>(ypart)[2 * i];
+  const float4 b = reinterpret_cast<const float4*>(ypart)[2 * i + 1];
+  const uint4 og = reinterpret_cast<const uint4*>(o_gdn)[i];
+  const uint2 lo = pack_bf16x4(a.x + gg * bf16_to_f32(og.x & 0xFFFFu), a.y + gg * bf16_to_f32(og.x >> 16),
+                               a.z + gg * bf16_to_f32(og.y & 0xFFFFu), a.w + gg * bf16_to_f32(og.y >> 16));
+  const uint2 hi = pack_bf16x4(b.x + gg * bf16_to_f32(og.z & 0xFFFFu), b.y + gg * bf16_to_f32(og.z >> 16),
+                               b.z + gg * bf16_to_f32(og.w & 0xFFFFu), b.w + gg * bf16_to_f32(og.w >> 16));
+  reinterpret_cast<uint4*>(out)[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+hipError_t launch_hlta_combine(const float* ypart, const uint16_t* o_gdn, const float* gates,
+                               uint16_t* out, int B, int T, int H, hipStream_t stream) {
+  const long n8 = (long)B * T * H * WD / 8;
+  if (n8 == 0) return hipSuccess;
+  const long nb = (n8 + 255) / 256;
+  if (nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hlta_combine_kernel<<<(unsigned)nb, 256, 0, stream>>>(ypart, o_gdn, gates, out, n8, H);
+  return hipGetLastError();
+}
+
+long window_workgroups(int B, int T, int H, int L) {
+  if (L <= 0) return 0;
+  return (long)B * H * ((T + L - 1) / L) * ((L + BQ - 1) / BQ);
 }
 
 hipError_t launch_window(const WinArgs& args_in, int qf, bool hybrid, hipStream_t stream) {
