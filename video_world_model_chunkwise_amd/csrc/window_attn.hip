@@ -301,9 +301,9 @@ __device__ __forceinline__ void win_issue(const WinLoads<QF>& ld, const WinBuf& 
 
 // One key block of a branch: scores from buffer cb, online softmax, O update.
 // The lane's query sees the keys at group positions [hi - wl + 1, hi].
-template <int QF>
+template <int QF, bool ALIGN>
 __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
-                                          bool full, const bf16x8 (&qf)[8],
+                                          int size, float ks, bool full, const bf16x8 (&qf)[8],
                                           const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
                                           float& l_run) {
   constexpr bool FP8 = QF != QF_BF16;
@@ -345,8 +345,15 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
       for (int kt = 0; kt < 2; ++kt)
         S[kt] = QF == QF_FP4 ? mfma32x32x64_fp4(ka[kt][s], q8f[s], S[kt]) : mfma32x32x64_fp8(ka[kt][s], q8f[s], S[kt]);
   }
-  // ---- key scales, mask, block maximum (before the positive factor cq)
-  if (FP8) {
+  // ---- key scales, mask, block maximum (before the positive factor cq).
+  //      ALIGN: the block lies in one 64-token block of the call, so its keys
+  //      share one scale ks, folded into cq below.
+  const float cq = ALIGN ? qc.cq * ks : qc.cq;
+  if (ALIGN) {
+    __builtin_amdgcn_sched_group_barrier(0x100, QF == QF_FP4 ? 4 : 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+  }
+  if (FP8 && !ALIGN) {
     float4 s4[2][4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -368,20 +375,23 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   }
   if (!full) {
-    // valid iff hi - wl < pk <= hi, i.e. (unsigned)(hi - pk) < wl
+    // valid iff hi - wl < pk <= hi, i.e. (unsigned)(hi - pk) < wl, and (ALIGN)
+    // the key lies inside the block's size
     const int base = hi - pb;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)wl) S[kt][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int k = key_of(kt, r, qc.g);
+        if ((unsigned)(base - k) >= (unsigned)wl || (ALIGN && k >= size)) S[kt][r] = -INFINITY;
+      }
   }
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-  mx = max_with_partner(mx) * qc.cq;
+  mx = max_with_partner(mx) * cq;
   if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
     const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -401,7 +411,7 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
   for (int kt = 0; kt < 2; ++kt) {
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], qc.cq, -m_run));
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], cq, -m_run));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       P[kt][j] = to_bf16x8(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3], p[8 * j + 4],
@@ -448,8 +458,26 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
                                            const bf16x8 (&qf)[8], const i32x8 (&q8f)[2],
                                            WinLoads<QF>& ld, f32x16 (&O)[4], float& m_run,
                                            float& l_run) {
+  // Quantised keys in frames of at least one block: blocks never straddle a
+  // frame end or a 64-token block of the call, so each block's keys share one
+  // scale (one uniform load instead of the per-key scale reads).  Otherwise
+  // blocks are 64 consecutive group positions.
+  constexpr bool ALIGN = QF != QF_BF16 && !SHORTL;
   const int L = a.L;
+  const KeyMap& km = br.km;
+  const float* kscale = (br.own_k ? a.k_scales2 : a.k_scales) + ((size_t)qc.b * a.H + qc.h) * a.nblk;
+  // token of the call at (sub-frame n, row m), and the end row of the block starting there
+  auto tok_of = [&](int n, int m) { return (n * km.dil + km.res - km.frame_offset) * L + m; };
+  auto blk_end = [&](int n, int m) { return ALIGN ? min(m + BK - (tok_of(n, m) & (BK - 1)), L) : m + BK; };
   int n0 = br.p_lo / L, m0 = br.p_lo - (br.p_lo / L) * L;
+  int nb = br.nb;
+  if (ALIGN) {
+    nb = 0;
+    for (int n = n0, m = m0; n * L + m <= br.p_hi; ++nb) {
+      const int e = blk_end(n, m);
+      if (e >= L) { ++n; m = 0; } else { m = e; }
+    }
+  }
   win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, br.p_lo, n0, m0);
   win_issue<QF>(ld, B0, qc.wave);
   win_wait_vmem();
@@ -461,36 +489,41 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   const int full_hi = min(br.pq0 + qc.mw_lo + br.fwd, br.p_last);
   const int need_lo = br.pq0 + qc.mw_lo - br.back;       // keys inside some window of the wave
   const int need_hi = min(br.pq0 + qc.mw_hi + br.fwd, br.p_last);
-  for (int jb = 0; jb < br.nb; jb += 2) {
+  for (int jb = 0; jb < nb; jb += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int jj = jb + half;
-      if (jj >= br.nb) break;
+      if (jj >= nb) break;
       const WinBuf& cb = half ? B1 : B0;
-      const WinBuf& nb = half ? B0 : B1;
-      const int pb = br.p_lo + BK * jj;
+      const WinBuf& nbuf = half ? B0 : B1;
+      const int pb = ALIGN ? n0 * L + m0 : br.p_lo + BK * jj;
+      const int e0 = blk_end(n0, m0);
+      const int size = ALIGN ? e0 - m0 : BK;
+      const float ks = ALIGN ? kscale[tok_of(n0, m0) / BK] : 1.f;
       // next block's (sub-frame, offset) and its loads
-      int n1 = n0, m1 = m0 + BK;
+      int n1 = n0, m1 = e0;
       while (m1 >= L) { m1 -= L; ++n1; }
-      if (jj + 1 < br.nb) {
+      if (jj + 1 < nb) {
         // inside one frame, unclamped, the next block's rows are this block's
         // rows 64 positions on
-        const bool step = !SHORTL && m0 + BK <= L && n1 == n0 && m1 + BK <= L && pb + 2 * BK - 1 <= br.p_hi;
+        const bool step = !SHORTL && size == BK && m0 + BK <= L && n1 == n0 && m1 + BK <= L &&
+                          (!ALIGN || blk_end(n1, m1) - m1 == BK) && pb + 2 * BK - 1 <= br.p_hi;
         if (step) {
 #pragma unroll
           for (int j = 0; j < WinGeom<QF>::NJ; ++j) ld.src[j] += ld.inc[j];
         } else {
-          win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, pb + BK, n1, m1);
+          win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1 * L + m1, n1, m1);
         }
-        win_issue<QF>(ld, nb, qc.wave);
+        win_issue<QF>(ld, nbuf, qc.wave);
       }
-      const bool full = pb >= full_lo && pb + BK - 1 <= full_hi;
+      const bool full = size == BK && pb >= full_lo && pb + BK - 1 <= full_hi;
       // a wave whose rows all lie past the frame's end (the last, partial
       // query tile), or whose windows all miss this block, only loads its
       // share of the block and keeps the barriers: a block masked for every
       // lane adds nothing to O, l or the running maximum
-      const bool touch = pb + BK - 1 >= need_lo && pb <= need_hi;
-      if (qc.active && touch) win_block<QF>(cb, qc, hi, wl, pb, full, qf, q8f, O, m_run, l_run);
+      const bool touch = pb + size - 1 >= need_lo && pb <= need_hi;
+      if (qc.active && touch)
+        win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks, full, qf, q8f, O, m_run, l_run);
       win_wait_vmem();
       lds_barrier();
       n0 = n1;
