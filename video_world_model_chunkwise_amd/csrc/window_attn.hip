@@ -470,6 +470,10 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   auto tok_of = [&](int n, int m) { return (n * km.dil + km.res - km.frame_offset) * L + m; };
   auto blk_end = [&](int n, int m) { return ALIGN ? min(m + BK - (tok_of(n, m) & (BK - 1)), L) : m + BK; };
   int n0 = br.p_lo / L, m0 = br.p_lo - (br.p_lo / L) * L;
+  // current block: end row e0 and (ALIGN) token block tb0 with its key scale
+  int e0 = blk_end(n0, m0);
+  int tb0 = ALIGN ? tok_of(n0, m0) / BK : 0;
+  float ks0 = ALIGN ? kscale[tb0] : 1.f;
   int nb = br.nb;
   if (ALIGN) {
     nb = 0;
@@ -497,17 +501,33 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       const WinBuf& cb = half ? B1 : B0;
       const WinBuf& nbuf = half ? B0 : B1;
       const int pb = ALIGN ? n0 * L + m0 : br.p_lo + BK * jj;
-      const int e0 = blk_end(n0, m0);
       const int size = ALIGN ? e0 - m0 : BK;
-      const float ks = ALIGN ? kscale[tok_of(n0, m0) / BK] : 1.f;
-      // next block's (sub-frame, offset) and its loads
-      int n1 = n0, m1 = e0;
-      while (m1 >= L) { m1 -= L; ++n1; }
-      if (jj + 1 < nb) {
+      // next block's (sub-frame, offset, end, token block) and its loads;
+      // inside a frame an aligned block starts at the current end with the
+      // next token block
+      int n1 = n0, m1 = e0, e1, tb1 = tb0;
+      if (ALIGN) {
+        if (e0 < L) {
+          e1 = min(e0 + BK, L);
+          tb1 = tb0 + 1;
+        } else {
+          n1 = n0 + 1;
+          m1 = 0;
+          const int t = tok_of(n1, 0);
+          e1 = min(BK - (t & (BK - 1)), L);
+          tb1 = t / BK;
+        }
+      } else {
+        while (m1 >= L) { m1 -= L; ++n1; }
+        e1 = m1 + BK;
+      }
+      const bool more = jj + 1 < nb;
+      const float ks1 = ALIGN && more ? kscale[tb1] : 1.f;
+      if (more) {
         // inside one frame, unclamped, the next block's rows are this block's
         // rows 64 positions on
         const bool step = !SHORTL && size == BK && m0 + BK <= L && n1 == n0 && m1 + BK <= L &&
-                          (!ALIGN || blk_end(n1, m1) - m1 == BK) && pb + 2 * BK - 1 <= br.p_hi;
+                          e1 - m1 == BK && pb + 2 * BK - 1 <= br.p_hi;
         if (step) {
 #pragma unroll
           for (int j = 0; j < WinGeom<QF>::NJ; ++j) ld.src[j] += ld.inc[j];
@@ -523,11 +543,14 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       // lane adds nothing to O, l or the running maximum
       const bool touch = pb + size - 1 >= need_lo && pb <= need_hi;
       if (qc.active && touch)
-        win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks, full, qf, q8f, O, m_run, l_run);
+        win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks0, full, qf, q8f, O, m_run, l_run);
       win_wait_vmem();
       lds_barrier();
       n0 = n1;
       m0 = m1;
+      e0 = e1;
+      tb0 = tb1;
+      ks0 = ks1;
     }
   }
 }
