@@ -375,16 +375,20 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
   }
   if (!full) {
-    // valid iff hi - wl < pk <= hi, i.e. (unsigned)(hi - pk) < wl, and (ALIGN)
-    // the key lies inside the block's size
-    const int base = hi - pb;
+    // valid iff hi - wl < pk <= hi, i.e. (unsigned)(hi - pk) < wl; with ALIGN
+    // also k < size, folded into the band: its top becomes min(hi - pb, size - 1)
+    // and its length shrinks by as much (never below zero)
+    int base = hi - pb, len = wl;
+    if (ALIGN) {
+      const int top = min(base, size - 1);
+      len = max(wl - (base - top), 0);
+      base = top;
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k = key_of(kt, r, qc.g);
-        if ((unsigned)(base - k) >= (unsigned)wl || (ALIGN && k >= size)) S[kt][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)len) S[kt][r] = -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
