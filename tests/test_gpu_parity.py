@@ -188,6 +188,36 @@ def test_window_partial_last_frame():
                       f"partial frame dil={dl}")
 
 
+# E4M3 Q/K: key blocks follow frame ends and the call's 64-token blocks
+# (frames of at least 64 tokens), or 64 group positions with per-key scales
+# (shorter frames); frame offsets, frame lengths that 64 does not divide, a
+# partial last frame and short frames move those boundaries around
+FP8_WIN_CASES = WIN_CASES + [(1, 40, 24, 2, 50, 6, 0), (1, 12, 70, 2, 130, 4, 5)]
+
+
+def _fp8_branch_check(B, T, L, H, w, dil, fo, seed):
+    inp = make_custom(B, T, H, 128, "bf16", seed=seed)
+    dv = inputs_to_dev(inp)
+    q8, qs = K.kairos_fp8_quantize(dv["q"])
+    k8, ks = K.kairos_fp8_quantize(dv["k"])
+    _, _, qh = oracle.fp8_quantize_blocks(inp["q"])
+    _, _, kh = oracle.fp8_quantize_blocks(inp["k"])
+    for dl in sorted({1, dil}):
+        out = K.kairos_window_fwd(q8, k8, dv["v"], L, w, dl, frame_offset=fo, q_scales=qs, k_scales=ks)
+        torch.cuda.synchronize()
+        ref = oracle.windowed_attention(qh, kh, inp["v"], L, w, dl, fo)
+        _assert_close(host(out), ref, f"fp8 window T={T} L={L} dil={dl} fo={fo}")
+
+
+@pytest.mark.parametrize("B,F,L,H,w,dil,fo", FP8_WIN_CASES)
+def test_window_single_branch_fp8(B, F, L, H, w, dil, fo):
+    _fp8_branch_check(B, F * L, L, H, w, dil, fo, F * L + w + 1)
+
+
+def test_window_partial_last_frame_fp8():
+    _fp8_branch_check(1, 4 * 100 + 37, 100, 2, 120, 2, 0, 78)
+
+
 @pytest.mark.parametrize("B,F,L,H,w,dil,fo", WIN_CASES[:3])
 def test_hlta_small(B, F, L, H, w, dil, fo):
     T = F * L
