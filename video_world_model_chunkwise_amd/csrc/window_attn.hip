@@ -98,14 +98,18 @@ __device__ __forceinline__ void win_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0
 // 256 + 32), V rows (256 + 32 bytes), fp32 key scales (E4M3 only).  A block
 // of U 16-byte units per row is U loads of 64 lanes (lane l of load m fills
 // unit 64 m + l).
-template <int QF>
+template <int QF, bool SHORTL>
 struct WinGeom {
   static constexpr bool FP8 = QF != QF_BF16;                  // block-quantised codes + key scales
   static constexpr int KU = QF == QF_FP4 ? K4ST / 16 : QF == QF_FP8 ? K8ST / 16 : KST * 2 / 16;   // units per K row (4 / 8 / 18)
   static constexpr int VU = VST / 16;                         // units per V row (16)
   static constexpr int KBYTES = BK * KU * 16;
   static constexpr int VBYTES = BK * VU * 16;
-  static constexpr int NLOAD = KU + VU + (FP8 ? 1 : 0);       // loads per block (all waves)
+  // per-key scales travel with the block only where blocks may straddle a
+  // quantisation block (frames shorter than a block); otherwise a block has
+  // one scale, read directly
+  static constexpr bool SCL = FP8 && SHORTL;
+  static constexpr int NLOAD = KU + VU + (SCL ? 1 : 0);       // loads per block (all waves)
   static constexpr int NJ = (NLOAD + 3) / 4;                  // loads per wave
 };
 
@@ -201,17 +205,17 @@ struct WinBuf {
 // This wave's share of a block's loads: entry j is load e = wave + 4 j of
 // the block (K loads, then V loads, then the E4M3 scales); per lane the key
 // row and byte offset inside the row, and the source address.
-template <int QF>
+template <int QF, bool SHORTL>
 struct WinLoads {
-  const uint8_t* src[WinGeom<QF>::NJ];
-  int row[WinGeom<QF>::NJ];
-  int col[WinGeom<QF>::NJ];
-  uint32_t inc[WinGeom<QF>::NJ];   // source step of a block inside one frame (64 rows)
+  const uint8_t* src[WinGeom<QF, SHORTL>::NJ];
+  int row[WinGeom<QF, SHORTL>::NJ];
+  int col[WinGeom<QF, SHORTL>::NJ];
+  uint32_t inc[WinGeom<QF, SHORTL>::NJ];   // source step of a block inside one frame (64 rows)
 };
 
-template <int QF>
-__device__ __forceinline__ void win_load_setup(WinLoads<QF>& ld, int wave, int H) {
-  using G = WinGeom<QF>;
+template <int QF, bool SHORTL>
+__device__ __forceinline__ void win_load_setup(WinLoads<QF, SHORTL>& ld, int wave, int H) {
+  using G = WinGeom<QF, SHORTL>;
   const int lane = threadIdx.x % 64;
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
@@ -240,9 +244,9 @@ __device__ __forceinline__ void win_load_setup(WinLoads<QF>& ld, int wave, int H
 // m0): positions past p_hi clamp to p_hi (masked out; clamping keeps loads in
 // bounds and values finite).
 template <int QF, bool SHORTL>
-__device__ __forceinline__ void win_block_addrs(WinLoads<QF>& ld, const WinArgs& a, const BranchRange& br,
+__device__ __forceinline__ void win_block_addrs(WinLoads<QF, SHORTL>& ld, const WinArgs& a, const BranchRange& br,
                                                 int b, int h, int wave, int pb, int n0, int m0) {
-  using G = WinGeom<QF>;
+  using G = WinGeom<QF, SHORTL>;
   constexpr int KROW = qk_row_bytes(QF);
   const KeyMap& km = br.km;
   const int p_hi = br.p_hi;
@@ -287,9 +291,9 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<QF>& ld, const WinArgs&
   }
 }
 
-template <int QF>
-__device__ __forceinline__ void win_issue(const WinLoads<QF>& ld, const WinBuf& bf, int wave) {
-  using G = WinGeom<QF>;
+template <int QF, bool SHORTL>
+__device__ __forceinline__ void win_issue(const WinLoads<QF, SHORTL>& ld, const WinBuf& bf, int wave) {
+  using G = WinGeom<QF, SHORTL>;
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
     const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
@@ -460,7 +464,7 @@ template <int QF, bool SHORTL>
 __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, const WinBuf& B1,
                                            const BranchRange& br, const QueryCtx& qc,
                                            const bf16x8 (&qf)[8], const i32x8 (&q8f)[2],
-                                           WinLoads<QF>& ld, f32x16 (&O)[4], float& m_run,
+                                           WinLoads<QF, SHORTL>& ld, f32x16 (&O)[4], float& m_run,
                                            float& l_run) {
   // Quantised keys in frames of at least one block: blocks never straddle a
   // frame end or a 64-token block of the call, so each block's keys share one
@@ -487,7 +491,7 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
     }
   }
   win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, br.p_lo, n0, m0);
-  win_issue<QF>(ld, B0, qc.wave);
+  win_issue<QF, SHORTL>(ld, B0, qc.wave);
   win_wait_vmem();
   lds_barrier();
   const int pq = br.pq0 + qc.mq;                         // this lane's query position
@@ -534,11 +538,11 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
                           e1 - m1 == BK && pb + 2 * BK - 1 <= br.p_hi;
         if (step) {
 #pragma unroll
-          for (int j = 0; j < WinGeom<QF>::NJ; ++j) ld.src[j] += ld.inc[j];
+          for (int j = 0; j < WinGeom<QF, SHORTL>::NJ; ++j) ld.src[j] += ld.inc[j];
         } else {
           win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1 * L + m1, n1, m1);
         }
-        win_issue<QF>(ld, nbuf, qc.wave);
+        win_issue<QF, SHORTL>(ld, nbuf, qc.wave);
       }
       const bool full = size == BK && pb >= full_lo && pb + BK - 1 <= full_hi;
       // a wave whose rows all lie past the frame's end (the last, partial
@@ -561,11 +565,11 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
 
 template <int QF, bool HYBRID, bool SHORTL>
 __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
-  using G = WinGeom<QF>;
+  using G = WinGeom<QF, SHORTL>;
   constexpr bool FP8 = G::FP8;
   __shared__ __attribute__((aligned(16))) uint8_t Kb0[G::KBYTES], Kb1[G::KBYTES];
   __shared__ __attribute__((aligned(16))) uint16_t Vb0[G::VBYTES / 2], Vb1[G::VBYTES / 2];
-  __shared__ __attribute__((aligned(16))) float sk0[BK], sk1[BK];
+  __shared__ __attribute__((aligned(16))) float sk0[G::SCL ? BK : 1], sk1[G::SCL ? BK : 1];
   const WinBuf B0{Kb0, Vb0, sk0};
   const WinBuf B1{Kb1, Vb1, sk1};
   const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -620,8 +624,8 @@ __global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
   }
   const int b = qc.b, h = qc.h, g = qc.g;
 
-  WinLoads<QF> ld;
-  win_load_setup<QF>(ld, wave, a.H);
+  WinLoads<QF, SHORTL> ld;
+  win_load_setup<QF, SHORTL>(ld, wave, a.H);
 
   // ---- Q operand registers (B operand of S^T = K Q^T) of a branch
   bf16x8 qf[8];
