@@ -208,35 +208,37 @@ struct WinBuf {
 template <int QF, bool SHORTL>
 struct WinLoads {
   const uint8_t* src[WinGeom<QF, SHORTL>::NJ];
-  int row[WinGeom<QF, SHORTL>::NJ];
-  int col[WinGeom<QF, SHORTL>::NJ];
   uint32_t inc[WinGeom<QF, SHORTL>::NJ];   // source step of a block inside one frame (64 rows)
 };
+
+// Key row and byte offset inside the row of this lane's load j (computed
+// where the addresses are rebuilt, so they hold no registers in between).
+template <int QF, bool SHORTL>
+__device__ __forceinline__ void slot_rowcol(int j, int wave, int& row, int& col) {
+  using G = WinGeom<QF, SHORTL>;
+  const int lane = threadIdx.x % 64;
+  const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
+  int U, upr;
+  if (e < G::KU) { U = 64 * e + lane; upr = G::KU; }
+  else if (e < G::KU + G::VU) { U = 64 * (e - G::KU) + lane; upr = G::VU; }
+  else { U = lane; upr = 1; }                      // scales: one per key
+  row = U / upr;
+  const int u = U % upr;                           // LDS slot of the row
+  if (e < G::KU)
+    col = QF == QF_FP4 ? (u ^ k4_swz(row)) * 16
+        : QF == QF_FP8 ? (u ^ k8_swz(row)) * 16 : (u % 16) * 16;   // bf16: padding copies a unit
+  else if (e < G::KU + G::VU) col = (u ^ v_swz(row)) * 16;
+  else col = 0;
+}
 
 template <int QF, bool SHORTL>
 __device__ __forceinline__ void win_load_setup(WinLoads<QF, SHORTL>& ld, int wave, int H) {
   using G = WinGeom<QF, SHORTL>;
-  const int lane = threadIdx.x % 64;
 #pragma unroll
   for (int j = 0; j < G::NJ; ++j) {
     const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
     ld.inc[j] = e < G::KU ? (uint32_t)BK * H * qk_row_bytes(QF)
               : e < G::KU + G::VU ? (uint32_t)BK * H * WD * 2 : 4u;    // scales: next 64-token block
-  }
-#pragma unroll
-  for (int j = 0; j < G::NJ; ++j) {
-    const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
-    int U, upr;
-    if (e < G::KU) { U = 64 * e + lane; upr = G::KU; }
-    else if (e < G::KU + G::VU) { U = 64 * (e - G::KU) + lane; upr = G::VU; }
-    else { U = lane; upr = 1; }                      // scales: one per key
-    ld.row[j] = U / upr;
-    const int u = U % upr;                           // LDS slot of the row
-    if (e < G::KU)
-      ld.col[j] = QF == QF_FP4 ? (u ^ k4_swz(ld.row[j])) * 16
-                : QF == QF_FP8 ? (u ^ k8_swz(ld.row[j])) * 16 : (u % 16) * 16;   // bf16: padding copies a unit
-    else if (e < G::KU + G::VU) ld.col[j] = (u ^ v_swz(ld.row[j])) * 16;
-    else ld.col[j] = 0;
   }
 }
 
@@ -271,17 +273,19 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<QF, SHORTL>& ld, const 
   for (int j = 0; j < G::NJ; ++j) {
     const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
     if (e >= G::NLOAD) continue;
-    const int d = min(pb + ld.row[j], p_hi) - pb;
+    int row, col;
+    slot_rowcol<QF, SHORTL>(j, wave, row, col);
+    const int d = min(pb + row, p_hi) - pb;
     const int m = m0 + d;
     int n, mm;
     if (SHORTL) { n = n0 + m / L; mm = m - (m / L) * L; }
     else { n = n0 + (m >= L ? 1 : 0); mm = m >= L ? m - L : m; }
     if (e < G::KU) {
       const uint8_t* base = SHORTL ? frame_base(km, kx, kring, KROW, b, h, a.T, a.H, n) : (n == n0 ? k0 : k1);
-      ld.src[j] = base + (size_t)mm * rs_k + ld.col[j];
+      ld.src[j] = base + (size_t)mm * rs_k + col;
     } else if (e < G::KU + G::VU) {
       const uint8_t* base = SHORTL ? frame_base(km, vx, vring, 2 * WD, b, h, a.T, a.H, n) : (n == n0 ? v0 : v1);
-      ld.src[j] = base + (size_t)mm * rs_v + ld.col[j];
+      ld.src[j] = base + (size_t)mm * rs_v + col;
     } else {
       // E4M3 calls have no ring: rows are tokens of the call
       const int tok = (n * km.dil + km.res - km.frame_offset) * L + mm;
@@ -563,8 +567,15 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   }
 }
 
+// Workgroups per CU: three with 4-bit Q/K in block-aligned frames (its
+// operands are half as wide, so it fits 168 VGPRs with few spills: 14.27 vs
+// 15.34 ms at two); two otherwise (E4M3 at three spills about 30 registers
+// and runs slower; short frames keep per-key scales in registers).
+template <int QF, bool SHORTL>
+constexpr int win_wgs_per_cu() { return QF == QF_FP4 && !SHORTL ? 3 : 2; }
+
 template <int QF, bool HYBRID, bool SHORTL>
-__global__ __launch_bounds__(256, 2) void win_attn_kernel(WinArgs a) {
+__global__ __launch_bounds__(256, (win_wgs_per_cu<QF, SHORTL>())) void win_attn_kernel(WinArgs a) {
   using G = WinGeom<QF, SHORTL>;
   constexpr bool FP8 = G::FP8;
   __shared__ __attribute__((aligned(16))) uint8_t Kb0[G::KBYTES], Kb1[G::KBYTES];
