@@ -19,17 +19,19 @@
 // Work decomposition: one workgroup (4 waves) per (batch, head, frame,
 // 128-query tile); query tiles never straddle a frame, so each tile has one
 // contiguous key range per branch in group-position space.  Keys are walked
-// in blocks of 64 positions; each block's K and V rows (rows of one block may
-// come from two frames, or from the ring of a streamed rollout) go from
-// global memory straight into double-buffered LDS, token-major, each lane of
-// a load writing 16 bytes of one row.  Each wave owns 32 queries:
-// S^T = K Q^T on 32x32 matrix-core tiles with Q held in registers, an online
-// softmax in exp2 form (one query per lane, the row reduction is within the
-// lane plus one exchange with lane ^ 32), then O^T += V^T P^T with P taken
-// straight from the score registers and the V^T operands read with the
-// transposing LDS read.  With FP8 Q/K the score product uses the 32x32x64
-// E4M3 instruction and the per-64-token-block scales multiply the fp32
-// scores; P V stays bf16.
+// in blocks of at most 64 positions: with bf16 Q/K, 64 consecutive group
+// positions (rows of one block may come from two frames, or from the ring of
+// a streamed rollout); with quantised Q/K in frames of at least 64 tokens,
+// blocks stop at frame ends and at the call's 64-token quantisation blocks,
+// so each block has one key scale, applied together with the query's.  Each
+// block's K and V rows go from global memory straight into double-buffered
+// LDS, token-major, each lane of a load writing 16 bytes of one row.  Each
+// wave owns 32 queries: S^T = K Q^T on 32x32 matrix-core tiles with Q held
+// in registers, an online softmax in exp2 form (one query per lane, the row
+// reduction is within the lane plus one exchange with lane ^ 32), then
+// O^T += V^T P^T with P taken straight from the score registers and the V^T
+// operands read with the transposing LDS read.  With E4M3 (E2M1) Q/K the
+// score product uses the 32x32x64 f8f6f4 instruction; P V stays bf16.
 //
 // Key order inside a 32-key tile: the score tile's row r maps to key
 // pi(r) = 16 j + 8 g + 4 h + i for r = 16 j + 8 h + 4 g + i (bits g and h
@@ -41,8 +43,8 @@
 // to rescale away at the end, and the O rescale is skipped in almost every
 // block.
 //
-// Two workgroups share a CU (two waves per SIMD), so one wave's softmax
-// arithmetic overlaps the other's matrix products.  To fit, the hybrid
+// Two workgroups share a CU (two waves per SIMD; three with 4-bit Q/K), so
+// one wave's softmax arithmetic overlaps another's matrix products.  To fit, the hybrid
 // kernel parks the finished first branch (gated, normalised, fp32) in a
 // workspace row per query and adds it back in the epilogue.
 #include "common.hpp"
@@ -94,10 +96,11 @@ __device__ __forceinline__ void to_lds4(const void* g, void* lds) {
 }
 __device__ __forceinline__ void win_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
-// LDS layout of one key block: K rows (E4M3: 128 bytes + 16 padding; bf16:
-// 256 + 32), V rows (256 + 32 bytes), fp32 key scales (E4M3 only).  A block
-// of U 16-byte units per row is U loads of 64 lanes (lane l of load m fills
-// unit 64 m + l).
+// LDS layout of one key block: K rows (E4M3 128 bytes and E2M1 64 bytes,
+// 16-byte units XOR-swizzled; bf16 256 bytes + 32 padding), V rows (256
+// bytes, swizzled), and fp32 key scales for quantised keys in frames shorter
+// than a block.  A block of U 16-byte units per row is U loads of 64 lanes
+// (lane l of load m fills unit 64 m + l).
 template <int QF, bool SHORTL>
 struct WinGeom {
   static constexpr bool FP8 = QF != QF_BF16;                  // block-quantised codes + key scales
