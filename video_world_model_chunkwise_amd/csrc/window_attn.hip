@@ -212,6 +212,11 @@ template <int QF, bool SHORTL>
 struct WinLoads {
   const uint8_t* src[WinGeom<QF, SHORTL>::NJ];
   uint32_t inc[WinGeom<QF, SHORTL>::NJ];   // source step of a block inside one frame (64 rows)
+  // blocks inside one frame (aligned quantised blocks): wave-uniform address
+  // of the block's first K and V rows and per-lane offsets from them
+  const uint8_t* kb;
+  const uint8_t* vb;
+  uint32_t off[WinGeom<QF, SHORTL>::NJ];
 };
 
 // Key row and byte offset inside the row of this lane's load j (computed
@@ -295,6 +300,44 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<QF, SHORTL>& ld, const 
       const float* ksc = br.own_k ? a.k_scales2 : a.k_scales;
       ld.src[j] = reinterpret_cast<const uint8_t*>(ksc + ((size_t)b * a.H + h) * a.nblk + tok / 64);
     }
+  }
+}
+
+// Addresses of an aligned block (inside sub-frame n0, from row m0): rows past
+// the block's last valid row dmax repeat it (masked out), so every row stays
+// inside the frame and the call.
+template <int QF, bool SHORTL>
+__device__ __forceinline__ void win_block_addrs_al(WinLoads<QF, SHORTL>& ld, const WinArgs& a,
+                                                   const BranchRange& br, int b, int h, int wave, int n0,
+                                                   int m0, int dmax) {
+  using G = WinGeom<QF, SHORTL>;
+  constexpr int KROW = qk_row_bytes(QF);
+  const KeyMap& km = br.km;
+  const uint8_t* kx = reinterpret_cast<const uint8_t*>(br.own_k ? a.k2 : a.k);
+  const uint8_t* kring = reinterpret_cast<const uint8_t*>(a.k_ring);
+  const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
+  const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
+  const uint32_t rs_k = (uint32_t)a.H * KROW, rs_v = (uint32_t)a.H * WD * 2;
+  ld.kb = frame_base(km, kx, kring, KROW, b, h, a.T, a.H, n0) + (size_t)m0 * rs_k;
+  ld.vb = frame_base(km, vx, vring, 2 * WD, b, h, a.T, a.H, n0) + (size_t)m0 * rs_v;
+#pragma unroll
+  for (int j = 0; j < G::NJ; ++j) {
+    const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
+    if (e >= G::NLOAD) continue;
+    int row, col;
+    slot_rowcol<QF, SHORTL>(j, wave, row, col);
+    ld.off[j] = (uint32_t)min(row, dmax) * (e < G::KU ? rs_k : rs_v) + (uint32_t)col;
+  }
+}
+
+template <int QF, bool SHORTL>
+__device__ __forceinline__ void win_issue_al(const WinLoads<QF, SHORTL>& ld, const WinBuf& bf, int wave) {
+  using G = WinGeom<QF, SHORTL>;
+#pragma unroll
+  for (int j = 0; j < G::NJ; ++j) {
+    const int e = (wave & 3) + 4 * j;   // wave < 4: lets the compiler fold the slot kinds
+    if (e < G::KU) to_lds16(ld.kb + ld.off[j], bf.K + 1024 * e);
+    else if (e < G::KU + G::VU) to_lds16(ld.vb + ld.off[j], reinterpret_cast<uint8_t*>(bf.V) + 1024 * (e - G::KU));
   }
 }
 
@@ -497,8 +540,15 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       if (e >= L) { ++n; m = 0; } else { m = e; }
     }
   }
-  win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, br.p_lo, n0, m0);
-  win_issue<QF, SHORTL>(ld, B0, qc.wave);
+  // last valid row of the current block (aligned blocks)
+  int dmax0 = ALIGN ? min(e0 - m0, br.p_hi - br.p_lo + 1) - 1 : 0;
+  if (ALIGN) {
+    win_block_addrs_al<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n0, m0, dmax0);
+    win_issue_al<QF, SHORTL>(ld, B0, qc.wave);
+  } else {
+    win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, br.p_lo, n0, m0);
+    win_issue<QF, SHORTL>(ld, B0, qc.wave);
+  }
   win_wait_vmem();
   lds_barrier();
   const int pq = br.pq0 + qc.mq;                         // this lane's query position
@@ -538,18 +588,30 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       }
       const bool more = jj + 1 < nb;
       const float ks1 = ALIGN && more ? kscale[tb1] : 1.f;
+      int dmax1 = 0;
       if (more) {
-        // inside one frame, unclamped, the next block's rows are this block's
-        // rows 64 positions on
-        const bool step = !SHORTL && size == BK && m0 + BK <= L && n1 == n0 && m1 + BK <= L &&
-                          e1 - m1 == BK && pb + 2 * BK - 1 <= br.p_hi;
-        if (step) {
-#pragma unroll
-          for (int j = 0; j < WinGeom<QF, SHORTL>::NJ; ++j) ld.src[j] += ld.inc[j];
+        if (ALIGN) {
+          // a full next block in the same frame is this block's rows 64 on
+          dmax1 = min(e1 - m1, br.p_hi - (n1 * L + m1) + 1) - 1;
+          if (dmax0 == BK - 1 && dmax1 == BK - 1 && n1 == n0) {
+            ld.kb += (size_t)BK * a.H * qk_row_bytes(QF);
+            ld.vb += (size_t)BK * a.H * WD * 2;
+          } else {
+            win_block_addrs_al<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1, m1, dmax1);
+          }
+          win_issue_al<QF, SHORTL>(ld, nbuf, qc.wave);
         } else {
-          win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1 * L + m1, n1, m1);
+          // inside one frame, unclamped, the next block's rows are this block's
+          // rows 64 positions on
+          const bool step = !SHORTL && m0 + BK <= L && n1 == n0 && m1 + BK <= L && pb + 2 * BK - 1 <= br.p_hi;
+          if (step) {
+#pragma unroll
+            for (int j = 0; j < WinGeom<QF, SHORTL>::NJ; ++j) ld.src[j] += ld.inc[j];
+          } else {
+            win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1 * L + m1, n1, m1);
+          }
+          win_issue<QF, SHORTL>(ld, nbuf, qc.wave);
         }
-        win_issue<QF, SHORTL>(ld, nbuf, qc.wave);
       }
       const bool full = size == BK && pb >= full_lo && pb + BK - 1 <= full_hi;
       // a wave whose rows all lie past the frame's end (the last, partial
@@ -566,6 +628,7 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       e0 = e1;
       tb0 = tb1;
       ks0 = ks1;
+      dmax0 = dmax1;
     }
   }
 }
