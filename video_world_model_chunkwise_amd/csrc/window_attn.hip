@@ -633,12 +633,13 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   }
 }
 
-// Workgroups per CU: three with 4-bit Q/K in block-aligned frames (its
-// operands are half as wide, so it fits 168 VGPRs with few spills: 14.27 vs
-// 15.34 ms at two); two otherwise (E4M3 at three spills about 30 registers
-// and runs slower; short frames keep per-key scales in registers).
+// Workgroups per CU: three with quantised Q/K in block-aligned frames (one
+// key scale per block and uniform load bases leave them near 168 VGPRs: a few
+// spilled registers, and 6.6% faster (E4M3) and 7% (E2M1) than at two); two
+// for bf16 Q/K and for frames shorter than a block (per-key scales, 64-bit
+// per-lane addresses).
 template <int QF, bool SHORTL>
-constexpr int win_wgs_per_cu() { return QF == QF_FP4 && !SHORTL ? 3 : 2; }
+constexpr int win_wgs_per_cu() { return QF != QF_BF16 && !SHORTL ? 3 : 2; }
 
 template <int QF, bool HYBRID, bool SHORTL>
 __global__ __launch_bounds__(256, (win_wgs_per_cu<QF, SHORTL>())) void win_attn_kernel(WinArgs a) {
