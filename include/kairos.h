@@ -92,7 +92,8 @@ typedef struct {
 } kairos_gdn_desc;
 
 /* Hybrid layer problem.  g describes q, k, v, alpha, beta, state (io must be
- * KAIROS_BF16, d == 128).  The sequence is T tokens of frames of L tokens
+ * KAIROS_BF16, d == 128; H <= 65536, since the window kernel addresses a key
+ * block's rows by 32-bit offsets).  The sequence is T tokens of frames of L tokens
  * (the last frame may be partial when ring_frames == 0).  window w >= 1 in
  * tokens; dilation >= 1.  frame_offset is the absolute index of the call's
  * first frame.  window_qk: KAIROS_BF16, or KAIROS_FP8_E4M3 / KAIROS_FP4_E2M1

@@ -120,6 +120,7 @@ def test_hlta_validation():
     assert _hlta_call(K.hlta_desc(**{**base, "d": 64})) == UNSUP
     assert _hlta_call(K.hlta_desc(**base, io=K.F32)) == DTYPE
     assert _hlta_call(K.hlta_desc(**{**base, "window": 0})) == SHAPE
+    assert _hlta_call(K.hlta_desc(**{**base, "H": 65537})) == SHAPE
     assert _hlta_call(K.hlta_desc(**{**base, "dilation": 0})) == SHAPE
     assert _hlta_call(K.hlta_desc(**base, frame_offset=-1)) == SHAPE
     # a ring needs whole frames and enough of them, and no fp8

@@ -57,6 +57,8 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
   if (d->g.dk != 128) return KAIROS_ERR_UNSUPPORTED;
   if (d->L < 1 || d->window < 1 || d->dilation < 1 || d->frame_offset < 0 || d->ring_frames < 0)
     return KAIROS_ERR_SHAPE;
+  // the window kernel addresses a key block's rows as 32-bit offsets (row x H x 256 bytes)
+  if (d->g.H > 65536) return KAIROS_ERR_SHAPE;
   if (d->window_kind != KAIROS_WINDOW_CAUSAL && d->window_kind != KAIROS_WINDOW_CENTERED)
     return KAIROS_ERR_SHAPE;
   if (d->window_kind == KAIROS_WINDOW_CENTERED && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
