@@ -77,6 +77,8 @@ __device__ __forceinline__ constexpr int k8_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ constexpr int k4_swz(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ constexpr int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 constexpr float RESCALE_SLACK = 8.f;
+// block sums above this send a block to the maximum and rescale path (2^20)
+constexpr float SPEC_LIMIT = 1048576.f;
 
 typedef short wshort4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void wlds_void;
@@ -353,16 +355,15 @@ __device__ __forceinline__ void win_issue(const WinLoads<QF, SHORTL>& ld, const 
   }
 }
 
-// One key block of a branch: scores from buffer cb, online softmax, O update.
-// The lane's query sees the keys at group positions [hi - wl + 1, hi].
+// Scores S^T of one key block from buffer cb (two 32-key tiles; lane: query
+// ql, key key_of(kt, r, g)), per-key scales applied unless ALIGN, and keys
+// outside the lane's window at -inf.  The lane's query sees the keys at group
+// positions [hi - wl + 1, hi].
 template <int QF, bool ALIGN>
-__device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
-                                          int size, float ks, bool full, const bf16x8 (&qf)[8],
-                                          const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
-                                          float& l_run) {
+__device__ __forceinline__ void win_scores(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
+                                           int size, bool full, const bf16x8 (&qf)[8],
+                                           const i32x8 (&q8f)[2], f32x16 (&S)[2]) {
   constexpr bool FP8 = QF != QF_BF16;
-  // ---- scores S^T (two 32-key tiles), lane: query ql, key key_of(kt, r, g)
-  f32x16 S[2];
   S[0] = f32x16{};
   S[1] = f32x16{};
   if (!FP8) {
@@ -399,10 +400,8 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
       for (int kt = 0; kt < 2; ++kt)
         S[kt] = QF == QF_FP4 ? mfma32x32x64_fp4(ka[kt][s], q8f[s], S[kt]) : mfma32x32x64_fp8(ka[kt][s], q8f[s], S[kt]);
   }
-  // ---- key scales, mask, block maximum (before the positive factor cq).
-  //      ALIGN: the block lies in one 64-token block of the call, so its keys
-  //      share one scale ks, folded into cq below.
-  const float cq = ALIGN ? qc.cq * ks : qc.cq;
+  // ---- per-key scales and mask.  ALIGN: the block lies in one 64-token block
+  //      of the call, so its keys share one scale, folded into cq by the caller.
   if (ALIGN) {
     __builtin_amdgcn_sched_group_barrier(0x100, QF == QF_FP4 ? 4 : 8, 1);
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
@@ -444,43 +443,80 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
       for (int r = 0; r < 16; ++r)
         if ((unsigned)(base - key_of(kt, r, qc.g)) >= (unsigned)len) S[kt][r] = -INFINITY;
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-  mx = max_with_partner(mx) * cq;
-  if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
-    const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-    m_run = m_new;
-  }
-  // ---- probabilities -> bf16 operands: registers 8j..8j+7 of a tile are keys
-  //      32 kt + 16 j + 8 g + 0..7.  The row sum adds the bf16-rounded
-  //      probabilities (the weights the P V product uses), two per instruction.
-  bf16x8 P[2][2];
+}
+
+// Probabilities exp2(S cq - m) as bf16 operands (registers 8j..8j+7 of a tile
+// are keys 32 kt + 16 j + 8 g + 0..7) and the lane's share of their sum, which
+// adds the bf16-rounded values (the weights the P V product uses), two per
+// instruction.
+__device__ __forceinline__ float win_probs(const f32x16 (&S)[2], float cq, float m, bf16x8 (&P)[2][2]) {
+  float l = 0.f;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], cq, -m_run));
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[kt][r], cq, -m));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       P[kt][j] = to_bf16x8(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3], p[8 * j + 4],
                            p[8 * j + 5], p[8 * j + 6], p[8 * j + 7]);
       const uint4 pw = __builtin_bit_cast(uint4, P[kt][j]);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones, l_run, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones, l, false);
     }
   }
+  return l;
+}
+
+// One key block of a branch: scores from buffer cb, online softmax, O update.
+// With spec, the probabilities are first formed against the running maximum
+// as it stands, without the block maximum: a lane whose block sum stays at or
+// below SPEC_LIMIT has every probability at or below it, which bounds O and l
+// as the lazy rescale does.  Only if some lane of the wave exceeds it (its
+// maximum rose by more than log2(SPEC_LIMIT) - 6, or the lane has seen no key
+// yet) are the scores formed again and the block takes the maximum and
+// rescale path; after that every lane's probabilities are at most
+// 2^RESCALE_SLACK, so one repeat suffices.  The first block a wave takes of a
+// branch goes to that path directly.
+template <int QF, bool ALIGN>
+__device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
+                                          int size, float ks, bool full, bool spec, const bf16x8 (&qf)[8],
+                                          const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
+                                          float& l_run) {
+  const float cq = ALIGN ? qc.cq * ks : qc.cq;
+  f32x16 S[2];
+  bf16x8 P[2][2];
+  float l_blk = 0.f;
+  bool redo = true;
+  if (spec) {
+    win_scores<QF, ALIGN>(cb, qc, hi, wl, pb, size, full, qf, q8f, S);
+    l_blk = win_probs(S, cq, m_run, P);
+    redo = __ballot(l_blk > SPEC_LIMIT) != 0;
+  }
+  if (redo) {
+    win_scores<QF, ALIGN>(cb, qc, hi, wl, pb, size, full, qf, q8f, S);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
+    mx = max_with_partner(mx) * cq;
+    if (__ballot(mx > m_run + RESCALE_SLACK) != 0) {
+      const float m_new = mx > m_run + RESCALE_SLACK ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    l_blk = win_probs(S, cq, m_run, P);
+  }
+  l_run += l_blk;
   // ---- O^T += V^T P^T   (lane: O^T[32dt + 8(r/4) + 4g + r%4][query ql]); the
   //      V^T operand of (kt, j, dt): features 32 dt + lane%32, keys
   //      32 kt + 16 j + 8 g + 0..7.  Products in the order (kt, j) outer, dt
@@ -558,6 +594,7 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   const int full_hi = min(br.pq0 + qc.mw_lo + br.fwd, br.p_last);
   const int need_lo = br.pq0 + qc.mw_lo - br.back;       // keys inside some window of the wave
   const int need_hi = min(br.pq0 + qc.mw_hi + br.fwd, br.p_last);
+  bool spec = false;                                     // a block of this branch taken
   for (int jb = 0; jb < nb; jb += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -619,8 +656,10 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       // share of the block and keeps the barriers: a block masked for every
       // lane adds nothing to O, l or the running maximum
       const bool touch = pb + size - 1 >= need_lo && pb <= need_hi;
-      if (qc.active && touch)
-        win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks0, full, qf, q8f, O, m_run, l_run);
+      if (qc.active && touch) {
+        win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks0, full, spec, qf, q8f, O, m_run, l_run);
+        spec = true;
+      }
       win_wait_vmem();
       lds_barrier();
       n0 = n1;
