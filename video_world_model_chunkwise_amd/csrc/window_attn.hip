@@ -41,7 +41,9 @@
 // The running maximum is only raised when a block's maximum exceeds it by
 // more than 8 (log2 units): probabilities then stay <= 2^8, which is exact
 // to rescale away at the end, and the O rescale is skipped in almost every
-// block.
+// block.  A block first forms its probabilities against the running maximum
+// as it stands and checks only their sum; the block maximum is taken (and
+// the block formed again) only when that sum exceeds 2^20.
 //
 // Two workgroups share a CU (two waves per SIMD; three with 4-bit Q/K), so
 // one wave's softmax arithmetic overlaps another's matrix products.  To fit, the hybrid
@@ -448,9 +450,9 @@ __device__ __forceinline__ void win_scores(const WinBuf& cb, const QueryCtx& qc,
 // Probabilities exp2(S cq - m) as bf16 operands (registers 8j..8j+7 of a tile
 // are keys 32 kt + 16 j + 8 g + 0..7) and the lane's share of their sum, which
 // adds the bf16-rounded values (the weights the P V product uses), two per
-// instruction.
+// instruction, in one partial sum per tile.
 __device__ __forceinline__ float win_probs(const f32x16 (&S)[2], float cq, float m, bf16x8 (&P)[2][2]) {
-  float l = 0.f;
+  float lk[2] = {0.f, 0.f};
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -462,13 +464,13 @@ __device__ __forceinline__ float win_probs(const f32x16 (&S)[2], float cq, float
       P[kt][j] = to_bf16x8(p[8 * j], p[8 * j + 1], p[8 * j + 2], p[8 * j + 3], p[8 * j + 4],
                            p[8 * j + 5], p[8 * j + 6], p[8 * j + 7]);
       const uint4 pw = __builtin_bit_cast(uint4, P[kt][j]);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones, l, false);
+      lk[kt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones, lk[kt], false);
+      lk[kt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones, lk[kt], false);
+      lk[kt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones, lk[kt], false);
+      lk[kt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones, lk[kt], false);
     }
   }
-  return l;
+  return lk[0] + lk[1];
 }
 
 // One key block of a branch: scores from buffer cb, online softmax, O update.
