@@ -263,17 +263,19 @@ def main():
     # the same stage on 4-bit (E2M1) Q/K, and the whole layer with 4-bit windows
     c4q = torch.empty((w.B, w.T, w.H, w.d // 2), dtype=torch.uint8, device=dev)
     c4k = torch.empty_like(c4q)
-    t_q4 = st.run("fp4_quant_q", lambda: K.kairos_fp4_quantize(d["q"], c4q, sq), reps)
-    K.kairos_fp4_quantize(d["k"], c4k, sk)
+    # scales of their own: the centred stage below reads the E4M3 scales
+    sq4, sk4 = torch.empty_like(sq), torch.empty_like(sk)
+    t_q4 = st.run("fp4_quant_q", lambda: K.kairos_fp4_quantize(d["q"], c4q, sq4), reps)
+    K.kairos_fp4_quantize(d["k"], c4k, sk4)
     t_win4 = st.run("window_hybrid_fp4", lambda: K.kairos_hlta_window_fwd(
-        c4q, c4k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
-        k_scales=sk, out=bufs["out"], workspace=yws), reps)
+        c4q, c4k, d["v"], o_gdn, d["gates"], w.L, w.window, w.dilation, q_scales=sq4,
+        k_scales=sk4, out=bufs["out"], workspace=yws), reps)
     desc4 = K.hlta_desc(w.B, w.T, w.H, w.d, w.L, w.window, w.dilation, window_qk=K.FP4_E2M1)
     ws4 = torch.empty(K.kairos_hlta_workspace_size(desc4), dtype=torch.uint8, device=dev)
     t_layer4 = st.run("layer_fp4", lambda: K.kairos_hlta_fwd(
         d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["gates"], w.L, w.window, w.dilation,
         window_qk=K.FP4_E2M1, out=bufs["out"], state_out=bufs["state"], workspace=ws4), reps)
-    del ws4, c4q, c4k
+    del ws4, c4q, c4k, sq4, sk4
     # the same stage with centred windows (Eq. 7 as printed) and the pages' DSWA dilation 6
     t_win_c = st.run("window_hybrid_centered_dil6", lambda: K.kairos_hlta_window_fwd(
         codes_q, codes_k, d["v"], o_gdn, d["gates"], w.L, w.window, 6, q_scales=sq,

@@ -218,6 +218,41 @@ def test_window_partial_last_frame_fp8():
     _fp8_branch_check(1, 4 * 100 + 37, 100, 2, 120, 2, 0, 78)
 
 
+@pytest.mark.parametrize("qf", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("gain", [64.0, 1024.0])
+def test_window_wide_scores(qf, gain):
+    """Queries scaled by a power of two so that scores spread over tens to
+    hundreds of log2 units: the running maximum keeps rising from block to
+    block, which sends blocks formed against the running maximum alone back
+    to the maximum and rescale path (and, past a few such blocks, stops
+    those attempts for the wave)."""
+    B, F, L, H, w, dil = 1, 6, 200, 2, 500, 2
+    T = F * L
+    print(f"wide scores {qf} gain={gain}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=int(gain) + 11)
+    from workloads import to_bf16_bits
+    inp["q"] = inp["q"] * np.float32(gain)                 # exact: gain is a power of two
+    inp["q_bits"] = to_bf16_bits(inp["q"])
+    dv = inputs_to_dev(inp)
+    for dl in (1, dil):
+        if qf == "bf16":
+            out = K.kairos_window_fwd(dv["q"], dv["k"], dv["v"], L, w, dl)
+            qh, kh = inp["q"], inp["k"]
+        elif qf == "fp8":
+            q8, qs = K.kairos_fp8_quantize(dv["q"])
+            k8, ks = K.kairos_fp8_quantize(dv["k"])
+            out = K.kairos_window_fwd(q8, k8, dv["v"], L, w, dl, q_scales=qs, k_scales=ks)
+            qh, kh = oracle.fp8_quantize_blocks(inp["q"])[2], oracle.fp8_quantize_blocks(inp["k"])[2]
+        else:
+            q4, qs = K.kairos_fp4_quantize(dv["q"])
+            k4, ks = K.kairos_fp4_quantize(dv["k"])
+            out = K.kairos_window_fwd(q4, k4, dv["v"], L, w, dl, q_scales=qs, k_scales=ks)
+            qh, kh = oracle.fp4_quantize_blocks(inp["q"])[2], oracle.fp4_quantize_blocks(inp["k"])[2]
+        torch.cuda.synchronize()
+        ref = oracle.windowed_attention(qh, kh, inp["v"], L, w, dl)
+        _assert_close(host(out), ref, f"wide scores {qf} gain={gain} dil={dl}")
+
+
 @pytest.mark.parametrize("B,F,L,H,w,dil,fo", WIN_CASES[:3])
 def test_hlta_small(B, F, L, H, w, dil, fo):
     T = F * L

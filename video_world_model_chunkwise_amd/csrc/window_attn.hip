@@ -41,9 +41,9 @@
 // The running maximum is only raised when a block's maximum exceeds it by
 // more than 8 (log2 units): probabilities then stay <= 2^8, which is exact
 // to rescale away at the end, and the O rescale is skipped in almost every
-// block.  A block first forms its probabilities against the running maximum
-// as it stands and checks only their sum; the block maximum is taken (and
-// the block formed again) only when that sum exceeds 2^20.
+// block.  Most blocks first form their probabilities against the running
+// maximum as it stands and check only their sum; the block maximum is taken
+// (and the block formed again) only when that sum exceeds 2^32.
 //
 // Two workgroups share a CU (two waves per SIMD; three with 4-bit Q/K), so
 // one wave's softmax arithmetic overlaps another's matrix products.  To fit, the hybrid
@@ -79,8 +79,11 @@ __device__ __forceinline__ constexpr int k8_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ constexpr int k4_swz(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ constexpr int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 constexpr float RESCALE_SLACK = 8.f;
-// block sums above this send a block to the maximum and rescale path (2^20)
-constexpr float SPEC_LIMIT = 1048576.f;
+// a lane's block sum above this (2^32) sends the block to the maximum and
+// rescale path; a wave stops forming blocks against the running maximum
+// alone after SPEC_TRIES such blocks in one branch
+constexpr float SPEC_LIMIT = 4294967296.f;
+constexpr int SPEC_TRIES = 4;
 
 typedef short wshort4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void wlds_void;
@@ -450,7 +453,7 @@ __device__ __forceinline__ void win_scores(const WinBuf& cb, const QueryCtx& qc,
 // Probabilities exp2(S cq - m) as bf16 operands (registers 8j..8j+7 of a tile
 // are keys 32 kt + 16 j + 8 g + 0..7) and the lane's share of their sum, which
 // adds the bf16-rounded values (the weights the P V product uses), two per
-// instruction, in one partial sum per tile.
+// instruction.
 __device__ __forceinline__ float win_probs(const f32x16 (&S)[2], float cq, float m, bf16x8 (&P)[2][2]) {
   float lk[2] = {0.f, 0.f};
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
@@ -481,10 +484,10 @@ __device__ __forceinline__ float win_probs(const f32x16 (&S)[2], float cq, float
 // maximum rose by more than log2(SPEC_LIMIT) - 6, or the lane has seen no key
 // yet) are the scores formed again and the block takes the maximum and
 // rescale path; after that every lane's probabilities are at most
-// 2^RESCALE_SLACK, so one repeat suffices.  The first block a wave takes of a
-// branch goes to that path directly.
+// 2^RESCALE_SLACK, so one repeat suffices.  Returns whether an attempt was
+// made and failed.
 template <int QF, bool ALIGN>
-__device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
+__device__ __forceinline__ bool win_block(const WinBuf& cb, const QueryCtx& qc, int hi, int wl, int pb,
                                           int size, float ks, bool full, bool spec, const bf16x8 (&qf)[8],
                                           const i32x8 (&q8f)[2], f32x16 (&O)[4], float& m_run,
                                           float& l_run) {
@@ -519,6 +522,7 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
     l_blk = win_probs(S, cq, m_run, P);
   }
   l_run += l_blk;
+  const bool failed = spec && redo;
   // ---- O^T += V^T P^T   (lane: O^T[32dt + 8(r/4) + 4g + r%4][query ql]); the
   //      V^T operand of (kt, j, dt): features 32 dt + lane%32, keys
   //      32 kt + 16 j + 8 g + 0..7.  Products in the order (kt, j) outer, dt
@@ -544,6 +548,7 @@ __device__ __forceinline__ void win_block(const WinBuf& cb, const QueryCtx& qc, 
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  return failed;
 }
 
 // One windowed branch over its key blocks: online softmax into O (unnormalised)
@@ -596,7 +601,13 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   const int full_hi = min(br.pq0 + qc.mw_lo + br.fwd, br.p_last);
   const int need_lo = br.pq0 + qc.mw_lo - br.back;       // keys inside some window of the wave
   const int need_hi = min(br.pq0 + qc.mw_hi + br.fwd, br.p_last);
-  bool spec = false;                                     // a block of this branch taken
+  // A block is formed against the running maximum alone only if every lane's
+  // window began before it (each lane has a key, hence a finite maximum), the
+  // wave's previous block did not fail such an attempt, and fewer than
+  // SPEC_TRIES attempts failed in this branch: with widely spread scores the
+  // maximum keeps rising, and a failed attempt costs most of a block.
+  bool spec = false;
+  int nfail = 0;
   for (int jb = 0; jb < nb; jb += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -659,8 +670,10 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       // lane adds nothing to O, l or the running maximum
       const bool touch = pb + size - 1 >= need_lo && pb <= need_hi;
       if (qc.active && touch) {
-        win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks0, full, spec, qf, q8f, O, m_run, l_run);
-        spec = true;
+        const bool failed = win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks0, full, spec && pb > full_lo,
+                                                 qf, q8f, O, m_run, l_run);
+        nfail += failed;
+        spec = !failed && nfail < SPEC_TRIES;
       }
       win_wait_vmem();
       lds_barrier();
