@@ -407,10 +407,6 @@ __device__ __forceinline__ void win_scores(const WinBuf& cb, const QueryCtx& qc,
   }
   // ---- per-key scales and mask.  ALIGN: the block lies in one 64-token block
   //      of the call, so its keys share one scale, folded into cq by the caller.
-  if (ALIGN) {
-    __builtin_amdgcn_sched_group_barrier(0x100, QF == QF_FP4 ? 4 : 8, 1);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-  }
   if (FP8 && !ALIGN) {
     float4 s4[2][4];
 #pragma unroll
