@@ -449,7 +449,7 @@ __device__ __forceinline__ void win_scores(const WinBuf& cb, const QueryCtx& qc,
 // Probabilities exp2(S cq - m) as bf16 operands (registers 8j..8j+7 of a tile
 // are keys 32 kt + 16 j + 8 g + 0..7) and the lane's share of their sum, which
 // adds the bf16-rounded values (the weights the P V product uses), two per
-// instruction.
+// instruction, into one partial sum per score tile.
 __device__ __forceinline__ float win_probs(const f32x16 (&S)[2], float cq, float m, bf16x8 (&P)[2][2]) {
   float lk[2] = {0.f, 0.f};
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
