@@ -281,6 +281,34 @@ def test_hlta_fp8_small():
     _assert_close(host(S), S_ref, "S fp8")
 
 
+@pytest.mark.parametrize("qf", ["bf16", "fp8"])
+def test_hlta_window_stage_wide_scores(qf):
+    """The two-branch window stage (both windowed branches, gates, and a given
+    GDN output, here zero) with queries scaled by 1024: scores spread over
+    hundreds of log2 units in both branches of one kernel."""
+    from workloads import to_bf16_bits
+    B, F, L, H, w, dil = 1, 6, 150, 2, 200, 4
+    T = F * L
+    print(f"wide-score window stage {qf}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=907)
+    inp["q"] = inp["q"] * np.float32(1024.0)               # exact: a power of two
+    inp["q_bits"] = to_bf16_bits(inp["q"])
+    dv = inputs_to_dev(inp)
+    o_gdn = torch.zeros_like(dv["v"])
+    ws = torch.empty(4 * B * T * H * 128, dtype=torch.uint8, device="cuda:0")
+    if qf == "bf16":
+        y = K.kairos_hlta_window_fwd(dv["q"], dv["k"], dv["v"], o_gdn, dv["gates"], L, w, dil, workspace=ws)
+    else:
+        q8, qs = K.kairos_fp8_quantize(dv["q"])
+        k8, ks = K.kairos_fp8_quantize(dv["k"])
+        y = K.kairos_hlta_window_fwd(q8, k8, dv["v"], o_gdn, dv["gates"], L, w, dil, q_scales=qs,
+                                     k_scales=ks, workspace=ws)
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.hlta_rows(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"], L, w,
+                                dil, np.arange(T), window_qk=qf, o_gdn=np.zeros_like(inp["v"]))
+    _assert_close(host(y), y_ref, f"wide-score window stage {qf}")
+
+
 def test_streaming_equals_full_run():
     """Recurrent state passing: frames fed one call at a time with the GDN state
     carried and a key/value ring equal one full-length oracle run."""
