@@ -12,7 +12,8 @@
  *   Sec. 2.2.2, Eq. 8                 dilated SWA on the frame-rearranged sequence
  *   Sec. 2.2.2, "Long-Horizon Generation"  recurrent state passing, constant memory per step
  * and the project page "Kairos: A Native World Model Stack for Physical AI"
- * (TL;DR, Q3: FP8 attention quantisation, tiled GatedDeltaNet).
+ * (Sec. 2, Q2: FP8/INT4 attention quantisation and a tiled GatedDeltaNet;
+ * Sec. 7: the tiled GatedDeltaNet streams its inputs to hide DRAM latency).
  *
  * Conventions shared by every entry point
  * --------------------------------------
@@ -32,11 +33,13 @@
  * The softmax scale is 1/sqrt(d).
  *
  * Ownership and streams: the caller owns every buffer (device memory unless
- * stated).  Entry points allocate nothing: scratch space comes from the
- * caller's workspace, sized by the *_workspace_size calls.  Work is enqueued
- * on `stream` (a hipStream_t; NULL is the null stream) and the call returns
- * without synchronising; nothing is copied between host and device.  The
- * current HIP device is used.  Calls keep no global state, so they are
+ * stated).  Compute entry points allocate nothing: scratch space comes from
+ * the caller's workspace, sized by the *_workspace_size calls.  Work is
+ * enqueued on `stream` (a hipStream_t; NULL is the null stream) and the call
+ * returns without synchronising; nothing is copied between host and device.
+ * The current HIP device is used.  Calls keep no global state: the only
+ * state a call touches is what the caller passes in (buffers, and for the
+ * layer call an optional kairos_context the caller created), so calls are
  * reentrant; calls that share output buffers on one stream are ordered by it.
  *
  * Errors: all arguments are validated on the host before anything is
@@ -173,6 +176,21 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
                       const void* v, const float* q_scales, const float* k_scales,
                       const void* k_ring, const void* v_ring, void* out, void* stream);
 
+/* Execution context of kairos_hlta_fwd, owned by the caller: a side stream
+ * of the device current at creation (default priority, non-blocking) and
+ * three events, with which a layer call runs part of its work beside the
+ * caller's stream (see kairos_hlta_fwd).  kairos_context_create allocates
+ * these host-side HIP objects (no device memory) and writes the handle to
+ * *ctx (NULL on failure: KAIROS_ERR_NULL for ctx == NULL, KAIROS_ERR_HIP when
+ * the runtime refuses).  kairos_context_destroy releases them (NULL is a
+ * no-op); work already enqueued on the side stream still completes.  A
+ * context may be shared by calls on several streams and host threads (an
+ * internal lock orders its event pairs); destroy it only when no call that
+ * uses it is running. */
+typedef struct kairos_context_t* kairos_context;
+int kairos_context_create(kairos_context* ctx);
+int kairos_context_destroy(kairos_context ctx);
+
 /* Hybrid layer forward: y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn
  * per head (Sec. 2.2, Fig. 5 pathways, run as parallel gated branches).
  *   gate_logits  [3][H] fp32 (device memory)
@@ -181,21 +199,24 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
  *                with the call's last min(R, F) frames
  *   out          [B][T][H][d] bf16; state_out as in kairos_gdn_fwd
  *   workspace    >= kairos_hlta_workspace_size bytes
- * Streams: everything is ordered on `stream`.  Part of the work may run on
- * a side stream the library creates on the device's first layer call and
- * keeps until the process ends: the windowed branches' operand pre-passes
- * (quantised Q/K, RoPE), or, when the window kernel and the GDN scan fit on
- * the device together (e.g. one streamed frame), the whole GDN branch.  The
- * side stream waits for an event recorded on `stream`, and `stream` waits
- * for it before anything that reads its results, so the call behaves as one
- * stream and can be captured into a graph (make one call on the device
- * before the first capture, so the side stream is not created during
- * capture).  Calls from several host threads are safe; their side work
- * shares the side stream. */
+ *   ctx          NULL, or a context of the current device (else
+ *                KAIROS_ERR_UNSUPPORTED)
+ * Streams: with ctx == NULL everything runs on `stream`.  With a context,
+ * part of the work runs on its side stream: the windowed branches' operand
+ * pre-passes (quantised Q/K, RoPE) beside the GDN scan, or, when the window
+ * kernel and the GDN scan fit on the device together (e.g. one streamed
+ * frame), the whole GDN branch beside the window kernel.  The side stream
+ * waits for an event recorded on `stream`, and `stream` waits for it before
+ * anything that reads its results, so the call behaves as one stream and can
+ * be captured into a graph.  While the side stream belongs to an open graph
+ * capture, a call on a stream outside that capture runs on `stream` alone
+ * (same results), so captures and eager calls on other threads can share a
+ * context. */
 int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, const float* gate_logits,
                     const float* state_in, void* k_ring, void* v_ring, void* out,
-                    float* state_out, void* workspace, size_t workspace_bytes, void* stream);
+                    float* state_out, void* workspace, size_t workspace_bytes,
+                    kairos_context ctx, void* stream);
 
 /* The windowed stage of kairos_hlta_fwd on its own: both windowed branches
  * and the gated combination with an already computed GDN branch output.
@@ -274,7 +295,7 @@ int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, v
                 float* scales, void* stream);
 
 /* 4-bit quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block), the
- * 4-bit attention quantisation of the project page (TL;DR / Q3) as OCP FP4
+ * INT4 attention quantisation of the project page (Sec. 2, Q2) as OCP FP4
  * E2M1 codes (the matrix instructions take 4-bit floating-point operands, not
  * 4-bit integers): s = amax / 6 (fp32; 1 when amax == 0), code = E2M1 of the
  * correctly rounded fp32 quotient x / s, round to nearest with ties to the
@@ -284,7 +305,10 @@ int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, v
 int kairos_fp4_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
                         int32_t H, int32_t d, void* stream);
 
-/* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block):
+/* FP8 E4M3 quantisation of x [B][T][H][d] bf16 per (b, h, 64-token block),
+ * the FP8 attention quantisation of the project page (Sec. 2, Q2: FP8/INT4
+ * attention quantisation in the deployment co-design; Sec. 1 TL;DR: FP8
+ * inference):
  * s = amax / 448 (fp32; 1 when amax == 0), code = E4M3(x / s) with an IEEE
  * fp32 division, round to nearest even, saturating at 448 (OCP E4M3: bias 7,
  * subnormals, no infinities).  codes [B][T][H][d] uint8, scales

@@ -37,10 +37,51 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert K.version() == 103
+    assert K.version() == 200
     assert K.status_string(0) == "ok"
     assert "align" in K.status_string(ALIGN)
     assert K.status_string(12345) == "unknown status"
+
+
+def _writable_symbols():
+    """Demangled names of the library's own writable data symbols (.data/.bss),
+    from nm; kernel launch handles (names with a parameter list) excluded."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-C", "--defined-only", K.lib_path], check=True, capture_output=True,
+                         text=True).stdout
+    names = []
+    for line in out.splitlines():
+        parts = line.split(maxsplit=2)
+        if len(parts) == 3 and parts[1] in "bBdD" and "(" not in parts[2]:
+            if parts[2].startswith(("kairos", "(anonymous namespace)")):
+                names.append(parts[2])
+    return names
+
+
+# the only file-scope state: the per-device device addresses of the no-alloc
+# entry point's scratch array (resolved once per device)
+ALLOWED_STATE = {"kairos::noalloc_scratch_ptr", "kairos::noalloc_scratch_mu"}
+
+
+def test_no_global_state():
+    """The library keeps no process-wide mutable state of its own: the layer
+    call's side stream and events live in a caller-created kairos_context."""
+    names = _writable_symbols()
+    assert set(names) <= ALLOWED_STATE, names
+
+
+@host_only
+def test_context_arguments():
+    L = K.lib()
+    assert L.kairos_context_create(None) == NULL
+    assert L.kairos_context_destroy(None) == OK
+    h = ctypes.c_void_p(1234)
+    st = L.kairos_context_create(ctypes.byref(h))     # no device here: the runtime refuses
+    assert st == -8 and not h.value
 
 
 def test_workspace_sizes():
@@ -93,6 +134,11 @@ def test_gdn_pointer_errors():
     nx = 64 * 2 * 128 * 4
     assert _gdn_call(d, out=0x10000 + nx // 2) == ALIAS          # out overlaps q
     assert _gdn_call(d, s_in=0x90000, s_out=0x90000 + 16) == ALIAS  # partial state overlap
+    # the chunk kernels' 32-bit row offsets: 63 * H * d * 2 + d * 2 < 2^32
+    assert K.kairos_gdn_workspace_size(K.gdn_desc(1, 64, 266304, 128)) > 0
+    with pytest.raises(K.KairosError) as e:
+        K.kairos_gdn_workspace_size(K.gdn_desc(1, 64, 266305, 128))
+    assert e.value.status == SHAPE
     db = K.gdn_desc(1, 64, 2, 128)
     assert _gdn_call(db) == WS                        # bf16 needs a workspace
     need = K.kairos_gdn_workspace_size(db)
@@ -108,7 +154,7 @@ def _hlta_call(desc, ws=None, nws=0, gates=6 * G, k_ring=None, v_ring=None, out=
     cv = lambda x: None if x is None else ctypes.c_void_p(x)
     return L.kairos_hlta_fwd(ctypes.byref(desc), cv(1 * G), cv(2 * G), cv(3 * G),
                              cv(4 * G), cv(5 * G), cv(gates), None, cv(k_ring), cv(v_ring),
-                             cv(out), None, cv(ws), nws, None)
+                             cv(out), None, cv(ws), nws, None, None)
 
 
 @host_only

@@ -93,12 +93,17 @@ def test_gdn_poisoned_buffers_and_determinism():
     _assert_same(res, ["o", "S"])
 
 
+@pytest.mark.parametrize("use_ctx", [False, True])
 @pytest.mark.parametrize("F,L,H,w,qk", [(6, 200, 2, 300, "bf16"), (6, 200, 2, 300, "fp8"),
                                          (8, 1024, 8, 1000, "bf16"), (8, 1024, 8, 1000, "fp8")])
-def test_layer_poisoned_buffers_and_determinism(F, L, H, w, qk):
+def test_layer_poisoned_buffers_and_determinism(F, L, H, w, qk, use_ctx):
+    """Single-stream calls, and with a context both of its schedules (the GDN
+    beside the window kernel for the small calls, the operand pre-passes
+    beside the scan for the larger ones)."""
     B, dil = 1, 4
     T = F * L
-    print(f"layer F{F} L{L} H{H} {qk}", flush=True)
+    print(f"layer F{F} L{L} H{H} {qk} ctx={use_ctx}", flush=True)
+    ctx = K.Context() if use_ctx else None
     dv = inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=600 + L + H))
     wq = K.FP8_E4M3 if qk == "fp8" else K.BF16
     nws = K.kairos_hlta_workspace_size(K.hlta_desc(B, T, H, 128, L, w, dil, window_qk=wq))
@@ -106,9 +111,12 @@ def test_layer_poisoned_buffers_and_determinism(F, L, H, w, qk):
     out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda:0")
     S = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
     res = _runs(lambda: K.kairos_hlta_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dv["gates"],
-                                          L, w, dil, window_qk=wq, out=out, state_out=S, workspace=ws),
+                                          L, w, dil, window_qk=wq, out=out, state_out=S, workspace=ws,
+                                          ctx=ctx),
                 [ws, out, S])
     _assert_same([r[1:] for r in res], ["y", "S"])
+    if ctx is not None:
+        ctx.close()
 
 
 def test_window_stage_poisoned_buffers_and_determinism():

@@ -17,7 +17,8 @@ symbols = (
     "kairos_status_string", "kairos_version", "kairos_gdn_workspace_size",
     "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
     "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
-    "kairos_gdn_prologue", "kairos_rope", "kairos_fp4_quantize",
+    "kairos_gdn_prologue", "kairos_rope", "kairos_fp4_quantize", "kairos_context_create",
+    "kairos_context_destroy",
 )
 
 
@@ -58,7 +59,10 @@ def lib():
         L.kairos_hlta_ring_frames_required.argtypes = [POINTER(HltaDesc), POINTER(c_int32)]
         L.kairos_gdn_fwd.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]
         L.kairos_window_fwd.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 9
-        L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p]
+        L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p,
+                                                                             c_void_p]
+        L.kairos_context_create.argtypes = [POINTER(c_void_p)]
+        L.kairos_context_destroy.argtypes = [c_void_p]
         L.kairos_hlta_window_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_size_t, c_void_p]
         L.kairos_gdn_prologue.argtypes = [POINTER(GdnDesc), c_int32] + [c_void_p] * 11
         L.kairos_rope.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 4
@@ -69,6 +73,33 @@ def lib():
             getattr(L, name).restype = c_int if name != "kairos_status_string" else c_char_p
         _lib = L
     return _lib
+
+
+class Context:
+    """A kairos_context of the current device (side stream and events of the
+    layer call), destroyed with close() or when garbage-collected."""
+
+    def __init__(self):
+        h = c_void_p()
+        _check(lib().kairos_context_create(byref(h)), "kairos_context_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            _check(lib().kairos_context_destroy(self.handle), "kairos_context_destroy")
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
 
 def status_string(status: int) -> str:
@@ -273,9 +304,10 @@ def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=
 def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, frame_offset=0,
                     state_in=None, ring_frames=0, k_ring=None, v_ring=None, window_qk=BF16,
                     out=None, state_out=None, keep_state=True, workspace=None, stream=None,
-                    centered=False, rope_base=0.0):
+                    centered=False, rope_base=0.0, ctx=None):
     """Hybrid layer forward.  q, k, v: [B, T, H, 128] bf16; alpha, beta
-    [B, T, H] fp32; gate_logits [3, H] fp32.  Returns (out, state_out)."""
+    [B, T, H] fp32; gate_logits [3, H] fp32; ctx an optional Context (its
+    side stream runs part of the call).  Returns (out, state_out)."""
     torch = _torch()
     B, T, H, d = q.shape
     dev = q.device
@@ -302,7 +334,8 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
         raise ValueError(f"workspace too small: {ws.numel()} < {nws}")
     st = lib().kairos_hlta_fwd(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                _ptr(gate_logits), _ptr(state_in), _ptr(k_ring), _ptr(v_ring),
-                               _ptr(out), _ptr(state_out), _ptr(ws), nws, _stream(stream))
+                               _ptr(out), _ptr(state_out), _ptr(ws), nws,
+                               None if ctx is None else ctx.handle, _stream(stream))
     _check(st, "kairos_hlta_fwd")
     return out, state_out
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <new>
 
 #include "kairos.h"
 #include "common.hpp"
@@ -13,6 +14,18 @@
 #include "launch.hpp"
 
 using namespace kairos;
+
+// Execution context of layer calls (kairos_context_create): a side stream of
+// the device it was created on, the events that fork work onto it and join
+// it back, and the device's compute-unit count.  Owned by the caller; the
+// mutex orders the record / wait pairs of calls that share the context.
+struct kairos_context_t {
+  int device = -1;
+  int cus = 0;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, gdn = nullptr;
+  std::mutex mu;
+};
 
 namespace {
 
@@ -46,6 +59,15 @@ int check_gdn_desc(const kairos_gdn_desc* d) {
   if (d->io == KAIROS_BF16 && d->dk == 32) return KAIROS_ERR_UNSUPPORTED;
   const int64_t n = (int64_t)d->B * d->T * d->H * d->dk;
   if (n > kMaxElems) return KAIROS_ERR_SHAPE;
+  // one workgroup per (b, h) of the fp32 path; the chunk kernels address the
+  // rows of a 64-token chunk by 32-bit byte offsets and count their
+  // workgroups in 32-bit integers
+  if ((int64_t)d->B * d->H > INT32_MAX) return KAIROS_ERR_SHAPE;
+  if (d->io == KAIROS_BF16) {
+    const int64_t tok_bytes = (int64_t)d->H * d->dk * 2;
+    if (63 * tok_bytes + d->dk * 2 >= ((int64_t)1 << 32)) return KAIROS_ERR_SHAPE;
+    if ((int64_t)d->B * d->H * ((d->T + 63) / 64) > INT32_MAX) return KAIROS_ERR_SHAPE;
+  }
   return KAIROS_OK;
 }
 
@@ -194,39 +216,18 @@ void fill_win_args(WinArgs& a, const kairos_hlta_desc* d) {
   a.frame_offset = (long)d->frame_offset;
 }
 
-// Per-device side stream of a layer call: the windowed branches' operand
-// pre-passes (block quantisers, RoPE) read only q and k, so they run beside
-// the gated delta rule's scan, which leaves part of the chip idle (one
-// workgroup per (b, h, row half), latency-bound), and join before the window
-// kernel.  Created on first use and kept until the process ends; the mutex
-// orders the event record / wait pairs of concurrent callers.
-struct SideStream {
-  std::mutex mu;
-  bool ready = false;
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, gdn = nullptr;
-  int cus = 0;   // compute units of the device
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_init;
-
-// The current device's side stream, or nullptr (then the pre-passes stay on
-// the caller's stream).
-SideStream* side_stream() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& sd = g_side[dev];
-  std::lock_guard<std::mutex> lk(g_side_init);
-  if (!sd.ready) {
-    if (!sd.s && hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (!sd.fork && hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (!sd.join && hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (!sd.gdn && hipEventCreateWithFlags(&sd.gdn, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (hipDeviceGetAttribute(&sd.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return nullptr;
-    sd.ready = true;
-  }
-  return &sd;
+// Whether a layer call may use its context's side stream: always when the
+// side stream is idle or eager; when it belongs to a graph capture (it was
+// forked into one and stays in it until that capture ends), only if the
+// caller's stream is part of the same capture.  Otherwise (another thread's
+// capture holds the side stream) the call runs on the caller's stream alone.
+bool side_usable(const kairos_context_t* c, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone, ss = hipStreamCaptureStatusNone;
+  unsigned long long cid = 0, sid = 0;
+  if (hipStreamGetCaptureInfo(c->side, &ss, &sid) != hipSuccess) return false;
+  if (ss == hipStreamCaptureStatusNone) return true;
+  if (hipStreamGetCaptureInfo(s, &cs, &cid) != hipSuccess) return false;
+  return ss == hipStreamCaptureStatusActive && cs == hipStreamCaptureStatusActive && cid == sid;
 }
 
 // Whether a layer call runs its GDN branch beside the window kernel (the
@@ -237,11 +238,11 @@ SideStream* side_stream() {
 // frame.  On larger calls the extra fp32 round trip and the scan's share of
 // the compute units cost more than the overlap saves (measured: one 1560-
 // token frame at H 24 -10%; 21 frames +10%; the B4 16 x 3600 FP8 layer +4%).
-bool overlap_gdn(const kairos_hlta_desc* d, const SideStream* sd) {
-  if (!sd || sd->cus <= 0 || d->g.dk != 128) return false;
+bool overlap_gdn(const kairos_hlta_desc* d, const kairos_context_t* c) {
+  if (!c || c->cus <= 0 || d->g.dk != 128) return false;
   const long win = window_workgroups(d->g.B, d->g.T, d->g.H, d->L);
   const long gdn = (long)d->g.B * d->g.H * (d->g.dk / (16 * gdn_chunk_waves(d->g.B, d->g.H, d->g.dk)));
-  return win + gdn <= 2L * sd->cus;
+  return win + gdn <= 2L * c->cus;
 }
 
 }  // namespace
@@ -263,7 +264,7 @@ const char* kairos_status_string(int status) {
   }
 }
 
-int kairos_version(void) { return 103; }
+int kairos_version(void) { return 200; }
 
 int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
   if (!bytes) return KAIROS_ERR_NULL;
@@ -402,12 +403,48 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
   return hip_status(launch_window(a, qf, true, (hipStream_t)stream));
 }
 
+int kairos_context_create(kairos_context* ctx) {
+  if (!ctx) return KAIROS_ERR_NULL;
+  *ctx = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KAIROS_ERR_HIP;
+  kairos_context_t* c = new (std::nothrow) kairos_context_t;
+  if (!c) return KAIROS_ERR_HIP;
+  c->device = dev;
+  bool ok = hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&c->fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&c->join, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&c->gdn, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    kairos_context_destroy(c);
+    return KAIROS_ERR_HIP;
+  }
+  *ctx = c;
+  return KAIROS_OK;
+}
+
+int kairos_context_destroy(kairos_context ctx) {
+  if (!ctx) return KAIROS_OK;
+  bool ok = true;
+  if (ctx->side) ok &= hipStreamDestroy(ctx->side) == hipSuccess;
+  for (hipEvent_t ev : {ctx->fork, ctx->join, ctx->gdn})
+    if (ev) ok &= hipEventDestroy(ev) == hipSuccess;
+  delete ctx;
+  return ok ? KAIROS_OK : KAIROS_ERR_HIP;
+}
+
 int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, const float* gate_logits,
                     const float* state_in, void* k_ring, void* v_ring, void* out, float* state_out,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, kairos_context ctx, void* stream) {
   int st = check_hlta_desc(desc, true);
   if (st != KAIROS_OK) return st;
+  if (ctx) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KAIROS_ERR_HIP;
+    if (dev != ctx->device) return KAIROS_ERR_UNSUPPORTED;
+  }
   st = check_gdn_ptrs(&desc->g, q, k, v, alpha, beta, state_in, out, state_out);
   if (st != KAIROS_OK) return st;
   if (!gate_logits) return KAIROS_ERR_NULL;
@@ -435,18 +472,27 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   // * otherwise: the GDN branch first, the operand pre-passes on the side
   //   stream once its prep kernel is done (both are bandwidth-bound; the
   //   scan is not), the window kernel's epilogue adds the GDN output.
-  SideStream* sd = T > 0 ? side_stream() : nullptr;
-  const bool ovl = overlap_gdn(desc, sd);
-  if (!ovl && !ws.has1 && !ws.has2) sd = nullptr;      // one stream is enough
+  kairos_context_t* sd = T > 0 ? ctx : nullptr;
   std::unique_lock<std::mutex> lk;
-  if (sd) lk = std::unique_lock<std::mutex>(sd->mu);
+  if (sd) {
+    lk = std::unique_lock<std::mutex>(sd->mu);
+    if (!side_usable(sd, s)) {
+      lk.unlock();
+      sd = nullptr;
+    }
+  }
+  const bool ovl = overlap_gdn(desc, sd);
+  if (sd && !ovl && !ws.has1 && !ws.has2) {            // one stream is enough
+    lk.unlock();
+    sd = nullptr;
+  }
   hipError_t e;
   if (ovl) {
-    if (hipEventRecord(sd->fork, s) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+    if (hipEventRecord(sd->fork, s) != hipSuccess || hipStreamWaitEvent(sd->side, sd->fork, 0) != hipSuccess)
       return KAIROS_ERR_HIP;
     e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha, beta,
-                         state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, sd->s);
-    if (e != hipSuccess || hipEventRecord(sd->gdn, sd->s) != hipSuccess) return KAIROS_ERR_HIP;
+                         state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, sd->side);
+    if (e != hipSuccess || hipEventRecord(sd->gdn, sd->side) != hipSuccess) return KAIROS_ERR_HIP;
   } else {
     e = launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, alpha, beta,
                          state_in, o_gdn, state_out, B, T, H, D, 0, wsb + ws.gdn, s,
@@ -454,7 +500,7 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     if (e != hipSuccess) return KAIROS_ERR_HIP;
   }
   if (T == 0) return KAIROS_OK;
-  const hipStream_t so = (sd && !ovl) ? sd->s : s;   // stream of the operand pre-passes
+  const hipStream_t so = (sd && !ovl) ? sd->side : s;   // stream of the operand pre-passes
   if (so != s && hipStreamWaitEvent(so, sd->fork, 0) != hipSuccess) return KAIROS_ERR_HIP;
   WinArgs a;
   fill_win_args(a, desc);
