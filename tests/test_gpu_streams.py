@@ -3,8 +3,8 @@ context's side stream, joined back by events.  Callers on two streams at
 once, a layer call captured into a graph and replayed with eager work in
 between, and eager calls on a second host thread while the first thread
 holds a capture open on the same context must all give results
-bit-identical to plain sequential calls (same kernels, same inputs: any race
-or missing join shows as a difference)."""
+bit-identical to sequential calls of the same schedule (same kernels, same
+inputs: any race or missing join shows as a difference)."""
 import threading
 
 import pytest
@@ -32,10 +32,15 @@ def _layer(dv, L, w, dil, out, state, ws, stream=None, ctx=None):
 
 
 def test_context_matches_single_stream():
-    """Both schedules a context enables (GDN beside the window kernel for a
-    small call, pre-passes beside the scan for a larger one) against the
-    single-stream call."""
-    for (B, F, L, H, w, dil, seed) in ((1, 6, 200, 2, 300, 4, 504), (1, 8, 1024, 8, 1000, 4, 505)):
+    """Both schedules a context enables against the single-stream call.  For a
+    larger call the pre-passes run beside the scan: same kernels, bit-identical
+    results.  For a small call the GDN branch runs beside the window kernel and
+    a combine kernel adds it: (o_swa + o_dswa) + o_gdn instead of the
+    epilogue's o_dswa + (o_swa + o_gdn) in fp32, so y may differ by the bf16
+    rounding of that reordering (at most one bf16 step); the state is the same
+    GDN computation and must be bit-identical."""
+    for (B, F, L, H, w, dil, seed, exact) in ((1, 6, 200, 2, 300, 4, 504, False),
+                                              (1, 8, 1024, 8, 1000, 4, 505, True)):
         T = F * L
         print(f"context vs single stream F{F} L{L} H{H}", flush=True)
         dv = inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=seed))
@@ -49,7 +54,13 @@ def test_context_matches_single_stream():
                 S.zero_()
                 _layer(dv, L, w, dil, o, S, ws, ctx=ctx)
                 torch.cuda.synchronize()
-                assert torch.equal(o, ref_o) and torch.equal(S, ref_S)
+                assert torch.equal(S, ref_S)
+                if exact:
+                    assert torch.equal(o, ref_o)
+                else:
+                    r = ref_o.float()
+                    step = r.abs() * 2.0 ** -7 + 1e-5 * r.abs().max()
+                    assert bool(((o.float() - r).abs() <= step).all())
 
 
 def test_layer_on_two_streams_at_once():
@@ -58,13 +69,13 @@ def test_layer_on_two_streams_at_once():
     print("two streams", flush=True)
     dvs = [inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=s)) for s in (501, 502)]
     bufs = [_bufs(B, T, H, L, w, dil) for _ in dvs]
+    ctx = K.Context()
     refs = []
     for dv, (o, S, ws) in zip(dvs, bufs):
-        _layer(dv, L, w, dil, o, S, ws)
+        _layer(dv, L, w, dil, o, S, ws, ctx=ctx)
         torch.cuda.synchronize()
         refs.append((o.clone(), S.clone()))
     streams = (torch.cuda.Stream(), torch.cuda.Stream())
-    ctx = K.Context()
     for it in range(3):
         for o, S, _ in bufs:
             o.zero_()
@@ -125,12 +136,17 @@ def test_capture_on_one_thread_eager_calls_on_another():
     dva = inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=506))
     dvb = inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=507))
     ba, bb = _bufs(B, T, H, L, w, dil), _bufs(B, T, H, L, w, dil)
-    refs = []
+    # references of both schedules: with the context's side stream, and on
+    # one stream (what a call does while another capture holds the side stream)
+    ctx = K.Context()
+    refs, refs1 = [], []
     for dv, (o, S, ws) in ((dva, ba), (dvb, bb)):
-        _layer(dv, L, w, dil, o, S, ws)
+        _layer(dv, L, w, dil, o, S, ws, ctx=ctx)
         torch.cuda.synchronize()
         refs.append((o.clone(), S.clone()))
-    ctx = K.Context()
+        _layer(dv, L, w, dil, o, S, ws)
+        torch.cuda.synchronize()
+        refs1.append((o.clone(), S.clone()))
     sb = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     errors = []
@@ -157,7 +173,8 @@ def test_capture_on_one_thread_eager_calls_on_another():
         tb.join()
     assert not errors, errors
     torch.cuda.synchronize()
-    assert torch.equal(bb[0], refs[1][0]) and torch.equal(bb[1], refs[1][1]), "eager thread differs"
+    assert torch.equal(bb[1], refs[1][1]), "eager thread: state differs"
+    assert torch.equal(bb[0], refs[1][0]) or torch.equal(bb[0], refs1[1][0]), "eager thread differs"
     for it in range(2):
         ba[0].zero_()
         ba[1].zero_()
