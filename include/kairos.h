@@ -162,6 +162,22 @@ int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, co
                    void* out, float* state_out, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* kairos_gdn_fwd for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and kernels, with the workspace taken from a scratch array
+ * the library holds in each device's memory (64 MiB, a fixed part of the
+ * library's device image, kept until the process ends).  Calls nothing that
+ * allocates.  Arguments and errors as for kairos_gdn_fwd, with no workspace
+ * arguments; a problem whose workspace (kairos_gdn_workspace_size) exceeds
+ * 64 MiB returns KAIROS_ERR_WORKSPACE.  The first call on a device resolves
+ * that device's copy of the array (KAIROS_ERR_HIP if the runtime refuses).
+ * All no-alloc calls on one device share its array: calls that overlap in
+ * time on one device (concurrent streams or host threads) race and give
+ * undefined results; calls ordered on one stream are safe. */
+int kairos_gdn_fwd_noalloc(const kairos_gdn_desc* desc, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta,
+                           const float* state_in, void* out, float* state_out, void* stream);
+
 /* One windowed softmax branch on its own (Sec. 2.2.2): SWA when dilation == 1,
  * DSWA otherwise (Eq. 8 as a frame-residue index map; nothing is rearranged
  * in memory).  Uses desc->L, window, frame_offset, ring_frames, window_qk and

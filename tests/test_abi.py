@@ -64,7 +64,7 @@ def _writable_symbols():
 
 # the only file-scope state: the per-device device addresses of the no-alloc
 # entry point's scratch array (resolved once per device)
-ALLOWED_STATE = {"kairos::noalloc_scratch_ptr", "kairos::noalloc_scratch_mu"}
+ALLOWED_STATE = {"kairos::scratch", "kairos::noalloc_scratch_ptr", "kairos::noalloc_scratch_mu"}
 
 
 def test_no_global_state():
@@ -72,6 +72,26 @@ def test_no_global_state():
     call's side stream and events live in a caller-created kairos_context."""
     names = _writable_symbols()
     assert set(names) <= ALLOWED_STATE, names
+
+
+@host_only
+def test_gdn_noalloc_validation():
+    """The no-alloc entry point checks like kairos_gdn_fwd and refuses
+    problems whose workspace exceeds its 64 MiB array, before touching the
+    device."""
+    L = K.lib()
+    cv = ctypes.c_void_p
+    args = lambda: [cv(1 * G), cv(2 * G), cv(3 * G), cv(4 * G), cv(5 * G), None, cv(6 * G), None, None]
+    big = K.gdn_desc(4, 57600, 24, 128)
+    assert K.kairos_gdn_workspace_size(big) > 64 << 20
+    assert L.kairos_gdn_fwd_noalloc(ctypes.byref(big), *args()) == WS
+    d = K.gdn_desc(1, 64, 2, 128)
+    a = args()
+    a[6] = None                                            # out
+    assert L.kairos_gdn_fwd_noalloc(ctypes.byref(d), *a) == NULL
+    a = args()
+    a[6] = cv(1 * G + 64)                                  # out overlaps q
+    assert L.kairos_gdn_fwd_noalloc(ctypes.byref(d), *a) == ALIAS
 
 
 @host_only

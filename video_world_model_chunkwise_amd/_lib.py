@@ -18,7 +18,7 @@ symbols = (
     "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
     "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
     "kairos_gdn_prologue", "kairos_rope", "kairos_fp4_quantize", "kairos_context_create",
-    "kairos_context_destroy",
+    "kairos_context_destroy", "kairos_gdn_fwd_noalloc",
 )
 
 
@@ -58,6 +58,7 @@ def lib():
         L.kairos_hlta_workspace_size.argtypes = [POINTER(HltaDesc), POINTER(c_size_t)]
         L.kairos_hlta_ring_frames_required.argtypes = [POINTER(HltaDesc), POINTER(c_int32)]
         L.kairos_gdn_fwd.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]
+        L.kairos_gdn_fwd_noalloc.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p]
         L.kairos_window_fwd.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 9
         L.kairos_hlta_fwd.argtypes = [POINTER(HltaDesc)] + [c_void_p] * 11 + [c_void_p, c_size_t, c_void_p,
                                                                              c_void_p]
@@ -213,6 +214,31 @@ def kairos_gdn_fwd(q, k, v, alpha, beta, state_in=None, out=None, state_out=None
                               _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ws), nws,
                               _stream(stream))
     _check(st, "kairos_gdn_fwd")
+    return out, state_out
+
+
+def kairos_gdn_fwd_noalloc(q, k, v, alpha, beta, state_in=None, out=None, state_out=None,
+                           stream=None):
+    """kairos_gdn_fwd with the library's own per-device scratch array as the
+    workspace (nothing is allocated for it).  out and state_out must be given
+    (the point of the call is that nothing is allocated); returns them."""
+    torch = _torch()
+    B, T, H, d = q.shape
+    dev = q.device
+    io = F32 if q.dtype == torch.float32 else BF16
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _need(t, name, q.dtype, (B, T, H, d), dev)
+    _need(alpha, "alpha", torch.float32, (B, T, H), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, (B, H, d, d), dev)
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, (B, H, d, d), dev)
+    desc = gdn_desc(B, T, H, d, io)
+    st = lib().kairos_gdn_fwd_noalloc(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                      _ptr(beta), _ptr(state_in), _ptr(out), _ptr(state_out),
+                                      _stream(stream))
+    _check(st, "kairos_gdn_fwd_noalloc")
     return out, state_out
 
 

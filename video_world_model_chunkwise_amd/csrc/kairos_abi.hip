@@ -27,6 +27,23 @@ struct kairos_context_t {
   std::mutex mu;
 };
 
+namespace kairos {
+
+// Scratch array of kairos_gdn_fwd_noalloc, the workspace of callers that
+// cannot allocate device memory.  Each device the library runs on holds its
+// own copy until the process ends.  Host code never uses the array's name as
+// an address (on the host it is only a stand-in for the symbol): the device
+// address of each device's copy is resolved once, with that device current,
+// and kept in noalloc_scratch_ptr.  Every no-alloc call on a device shares
+// its copy, so such calls must not overlap on one device.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxNoallocDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+void* noalloc_scratch_ptr[kMaxNoallocDevices];
+std::mutex noalloc_scratch_mu;
+
+}  // namespace kairos
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 40;   // bound on any tensor's element count
@@ -238,11 +255,44 @@ bool side_usable(const kairos_context_t* c, hipStream_t s) {
 // frame.  On larger calls the extra fp32 round trip and the scan's share of
 // the compute units cost more than the overlap saves (measured: one 1560-
 // token frame at H 24 -10%; 21 frames +10%; the B4 16 x 3600 FP8 layer +4%).
+// Device address of the current device's copy of the scratch array,
+// resolved on the first no-alloc call on that device.
+int noalloc_scratch(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KAIROS_ERR_HIP;
+  if (dev >= kMaxNoallocDevices) return KAIROS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(noalloc_scratch_mu);
+  if (!noalloc_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KAIROS_ERR_HIP;
+    noalloc_scratch_ptr[dev] = ptr;
+  }
+  *p = noalloc_scratch_ptr[dev];
+  return KAIROS_OK;
+}
+
+// The launch sequence of kairos_gdn_fwd once the arguments are checked.
+int gdn_fwd_launch(const kairos_gdn_desc* desc, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* state_in, void* out,
+                   float* state_out, void* workspace, hipStream_t s);
+
 bool overlap_gdn(const kairos_hlta_desc* d, const kairos_context_t* c) {
   if (!c || c->cus <= 0 || d->g.dk != 128) return false;
   const long win = window_workgroups(d->g.B, d->g.T, d->g.H, d->L);
   const long gdn = (long)d->g.B * d->g.H * (d->g.dk / (16 * gdn_chunk_waves(d->g.B, d->g.H, d->g.dk)));
   return win + gdn <= 2L * c->cus;
+}
+
+int gdn_fwd_launch(const kairos_gdn_desc* desc, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* state_in, void* out,
+                   float* state_out, void* workspace, hipStream_t s) {
+  if (desc->io == KAIROS_F32)
+    return hip_status(launch_gdn_f32((const float*)q, (const float*)k, (const float*)v, alpha, beta,
+                                     state_in, (float*)out, state_out, desc->B, desc->T, desc->H,
+                                     desc->dk, s));
+  return hip_status(launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                     alpha, beta, state_in, (uint16_t*)out, state_out, desc->B,
+                                     desc->T, desc->H, desc->dk, 0, workspace, s));
 }
 
 }  // namespace
@@ -304,14 +354,25 @@ int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, co
       overlaps(workspace, need, k, nx) || overlaps(workspace, need, v, nx) ||
       overlaps(workspace, need, state_out, (size_t)desc->B * desc->H * desc->dk * desc->dv * 4))
     return KAIROS_ERR_ALIAS;
-  hipStream_t s = (hipStream_t)stream;
-  if (desc->io == KAIROS_F32)
-    return hip_status(launch_gdn_f32((const float*)q, (const float*)k, (const float*)v, alpha, beta,
-                                     state_in, (float*)out, state_out, desc->B, desc->T, desc->H,
-                                     desc->dk, s));
-  return hip_status(launch_gdn_chunk((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                     alpha, beta, state_in, (uint16_t*)out, state_out, desc->B,
-                                     desc->T, desc->H, desc->dk, 0, workspace, s));
+  return gdn_fwd_launch(desc, q, k, v, alpha, beta, state_in, out, state_out, workspace,
+                        (hipStream_t)stream);
+}
+
+int kairos_gdn_fwd_noalloc(const kairos_gdn_desc* desc, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* state_in, void* out,
+                           float* state_out, void* stream) {
+  int st = check_gdn_desc(desc);
+  if (st != KAIROS_OK) return st;
+  st = check_gdn_ptrs(desc, q, k, v, alpha, beta, state_in, out, state_out);
+  if (st != KAIROS_OK) return st;
+  const size_t need = gdn_ws_bytes(desc);
+  if (need > kNoallocScratchBytes) return KAIROS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = noalloc_scratch(&ws);
+    if (st != KAIROS_OK) return st;
+  }
+  return gdn_fwd_launch(desc, q, k, v, alpha, beta, state_in, out, state_out, ws, (hipStream_t)stream);
 }
 
 int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void* q, const void* k,
