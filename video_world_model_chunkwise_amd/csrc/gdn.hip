@@ -175,8 +175,14 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
                                                       int nchunks) {
   constexpr int DS = D / 32;
   __shared__ __attribute__((aligned(16))) PrepSmem sm;
-  const int c = blockIdx.x % nchunks;
-  const int bh = blockIdx.x / nchunks;
+  // Heads vary fastest, and each XCD takes a contiguous range of the
+  // (chunk, head) order: the waves of one chunk's heads run together on one
+  // XCD, so the per-token rows of k, alpha and beta (all heads of a token are
+  // adjacent in memory) are fetched once into that XCD's L2 and shared.
+  const int BH = (int)(gridDim.x / nchunks);
+  const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int c = lid / BH;
+  const int bh = lid % BH;
   const int b = bh / H, h = bh % H;
   const int t0 = c * CH;
   const int valid = min(CH, T - t0);
@@ -440,6 +446,7 @@ struct ScanCtx {
   size_t beta0;          // element offset of (b, t = 0, h) in beta
   int T, H, nchunks, n_base, wave;
   uint32_t tok_bytes;
+  bool vzero;            // transition rows: V is read as zero (empty buffer range)
 };
 
 // Per-lane byte offsets of the loader wave's loads inside a chunk: load m of
@@ -459,8 +466,10 @@ struct ScanLoadOffs {
   uint32_t t[TJ];
   // loads m = lw, lw + NW, ... < U of a tile of U loads
   static constexpr int share(int U) { return U > LW ? (U - 1 - LW) / NW + 1 : 0; }
+  // loads of the Q/V/T batch (no Q without outputs)
+  template <bool OUT>
   static constexpr int qvt_loads() {
-    return share(ScanGeom<D, NW>::KU) + share(ScanGeom<D, NW>::VU) + share(ScanGeom<D, NW>::TU);
+    return (OUT ? share(ScanGeom<D, NW>::KU) : 0) + share(ScanGeom<D, NW>::VU) + share(ScanGeom<D, NW>::TU);
   }
 };
 
@@ -491,7 +500,7 @@ __device__ __forceinline__ void scan_issue_k(const ScanCtx<D, NW>& x, const Scan
   }
 }
 
-template <int D, int NW, int LW>
+template <int D, int NW, int LW, bool OUT>
 __device__ __forceinline__ void scan_issue_qvt(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW, LW>& lo,
                                                const ScanBuf& bf, int c) {
   using G = ScanGeom<D, NW>;
@@ -499,7 +508,7 @@ __device__ __forceinline__ void scan_issue_qvt(const ScanCtx<D, NW>& x, const Sc
   const size_t e0 = x.head0 + (size_t)c * x.chunk_elems;
   const uint32_t nrec = chunk_bytes(x.T, c, x.tok_bytes, D);
   const auto rq = buf_rsrc(x.q + e0, nrec);
-  const auto rv = buf_rsrc(x.v + e0 + x.n_base, nrec);
+  const auto rv = buf_rsrc(x.v + e0 + x.n_base, x.vzero ? 0u : nrec);
   const auto rt = buf_rsrc(x.t_in + (x.tg0 + c) * CH * CH, CH * CH * 2);
 #pragma unroll
   for (int j = 0; j < L::TJ; ++j) {
@@ -511,10 +520,12 @@ __device__ __forceinline__ void scan_issue_qvt(const ScanCtx<D, NW>& x, const Sc
     const int m = LW + NW * j;
     if (m < G::VU) buf_to_lds16(rv, bf.V + opaque_offset(512 * m), lo.v[j]);
   }
+  if constexpr (OUT) {
 #pragma unroll
-  for (int j = 0; j < L::KJ; ++j) {
-    const int m = LW + NW * j;
-    if (m < G::KU) buf_to_lds16(rq, bf.Q + opaque_offset(512 * m), lo.kq[j]);
+    for (int j = 0; j < L::KJ; ++j) {
+      const int m = LW + NW * j;
+      if (m < G::KU) buf_to_lds16(rq, bf.Q + opaque_offset(512 * m), lo.kq[j]);
+    }
   }
 }
 
@@ -552,8 +563,9 @@ __device__ __forceinline__ void scan_store_o(const ScanCtx<D, NW>& x, const uint
   }
 }
 
-// One chunk of a compute wave: reads buffer cb.
-template <int D, int NW>
+// One chunk of a compute wave: reads buffer cb.  Without outputs (OUT
+// false) only the state is advanced: no Q, no P, no O.
+template <int D, int NW, bool OUT>
 __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBuf& cb,
                                            uint16_t* Pb, uint16_t* Os, f32x4 (&S)[D / 16], int c) {
   using G = ScanGeom<D, NW>;
@@ -568,7 +580,7 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
   // ---- P = lower(2^{g_t - g_i} q_t . k_i), as tiles of K Q^T: lane holds
   //      keys i0 .. i0+3 (consecutive tokens) of query t
   constexpr int NTASK = 12 / NW;
-  if constexpr (!G::PM) {
+  if constexpr (OUT && !G::PM) {
     uint4 pk[2][DS], pq[2][DS];
     float gt[2];
     float4 gi[2];
@@ -626,7 +638,7 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
       const uint16_t* qrow = cb.Q + (16 * (tt) + l16) * KST + 8 * g;                       \
       _Pragma("unroll") for (int s = 0; s < DS; ++s) {                                     \
         xk[buf][s] = *reinterpret_cast<const uint4*>(krow + 32 * s);                       \
-        xq[buf][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);                       \
+        if constexpr (OUT) xq[buf][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);    \
       }                                                                                    \
     }
     KAIROS_XY_LOAD(0, 0);
@@ -635,7 +647,7 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
     uint4 qw[DS];
     int p_t = 0;
     float p_gt = 0.f;
-    if constexpr (G::PM) {
+    if constexpr (OUT && G::PM) {
       const uint16_t* qrow = cb.Q + (16 * wave + l16) * KST + 8 * g;
 #pragma unroll
       for (int s = 0; s < DS; ++s) qw[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
@@ -649,7 +661,7 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
     for (int tt = 0; tt < 4; ++tt) {
       const int cur_b = tt & 1;
       float4 p_gi = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (G::PM) p_gi = *reinterpret_cast<const float4*>(cb.g2 + row_token(16 * tt + 4 * g));
+      if constexpr (OUT && G::PM) p_gi = *reinterpret_cast<const float4*>(cb.g2 + row_token(16 * tt + 4 * g));
       if (tt + 1 < 4) {
         KAIROS_XY_LOAD(tt + 1, cur_b ^ 1);
       } else {
@@ -671,9 +683,9 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
         X[tt] = mfma16x16x32(as_bf16x8(xk[cur_b][s]), Sop[s], X[tt]);
-        Y[tt] = mfma16x16x32(Sop[s], as_bf16x8(xq[cur_b][s]), Y[tt]);
+        if constexpr (OUT) Y[tt] = mfma16x16x32(Sop[s], as_bf16x8(xq[cur_b][s]), Y[tt]);
       }
-      if constexpr (G::PM) {
+      if constexpr (OUT && G::PM) {
         if (wave >= 2 * (tt / 2)) {
           f32x4 acc = zero4();
 #pragma unroll
@@ -734,10 +746,12 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
   // O^T = 2^g Y^T + E^T P^T;  S <- 2^{g_C} S + K^T diag(w) E
   {
     uint4 po[6];
+    if constexpr (OUT) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) po[tt] = *reinterpret_cast<const uint4*>(Pb + (16 * tt + l16) * TST + 8 * g);
-    po[4] = *reinterpret_cast<const uint4*>(Pb + (32 + l16) * TST + 32 + 8 * g);
-    po[5] = *reinterpret_cast<const uint4*>(Pb + (48 + l16) * TST + 32 + 8 * g);
+      for (int tt = 0; tt < 4; ++tt) po[tt] = *reinterpret_cast<const uint4*>(Pb + (16 * tt + l16) * TST + 8 * g);
+      po[4] = *reinterpret_cast<const uint4*>(Pb + (32 + l16) * TST + 32 + 8 * g);
+      po[5] = *reinterpret_cast<const uint4*>(Pb + (48 + l16) * TST + 32 + 8 * g);
+    }
     KAIROS_KT_LOAD(1, 1);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 WE[4];
@@ -746,15 +760,17 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
       WE[tt] = f32x4{w4[tt].x * E[tt][0], w4[tt].y * E[tt][1], w4[tt].z * E[tt][2], w4[tt].w * E[tt][3]};
     const bf16x8 WEop0 = regs_operand(WE[0], WE[1]);
     const bf16x8 WEop1 = regs_operand(WE[2], WE[3]);
-    const bf16x8 Eop0 = regs_operand(E[0], E[1]);
-    const bf16x8 Eop1 = regs_operand(E[2], E[3]);
+    if constexpr (OUT) {
+      const bf16x8 Eop0 = regs_operand(E[0], E[1]);
+      const bf16x8 Eop1 = regs_operand(E[2], E[3]);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      f32x4 o = f32x4{gmo[tt] * Y[tt][0], gmo[tt] * Y[tt][1], gmo[tt] * Y[tt][2], gmo[tt] * Y[tt][3]};
-      o = mfma16x16x32(Eop0, as_bf16x8(po[tt]), o);
-      if (tt >= 2) o = mfma16x16x32(Eop1, as_bf16x8(po[tt + 2]), o);
-      *reinterpret_cast<uint2*>(Os + row_token(16 * tt + l16) * G::OST + 16 * wave + 4 * g) =
-          pack_bf16x4(o[0], o[1], o[2], o[3]);
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4 o = f32x4{gmo[tt] * Y[tt][0], gmo[tt] * Y[tt][1], gmo[tt] * Y[tt][2], gmo[tt] * Y[tt][3]};
+        o = mfma16x16x32(Eop0, as_bf16x8(po[tt]), o);
+        if (tt >= 2) o = mfma16x16x32(Eop1, as_bf16x8(po[tt + 2]), o);
+        *reinterpret_cast<uint2*>(Os + row_token(16 * tt + l16) * G::OST + 16 * wave + 4 * g) =
+            pack_bf16x4(o[0], o[1], o[2], o[3]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -780,24 +796,25 @@ __device__ __forceinline__ void scan_chunk(const ScanCtx<D, NW>& x, const ScanBu
 // cb; 2^{g} and 2^{g_C - g} of chunk c+1.  Before the end barrier everything
 // but the newest batch has landed.  Two barriers per chunk, as in the compute
 // waves.
-template <int D, int NW, int LW>
+template <int D, int NW, int LW, bool OUT>
 __device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const ScanLoadOffs<D, NW, LW>& lo,
                                                 const ScanBuf& cb, const ScanBuf& nb, const uint16_t* Os,
                                                 int c) {
   using L = ScanLoadOffs<D, NW, LW>;
   const bool more1 = c + 1 < x.nchunks, more2 = c + 2 < x.nchunks;
   if (more1) scan_issue_k<D, NW, LW>(x, lo, nb, c + 1);
-  scan_store_o<D, NW, LW>(x, Os, c - 1, c > 0);
+  if constexpr (OUT) scan_store_o<D, NW, LW>(x, Os, c - 1, c > 0);
   lds_barrier();
   if constexpr (LW == 0) {
     if (more1) {
-      wait_vmem_le<L::share(ScanGeom<D, NW>::KU) + 2>();   // g and b of chunk c+1
+      // g and b of chunk c+1 (issued before its K loads and the two O stores)
+      wait_vmem_le<L::share(ScanGeom<D, NW>::KU) + (OUT ? 2 : 0)>();
       scan_decays(nb);
     }
   }
   if (more2) {
-    scan_issue_qvt<D, NW, LW>(x, lo, cb, c + 2);
-    wait_vmem_le<L::qvt_loads()>();                         // all but the batch just issued
+    scan_issue_qvt<D, NW, LW, OUT>(x, lo, cb, c + 2);
+    wait_vmem_le<L::template qvt_loads<OUT>()>();           // all but the batch just issued
   } else {
     wait_vmem();
   }
@@ -806,7 +823,7 @@ __device__ __forceinline__ void scan_load_chunk(const ScanCtx<D, NW>& x, const S
 
 // One loader wave: its load offsets, the first two chunks, then one
 // scan_load_chunk per chunk.
-template <int D, int NW, int LW>
+template <int D, int NW, int LW, bool OUT>
 __device__ __forceinline__ void scan_loader(const ScanCtx<D, NW>& x, const ScanBuf& B0, const ScanBuf& B1,
                                             const uint16_t* Os) {
   using G = ScanGeom<D, NW>;
@@ -831,30 +848,58 @@ __device__ __forceinline__ void scan_loader(const ScanCtx<D, NW>& x, const ScanB
   }
   if (x.nchunks > 0) {
     scan_issue_k<D, NW, LW>(x, lo, B0, 0);
-    scan_issue_qvt<D, NW, LW>(x, lo, B0, 0);
-    if (x.nchunks > 1) scan_issue_qvt<D, NW, LW>(x, lo, B1, 1);
+    scan_issue_qvt<D, NW, LW, OUT>(x, lo, B0, 0);
+    if (x.nchunks > 1) scan_issue_qvt<D, NW, LW, OUT>(x, lo, B1, 1);
     wait_vmem();
     if constexpr (LW == 0) scan_decays(B0);
   }
   lds_barrier();
   for (int c = 0; c < x.nchunks; c += 2) {
-    scan_load_chunk<D, NW, LW>(x, lo, B0, B1, Os, c);
-    if (c + 1 < x.nchunks) scan_load_chunk<D, NW, LW>(x, lo, B1, B0, Os, c + 1);
+    scan_load_chunk<D, NW, LW, OUT>(x, lo, B0, B1, Os, c);
+    if (c + 1 < x.nchunks) scan_load_chunk<D, NW, LW, OUT>(x, lo, B1, B0, Os, c + 1);
   }
-  if (x.nchunks > 0) scan_store_o<D, NW, LW>(x, Os, x.nchunks - 1, true);
+  if constexpr (OUT) {
+    if (x.nchunks > 0) scan_store_o<D, NW, LW>(x, Os, x.nchunks - 1, true);
+  }
 }
+
+// Arguments of a scan launch.  The sequence of each (b, h) is cut into nsegs
+// segments of seg_chunks chunks (one segment: the plain scan); a launch runs
+// nseg_launch segments (from segment 0), each as `tiles` row tiles of 16 NW
+// rows.  Tiles below D / (16 NW) advance rows of the state S; tiles above
+// advance rows of the segment's transition M (the same recurrence with v = 0,
+// started from the identity), so that S_end = S_start M + S_end(from zero).
+//   start state of segment j (state rows): init_seg[bh][j] when init_seg is
+//     given, else state_in for j = 0 (NULL: zero), else zero;
+//   end state: the last segment of the sequence -> state_out (NULL: dropped);
+//     other segments -> fin_seg[bh][j + 1] (NULL: dropped); transition rows
+//     -> fin_trans[bh][j].
+// The per-(b, h) segment arrays hold nsegs slots of D x D fp32.
+struct GdnScanArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* beta;
+  const uint16_t* t_in;
+  const float* g_in;
+  uint16_t* out;
+  const float* state_in;
+  float* state_out;
+  const float* init_seg;
+  float* fin_seg;
+  float* fin_trans;
+  int B, T, H, nchunks;
+  int seg_chunks, nsegs, nseg_launch, tiles;
+};
 
 // Workgroup: NW compute waves (16 rows of S each) and NW loader waves that
 // stream the next chunk into the other LDS buffer (each SIMD runs one of
 // each).  The double-buffered LDS tiles allow one workgroup per CU.
-template <int D, int NW>
-__global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ beta, const uint16_t* __restrict__ t_in, const float* __restrict__ g_in,
-    const float* state_in, uint16_t* __restrict__ out, float* state_out, int B, int T, int H) {
+template <int D, int NW, bool OUT>
+__global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(const GdnScanArgs a) {
   using G = ScanGeom<D, NW>;
   constexpr int NR = G::NR;
-  constexpr int NT = D / NR;          // workgroups per head
+  constexpr int NT = D / NR;          // workgroups per head and segment (state rows)
   constexpr int DT = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t K0[CH * G::KST], K1[CH * G::KST];
   __shared__ __attribute__((aligned(16))) uint16_t Q0[CH * G::KST], Q1[CH * G::KST];
@@ -867,47 +912,76 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
   const ScanBuf B0{K0, Q0, V0, T0, g0, gam0, w0, b0};
   const ScanBuf B1{K1, Q1, V1, T1, g1, gam1, w1, b1};
 
+  // (b, h) outermost, then segment, then row tile: the tiles of one segment
+  // are adjacent and share an XCD (and its L2) for the common K, Q, T reads
   const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int bh = lid / NT, tile = lid % NT;
-  if (bh >= B * H) return;
-  const int b = bh / H, h = bh % H;
+  const int per_bh = a.nseg_launch * a.tiles;
+  const int bh = lid / per_bh;
+  if (bh >= a.B * a.H) return;
+  const int j = (lid % per_bh) / a.tiles;
+  const int tile = lid % a.tiles;
+  const bool trans = tile >= NT;
+  if (trans && j == 0) return;        // the first segment starts from a given state
+  const int b = bh / a.H, h = bh % a.H;
+  const int c0 = j * a.seg_chunks;
+  const int nch = max(0, min(a.seg_chunks, a.nchunks - c0));
 
   const int lane = threadIdx.x % 64, l16 = lane % 16, g = lane / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
 
   ScanCtx<D, NW> x;
-  x.q = q; x.k = k; x.v = v; x.beta = beta; x.t_in = t_in; x.g_in = g_in; x.out = out;
-  x.T = T; x.H = H;
-  x.nchunks = (T + CH - 1) / CH;
-  x.n_base = tile * NR;
+  x.q = a.q; x.k = a.k; x.v = a.v; x.beta = a.beta; x.t_in = a.t_in; x.g_in = a.g_in; x.out = a.out;
+  x.T = a.T - c0 * CH; x.H = a.H;
+  x.nchunks = nch;
+  x.n_base = (tile % NT) * NR;
   x.wave = wave;
-  x.tok_bytes = (uint32_t)H * D * 2;
-  x.head0 = ((size_t)b * T * H + h) * D;
-  x.chunk_elems = (size_t)CH * H * D;
-  x.tg0 = (size_t)bh * x.nchunks;
-  x.beta0 = (size_t)b * T * H + h;
+  x.tok_bytes = (uint32_t)a.H * D * 2;
+  x.chunk_elems = (size_t)CH * a.H * D;
+  x.head0 = ((size_t)b * a.T * a.H + h) * D + (size_t)c0 * x.chunk_elems;
+  x.tg0 = (size_t)bh * a.nchunks + c0;
+  x.beta0 = (size_t)b * a.T * a.H + h + (size_t)c0 * CH * a.H;
+  x.vzero = trans;
 
   if (wave >= NW) {                   // ---- loader waves
     const int lw = wave - NW;
     if (lw == 0) {
-      scan_loader<D, NW, 0>(x, B0, B1, Os);
+      scan_loader<D, NW, 0, OUT>(x, B0, B1, Os);
     } else if constexpr (NW > 1) {
       if (lw == 1) {
-        scan_loader<D, NW, 1>(x, B0, B1, Os);
+        scan_loader<D, NW, 1, OUT>(x, B0, B1, Os);
       } else if constexpr (NW > 2) {
-        if (lw == 2) scan_loader<D, NW, 2>(x, B0, B1, Os);
-        else scan_loader<D, NW, 3>(x, B0, B1, Os);
+        if (lw == 2) scan_loader<D, NW, 2, OUT>(x, B0, B1, Os);
+        else scan_loader<D, NW, 3, OUT>(x, B0, B1, Os);
       }
     }
     return;
   }
 
   // ---- compute waves
-  const int n_w = x.n_base + 16 * wave;     // first S row of this wave
+  const int n_w = x.n_base + 16 * wave;     // first row (of S or M) of this wave
+  const size_t slot = (size_t)D * D;
+  const float* sinit = nullptr;
+  if (!trans) {
+    if (a.init_seg) sinit = a.init_seg + ((size_t)bh * a.nsegs + j) * slot;
+    else if (j == 0) sinit = a.state_in;
+  }
+  float* sfin = nullptr;
+  if (trans) {
+    if (a.fin_trans) sfin = a.fin_trans + ((size_t)bh * a.nsegs + j) * slot;
+  } else if (j == a.nsegs - 1) {
+    sfin = a.state_out ? a.state_out + (size_t)bh * slot : nullptr;
+  } else if (a.fin_seg) {
+    sfin = a.fin_seg + ((size_t)bh * a.nsegs + j + 1) * slot;
+  }
 
   f32x4 S[DT];
-  if (state_in) {
-    const float* src = state_in + ((size_t)bh * D + n_w + l16) * D;
+  if (trans) {                        // M starts as the identity: row n is e_n
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[dt][r] = (s_feature(dt, g) + r == n_w + l16) ? 1.f : 0.f;
+  } else if (sinit) {
+    const float* src = sinit + (a.init_seg ? 0 : (size_t)bh * slot) + (size_t)(n_w + l16) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const float4 s4 = *reinterpret_cast<const float4*>(src + s_feature(dt, g));
@@ -920,15 +994,78 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(
   lds_barrier();                      // chunk 0 has landed
 
   for (int c = 0; c < x.nchunks; c += 2) {
-    scan_chunk<D, NW>(x, B0, Pb, Os, S, c);
-    if (c + 1 < x.nchunks) scan_chunk<D, NW>(x, B1, Pb, Os, S, c + 1);
+    scan_chunk<D, NW, OUT>(x, B0, Pb, Os, S, c);
+    if (c + 1 < x.nchunks) scan_chunk<D, NW, OUT>(x, B1, Pb, Os, S, c + 1);
   }
 
-  if (state_out) {
-    float* dst = state_out + ((size_t)bh * D + n_w + l16) * D;
+  if (sfin) {
+    float* dst = sfin + (size_t)(n_w + l16) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<float4*>(dst + s_feature(dt, g)) = make_float4(S[dt][0], S[dt][1], S[dt][2], S[dt][3]);
+  }
+}
+
+// Segment starts from the pass over segments: slot 0 <- state_in (zero when
+// NULL); for j = 1 .. nsegs-2, slot j+1 (holding the end state of segment j
+// from a zero start) <- slot j * M_j + slot j+1, the affine map of the
+// recurrence over segment j applied to its true start.  fp32, one workgroup
+// per (b, h, 16 rows of S): rows of S are independent under the map.  The
+// next transition is fetched into registers while the current step runs and
+// then stored to the other LDS buffer.
+template <int D>
+__global__ __launch_bounds__(512) void gdn_seg_combine_kernel(const float* state_in, float* starts,
+                                                              const float* trans, int nsegs) {
+  constexpr int RB = 16;              // rows per workgroup
+  constexpr int CPT = RB * D / 512;   // columns per thread
+  constexpr int MV = D * D / 4 / 512; // float4 of a transition per thread
+  __shared__ __attribute__((aligned(16))) float Ml[2][D * D];
+  __shared__ __attribute__((aligned(16))) float Sl[RB * D];
+  const int bh = blockIdx.x / (D / RB), r0 = (blockIdx.x % (D / RB)) * RB;
+  const size_t slot = (size_t)D * D;
+  float* base = starts + (size_t)bh * nsegs * slot;
+  const float* tr = trans + (size_t)bh * nsegs * slot;
+  const int tid = threadIdx.x, row = tid / (D / CPT), col = (tid % (D / CPT)) * CPT;
+  for (int i = tid; i < RB * D; i += 512) {
+    const float v = state_in ? state_in[(size_t)bh * slot + (size_t)r0 * D + i] : 0.f;
+    base[(size_t)r0 * D + i] = v;
+  }
+  if (nsegs < 3) return;
+  float4 mr[MV];
+#pragma unroll
+  for (int u = 0; u < MV; ++u) mr[u] = reinterpret_cast<const float4*>(tr + slot)[tid + 512 * u];
+#pragma unroll
+  for (int u = 0; u < MV; ++u) reinterpret_cast<float4*>(Ml[0])[tid + 512 * u] = mr[u];
+  for (int i = tid; i < RB * D / 4; i += 512)
+    reinterpret_cast<float4*>(Sl)[i] = reinterpret_cast<const float4*>(base + slot + (size_t)r0 * D)[i];
+  __syncthreads();
+  for (int jj = 1; jj + 1 < nsegs; ++jj) {
+    const bool more = jj + 2 < nsegs;
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < MV; ++u) mr[u] = reinterpret_cast<const float4*>(tr + (size_t)(jj + 1) * slot)[tid + 512 * u];
+    }
+    const float* Mc = Ml[(jj - 1) & 1];
+    float* cur = base + (size_t)(jj + 1) * slot + (size_t)(r0 + row) * D + col;
+    float acc[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) acc[u] = cur[u];
+#pragma unroll 8
+    for (int m = 0; m < D; ++m) {
+      const float sv = Sl[row * D + m];
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) acc[u] = fmaf(sv, Mc[m * D + col + u], acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) cur[u] = acc[u];
+    __syncthreads();                  // every read of Sl and of this step's M done
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) Sl[row * D + col + u] = acc[u];
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < MV; ++u) reinterpret_cast<float4*>(Ml[jj & 1])[tid + 512 * u] = mr[u];
+    }
+    __syncthreads();
   }
 }
 
@@ -955,40 +1092,123 @@ int gdn_chunk_waves(int B, int H, int D) {
   return heads >= 64 ? 4 : (heads >= 16 ? 2 : 1);
 }
 
-size_t gdn_chunk_workspace(int B, int T, int H) {
-  const size_t nchunks = (size_t)(T + CH - 1) / CH;
-  const size_t tb = (size_t)B * H * nchunks * CH * CH * 2;
-  const size_t gb = (size_t)B * H * nchunks * CH * 4;
-  return ((tb + 255) / 256) * 256 + gb;
+// Segments of the scan over time (1: the plain scan).  With few (b, h) the
+// plain scan occupies few compute units for the whole sequence; splitting the
+// sequence into P segments runs P - 1 of them from known starts (zero state
+// and identity transition, without outputs) in a first pass, combines the
+// segment maps, and then all P with their true start states and outputs:
+// about twice the work on a sequential depth of two segments.  P is picked
+// from the shape alone (a 256-compute-unit budget; workgroups of 64 rows, two
+// per unit in the first pass, whose kernel needs no Q, P or O tiles, one in
+// the second), so that workspace sizes do not depend on the device.
+int gdn_segments(int B, int H, int T, int D) {
+  const long bh = (long)B * H;
+  const long n = (T + CH - 1) / CH;
+  if (n < 64 || D % 64 != 0) return 1;
+  const long cus = 256, nt = D / 64;
+  auto rounds = [](long w, long slots) { return (w + slots - 1) / slots; };
+  long best = rounds(bh * nt, cus) * n;
+  int best_p = 1;
+  for (int P = 2; P <= 8; ++P) {
+    const long L = (n + P - 1) / P;
+    if ((P - 1) * L >= n) continue;                    // empty last segment
+    const long w1 = bh * (nt + 2 * nt * (P - 2));      // first pass: segment 0, then S and M rows
+    const long w2 = bh * nt * P;                       // second pass
+    const long cost = rounds(w1, 2 * cus) * L + rounds(w2, cus) * L + P;   // + launches, combine
+    if (cost < best) {
+      best = cost;
+      best_p = P;
+    }
+  }
+  return best_p;
 }
 
-template <int D, int NW>
-static hipError_t launch_scan(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                              const float* beta, const uint16_t* t_ws, const float* g_ws,
-                              const float* state_in, uint16_t* out, float* state_out, int B, int T,
-                              int H, hipStream_t stream) {
-  constexpr int NT = D / (16 * NW);
-  const int nblk = B * H * NT;
-  gdn_scan_kernel<D, NW><<<nblk, 128 * NW, 0, stream>>>(q, k, v, beta, t_ws, g_ws, state_in, out,
-                                                       state_out, B, T, H);
+namespace {
+struct GdnWs {
+  size_t t, g, starts, trans, total;
+};
+GdnWs gdn_ws_layout(int B, int T, int H, int D) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t nchunks = (size_t)(T + CH - 1) / CH;
+  const size_t bh = (size_t)B * H;
+  const int P = gdn_segments(B, H, T, D);
+  GdnWs w{};
+  w.t = 0;
+  w.g = up(bh * nchunks * CH * CH * 2);
+  w.starts = w.g + up(bh * nchunks * CH * 4);
+  const size_t seg = P > 1 ? bh * P * (size_t)D * D * 4 : 0;
+  w.trans = w.starts + up(seg);
+  w.total = w.trans + up(seg);
+  return w;
+}
+}  // namespace
+
+size_t gdn_chunk_workspace(int B, int T, int H, int D) { return gdn_ws_layout(B, T, H, D).total; }
+
+template <int D, int NW, bool OUT>
+static hipError_t launch_scan(const GdnScanArgs& a, hipStream_t stream) {
+  const long nblk = (long)a.B * a.H * a.nseg_launch * a.tiles;
+  if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (nblk == 0) return hipSuccess;
+  gdn_scan_kernel<D, NW, OUT><<<(unsigned)nblk, 128 * NW, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_scan_nw(const GdnScanArgs& a, int nw, hipStream_t stream) {
+  if (nw == 4) return launch_scan<D, 4, true>(a, stream);
+  if (nw == 2) return launch_scan<D, 2, true>(a, stream);
+  if (nw == 1) return launch_scan<D, 1, true>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t launch_scan_segmented(GdnScanArgs a, int P, float* starts, float* trans,
+                                        hipStream_t stream) {
+  constexpr int NT4 = D / 64;
+  const int nchunks = a.nchunks;
+  a.seg_chunks = (nchunks + P - 1) / P;
+  a.nsegs = P;
+  // pass 1: segments 0 .. P-2 without outputs; segment ends -> starts[j + 1],
+  // transitions -> trans[j]
+  GdnScanArgs p1 = a;
+  p1.out = nullptr;
+  p1.state_out = nullptr;
+  p1.init_seg = nullptr;
+  p1.fin_seg = starts;
+  p1.fin_trans = trans;
+  p1.nseg_launch = P - 1;
+  p1.tiles = 2 * NT4;
+  hipError_t e = launch_scan<D, 4, false>(p1, stream);
+  if (e != hipSuccess) return e;
+  gdn_seg_combine_kernel<D><<<(unsigned)(a.B * a.H * (D / 16)), 512, 0, stream>>>(a.state_in, starts, trans, P);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // pass 2: all segments from their true starts, with outputs
+  GdnScanArgs p2 = a;
+  p2.init_seg = starts;
+  p2.fin_seg = nullptr;
+  p2.fin_trans = nullptr;
+  p2.nseg_launch = P;
+  p2.tiles = NT4;
+  return launch_scan<D, 4, true>(p2, stream);
 }
 
 hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* alpha, const float* beta, const float* state_in,
                             uint16_t* out, float* state_out, int B, int T, int H, int D, int nw,
                             void* workspace, hipStream_t stream, hipEvent_t after_prep) {
-  if (nw <= 0) nw = gdn_chunk_waves(B, H, D);
+  if (D != 64 && D != 128) return hipErrorInvalidValue;
   const int nchunks = (T + CH - 1) / CH;
   const size_t nt = (size_t)B * H * nchunks;
-  uint16_t* t_ws = reinterpret_cast<uint16_t*>(workspace);
-  float* g_ws = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) +
-                                         ((nt * CH * CH * 2 + 255) / 256) * 256);
+  const GdnWs w = gdn_ws_layout(B, T, H, D);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  uint16_t* t_ws = reinterpret_cast<uint16_t*>(wsb + w.t);
+  float* g_ws = reinterpret_cast<float*>(wsb + w.g);
   if (nchunks > 0) {
     if (nt > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (D == 128) gdn_prep_kernel<128><<<(unsigned)nt, 64, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
-    else if (D == 64) gdn_prep_kernel<64><<<(unsigned)nt, 64, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
-    else return hipErrorInvalidValue;
+    else gdn_prep_kernel<64><<<(unsigned)nt, 64, 0, stream>>>(k, alpha, beta, t_ws, g_ws, T, H, nchunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -996,16 +1216,22 @@ hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t
     const hipError_t e = hipEventRecord(after_prep, stream);
     if (e != hipSuccess) return e;
   }
-  if (D == 128) {
-    if (nw == 4) return launch_scan<128, 4>(q, k, v, beta, t_ws, g_ws, state_in, out, state_out, B, T, H, stream);
-    if (nw == 2) return launch_scan<128, 2>(q, k, v, beta, t_ws, g_ws, state_in, out, state_out, B, T, H, stream);
-    if (nw == 1) return launch_scan<128, 1>(q, k, v, beta, t_ws, g_ws, state_in, out, state_out, B, T, H, stream);
-  } else if (D == 64) {
-    if (nw == 4) return launch_scan<64, 4>(q, k, v, beta, t_ws, g_ws, state_in, out, state_out, B, T, H, stream);
-    if (nw == 2) return launch_scan<64, 2>(q, k, v, beta, t_ws, g_ws, state_in, out, state_out, B, T, H, stream);
-    if (nw == 1) return launch_scan<64, 1>(q, k, v, beta, t_ws, g_ws, state_in, out, state_out, B, T, H, stream);
+  GdnScanArgs a;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.t_in = t_ws; a.g_in = g_ws; a.out = out;
+  a.state_in = state_in; a.state_out = state_out;
+  a.init_seg = nullptr; a.fin_seg = nullptr; a.fin_trans = nullptr;
+  a.B = B; a.T = T; a.H = H; a.nchunks = nchunks;
+  a.seg_chunks = nchunks; a.nsegs = 1; a.nseg_launch = 1;
+  const int P = gdn_segments(B, H, T, D);
+  if (P > 1) {
+    float* starts = reinterpret_cast<float*>(wsb + w.starts);
+    float* trans = reinterpret_cast<float*>(wsb + w.trans);
+    return D == 128 ? launch_scan_segmented<128>(a, P, starts, trans, stream)
+                    : launch_scan_segmented<64>(a, P, starts, trans, stream);
   }
-  return hipErrorInvalidValue;
+  if (nw <= 0) nw = gdn_chunk_waves(B, H, D);
+  a.tiles = D / (16 * nw);
+  return D == 128 ? launch_scan_nw<128>(a, nw, stream) : launch_scan_nw<64>(a, nw, stream);
 }
 
 }  // namespace kairos

@@ -131,7 +131,7 @@ struct HltaWs {
 };
 
 size_t gdn_ws_bytes(const kairos_gdn_desc* d) {
-  return d->io == KAIROS_BF16 ? gdn_chunk_workspace(d->B, d->T, d->H) : 0;
+  return d->io == KAIROS_BF16 ? gdn_chunk_workspace(d->B, d->T, d->H, d->dk) : 0;
 }
 
 HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {

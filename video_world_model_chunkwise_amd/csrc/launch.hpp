@@ -74,15 +74,18 @@ hipError_t launch_gdn_f32(const float* q, const float* k, const float* v, const 
                           int B, int T, int H, int D, hipStream_t stream);
 // Chunkwise bf16 gated delta rule: a parallel per-chunk prep kernel (decays,
 // T = (I + A)^{-1}) into `workspace` (gdn_chunk_workspace bytes), then the
-// sequential scan.  nw: waves per scan workgroup (16 nw rows of S per
-// workgroup); <= 0 picks by problem size.
+// sequential scan, split over time into gdn_segments() segments when there
+// are few (b, h) (two scan passes and a combine).  nw: waves per scan
+// workgroup of the unsplit scan (16 nw rows of S per workgroup); <= 0 picks
+// by problem size.
 hipError_t launch_gdn_chunk(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const float* alpha, const float* beta, const float* state_in,
                             uint16_t* out, float* state_out, int B, int T, int H, int D, int nw,
                             void* workspace, hipStream_t stream,
                             hipEvent_t after_prep = nullptr);
 int gdn_chunk_waves(int B, int H, int D);
-size_t gdn_chunk_workspace(int B, int T, int H);
+size_t gdn_chunk_workspace(int B, int T, int H, int D);
+int gdn_segments(int B, int H, int T, int D);
 // Block quantiser: fmt 1 E4M3 (codes [B][T][H][D] bytes), 2 E2M1 (codes
 // [B][T][H][D/2] bytes); scales [B][H][ceil(T/64)]
 hipError_t launch_block_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
