@@ -115,7 +115,9 @@ typedef struct {
  * and k at each branch's positions p = (f div dil) * L + (t mod L), f the
  * absolute frame (SWA: the absolute token index; DSWA: the position in the
  * residue group's sub-sequence); applied before the FP8 quantisation; not on
- * the gated delta rule.  Not with a ring (KAIROS_ERR_UNSUPPORTED).
+ * the gated delta rule.  Positions are absolute, so a key rotated in one call
+ * is the same key in every later call: with a ring, the ring keeps the
+ * rotated keys (see kairos_hlta_fwd).
  * reserved must be 0. */
 typedef struct {
   kairos_gdn_desc g;
@@ -212,7 +214,12 @@ int kairos_context_destroy(kairos_context ctx);
  *   gate_logits  [3][H] fp32 (device memory)
  *   k_ring, v_ring  [B][R][L][H][d] bf16, required iff ring_frames > 0; read
  *                for the frames before the call, then updated in stream order
- *                with the call's last min(R, F) frames
+ *                with the call's last min(R, F) frames.  With rope_base > 0 the
+ *                key ring holds the windowed branches' rotated keys: when
+ *                dilation > 1 it is [2][B][R][L][H][d], part 0 the keys
+ *                rotated at SWA positions, part 1 at DSWA positions (one part
+ *                when dilation == 1); a rollout keeps rope_base, L, window
+ *                and dilation fixed across its calls
  *   out          [B][T][H][d] bf16; state_out as in kairos_gdn_fwd
  *   workspace    >= kairos_hlta_workspace_size bytes
  *   ctx          NULL, or a context of the current device (else

@@ -201,7 +201,11 @@ def test_hlta_validation():
     assert _hlta_call(K.hlta_desc(**base, rope_base=-1.0)) == SHAPE
     assert _hlta_call(K.hlta_desc(**base, rope_base=float("nan"))) == SHAPE
     assert _hlta_call(K.hlta_desc(**base, rope_base=float("inf"))) == SHAPE
-    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, rope_base=1e4)) == UNSUP
+    # RoPE with a ring: accepted (the ring keeps the rotated keys); here the
+    # ring pointers are missing, then the workspace
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, rope_base=1e4)) == NULL
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, rope_base=1e4), k_ring=8 * G,
+                      v_ring=9 * G) == WS
     assert _hlta_call(K.hlta_desc(**base, rope_base=1e4)) == WS
     d3 = K.hlta_desc(**base)
     d3.reserved = 1

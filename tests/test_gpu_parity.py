@@ -309,16 +309,20 @@ def test_hlta_window_stage_wide_scores(qf):
     _assert_close(host(y), y_ref, f"wide-score window stage {qf}")
 
 
-def test_streaming_equals_full_run():
+@pytest.mark.parametrize("rope_base,dil", [(0.0, 2), (1e4, 2), (1e4, 1), (500.0, 3)])
+def test_streaming_equals_full_run(rope_base, dil):
     """Recurrent state passing: frames fed one call at a time with the GDN state
-    carried and a key/value ring equal one full-length oracle run."""
-    B, F, L, H, w, dil = 1, 9, 96, 2, 150, 2
+    carried and a key/value ring equal one full-length oracle run; with RoPE
+    the ring keeps each branch's rotated keys (absolute positions)."""
+    B, F, L, H, w = 1, 9, 96, 2, 150
     T = F * L
-    inp = make_custom(B, T, H, 128, "bf16", seed=55)
+    print(f"stream rope_base={rope_base} dil={dil}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=55 + dil)
     dv = inputs_to_dev(inp)
     R = K.kairos_hlta_ring_frames_required(K.hlta_desc(B, L, H, 128, L, w, dil))
-    k_ring = torch.zeros((B, R, L, H, 128), dtype=torch.bfloat16, device="cuda:0")
-    v_ring = torch.zeros_like(k_ring)
+    k_ring = torch.zeros(K.ring_key_shape(B, R, L, H, 128, dil, rope_base), dtype=torch.bfloat16,
+                         device="cuda:0")
+    v_ring = torch.zeros((B, R, L, H, 128), dtype=torch.bfloat16, device="cuda:0")
     state = torch.zeros((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
     ys = []
     for f in range(F):
@@ -327,10 +331,10 @@ def test_streaming_equals_full_run():
                                  dv["v"][:, sl].contiguous(), dv["alpha"][:, sl].contiguous(),
                                  dv["beta"][:, sl].contiguous(), dv["gates"], L, w, dil,
                                  frame_offset=f, state_in=state, state_out=state, ring_frames=R,
-                                 k_ring=k_ring, v_ring=v_ring)
+                                 k_ring=k_ring, v_ring=v_ring, rope_base=rope_base)
         ys.append(y)
     torch.cuda.synchronize()
     y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
-                               L, w, dil)
+                               L, w, dil, rope_base=rope_base or None)
     _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
     _assert_close(host(state), S_ref, "stream S")

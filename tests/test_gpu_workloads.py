@@ -89,17 +89,21 @@ def test_workload2_layer_sampled():
 
 # ------------------------------------------------------------------ streamed 61 x 1560 rollout
 
-def test_workload3_streaming_sampled():
+@pytest.mark.parametrize("rope_base", [0.0, 1e4])
+def test_workload3_streaming_sampled(rope_base):
     """One call per frame with the GDN state carried and the key/value ring,
-    against a single full-length oracle run."""
+    against a single full-length oracle run; with RoPE (base 10000) the ring
+    keeps both windowed branches' rotated keys."""
     w = WORKLOADS[3]
+    print(f"{w.name} rope_base={rope_base}", flush=True)
     inp = make_inputs(3)
     d = inputs_to_dev(inp)
     L = w.L
     R = w.ring_frames
     assert R == K.kairos_hlta_ring_frames_required(K.hlta_desc(w.B, L, w.H, w.d, L, w.window, w.dilation))
-    k_ring = torch.zeros((w.B, R, L, w.H, w.d), dtype=torch.bfloat16, device="cuda:0")
-    v_ring = torch.zeros_like(k_ring)
+    k_ring = torch.zeros(K.ring_key_shape(w.B, R, L, w.H, w.d, w.dilation, rope_base),
+                         dtype=torch.bfloat16, device="cuda:0")
+    v_ring = torch.zeros((w.B, R, L, w.H, w.d), dtype=torch.bfloat16, device="cuda:0")
     state = torch.zeros((w.B, w.H, w.d, w.d), dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(d["v"])
     for f in range(w.T // L):
@@ -108,13 +112,14 @@ def test_workload3_streaming_sampled():
                           d["v"][:, sl].contiguous(), d["alpha"][:, sl].contiguous(),
                           d["beta"][:, sl].contiguous(), d["gates"], L, w.window, w.dilation,
                           frame_offset=f, state_in=state, state_out=state, ring_frames=R,
-                          k_ring=k_ring, v_ring=v_ring, out=y[:, sl])
+                          k_ring=k_ring, v_ring=v_ring, out=y[:, sl], rope_base=rope_base)
     torch.cuda.synchronize()
     hs = [0, 23]
     rows = _rows(w)
     sub = _sub(inp, [0], hs)
     y_ref, S_ref = oracle.hlta_rows(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"],
-                                    sub["gates"], w.L, w.window, w.dilation, rows)
+                                    sub["gates"], w.L, w.window, w.dilation, rows,
+                                    rope_base=rope_base or None)
     y_got = host(y[:, torch.as_tensor(rows, device=y.device)][:, :, hs])
     _check(y_got, y_ref, f"{w.name} y ({len(rows)} rows x {len(hs)} heads)")
     _check(host(state[:, hs]), S_ref, f"{w.name} final S ({len(hs)} heads)")

@@ -345,7 +345,8 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
     if state_in is not None:
         _need(state_in, "state_in", torch.float32, (B, H, d, d), dev)
     if ring_frames:
-        _need(k_ring, "k_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+        kshape = ring_key_shape(B, ring_frames, L, H, d, dilation, rope_base)
+        _need(k_ring, "k_ring", torch.bfloat16, kshape, dev)
         _need(v_ring, "v_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
     if out is None:
         out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
@@ -364,6 +365,12 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
                                None if ctx is None else ctx.handle, _stream(stream))
     _check(st, "kairos_hlta_fwd")
     return out, state_out
+
+
+def ring_key_shape(B, R, L, H, d, dilation, rope_base=0.0):
+    """Shape of a layer call's key ring: with RoPE and dilation > 1 it keeps
+    both windowed branches' rotated keys, [2, B, R, L, H, d]."""
+    return (2, B, R, L, H, d) if rope_base > 0 and dilation > 1 else (B, R, L, H, d)
 
 
 def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, frame_offset=0,

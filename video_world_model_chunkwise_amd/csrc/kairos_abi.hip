@@ -66,6 +66,11 @@ int qk_format(int window_qk) {
 }
 size_t qk_bytes(int qf, size_t n) { return qf == 2 ? n / 2 : qf == 1 ? n : 2 * n; }
 
+// Parts of a layer call's key ring: with RoPE and dilation > 1 the two
+// windowed branches rotate keys at different positions, and the ring keeps
+// each branch's rotated keys ([2][B][R][L][H][d]); otherwise one part.
+int ring_key_parts(const kairos_hlta_desc* d) { return d->rope_base > 0.f && d->dilation > 1 ? 2 : 1; }
+
 int check_gdn_desc(const kairos_gdn_desc* d) {
   if (!d) return KAIROS_ERR_NULL;
   if (d->B < 1 || d->H < 1 || d->T < 0) return KAIROS_ERR_SHAPE;
@@ -102,7 +107,6 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
     return KAIROS_ERR_SHAPE;
   if (d->window_kind == KAIROS_WINDOW_CENTERED && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   if (!(d->rope_base >= 0.f) || !(d->rope_base < 3.0e38f) || d->reserved != 0) return KAIROS_ERR_SHAPE;
-  if (d->rope_base > 0.f && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
   if (d->window_qk != KAIROS_BF16 && d->window_qk != KAIROS_FP8_E4M3 && d->window_qk != KAIROS_FP4_E2M1)
     return KAIROS_ERR_DTYPE;
   if (d->window_qk != KAIROS_BF16 && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
@@ -516,9 +520,12 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return KAIROS_ERR_ALIGN;
   const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
   const size_t nring = (size_t)desc->g.B * desc->ring_frames * desc->L * desc->g.H * desc->g.dk * 2;
-  if (overlaps(k_ring, nring, v_ring, nring) || overlaps(k_ring, nring, out, 2 * n) ||
-      overlaps(v_ring, nring, out, 2 * n) || overlaps(k_ring, nring, k, 2 * n) ||
-      overlaps(v_ring, nring, v, 2 * n) || overlaps(workspace, ws.total, out, 2 * n) ||
+  const size_t nkring = nring * ring_key_parts(desc);
+  if (overlaps(k_ring, nkring, v_ring, nring) || overlaps(k_ring, nkring, out, 2 * n) ||
+      overlaps(v_ring, nring, out, 2 * n) || overlaps(k_ring, nkring, k, 2 * n) ||
+      overlaps(v_ring, nring, v, 2 * n) || overlaps(k_ring, nkring, q, 2 * n) ||
+      overlaps(workspace, ws.total, k_ring, nkring) || overlaps(workspace, ws.total, v_ring, nring) ||
+      overlaps(workspace, ws.total, out, 2 * n) ||
       overlaps(workspace, ws.total, q, 2 * n) || overlaps(workspace, ws.total, k, 2 * n) ||
       overlaps(workspace, ws.total, v, 2 * n))
     return KAIROS_ERR_ALIAS;
@@ -605,6 +612,7 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     a.k2 = k2;
     a.q_scales2 = qs2;
     a.k_scales2 = ks2;
+    if (desc->ring_frames > 0) a.k_ring2 = (const uint16_t*)((const uint8_t*)k_ring + nring);
   }
   if (so != s && (hipEventRecord(sd->join, so) != hipSuccess || hipStreamWaitEvent(s, sd->join, 0) != hipSuccess))
     return KAIROS_ERR_HIP;
@@ -616,9 +624,14 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     if (e != hipSuccess) return KAIROS_ERR_HIP;
   }
   if (desc->ring_frames > 0) {
-    e = launch_ring_update((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)k_ring,
-                           (uint16_t*)v_ring, B, T / desc->L, desc->L, H, D,
-                           (long)desc->frame_offset, desc->ring_frames, s);
+    // the ring keeps the keys the windowed branches read: with RoPE the
+    // rotated ones (each branch's, at its own positions; absolute positions
+    // make a rotated key valid in every later call)
+    const int F = T / desc->L, R = desc->ring_frames;
+    const long fo = (long)desc->frame_offset;
+    e = launch_ring_copy(v, v_ring, B, F, desc->L, H, 2 * D, fo, R, s);
+    if (e == hipSuccess) e = launch_ring_copy(a.k, k_ring, B, F, desc->L, H, 2 * D, fo, R, s);
+    if (e == hipSuccess && ws.has2) e = launch_ring_copy(a.k2, (uint8_t*)k_ring + nring, B, F, desc->L, H, 2 * D, fo, R, s);
     if (e != hipSuccess) return KAIROS_ERR_HIP;
   }
   return KAIROS_OK;

@@ -21,6 +21,8 @@ struct WinArgs {
   const float* q_scales2;
   const float* k_scales2;
   const uint16_t* k_ring;   // [B][R][L][H][128] bf16 or null
+  const uint16_t* k_ring2;  // keys of the second branch's ring frames when they differ
+                            // from the first branch's (RoPE at the group positions)
   const uint16_t* v_ring;
   const uint16_t* o_gdn;    // bf16 [B][T][H][128] (hybrid only); null: the epilogue leaves
                             // sig(z_swa) o_swa + sig(z_dswa) o_dswa (fp32) in ypart and
@@ -90,9 +92,11 @@ int gdn_segments(int B, int H, int T, int D);
 // [B][T][H][D/2] bytes); scales [B][H][ceil(T/64)]
 hipError_t launch_block_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
                               int D, int fmt, hipStream_t stream);
-hipError_t launch_ring_update(const uint16_t* k, const uint16_t* v, uint16_t* k_ring,
-                              uint16_t* v_ring, int B, int F, int L, int H, int D, long frame_offset,
-                              int R, hipStream_t stream);
+// Ring update of a streamed call: copy the call's last min(R, F) frames of
+// src ([B][F * L][H][row_bytes]) into ring slots (frame_offset + f) mod R of
+// dst ([B][R][L][H][row_bytes]).
+hipError_t launch_ring_copy(const void* src, void* dst, int B, int F, int L, int H, int row_bytes,
+                            long frame_offset, int R, hipStream_t stream);
 // qf: 0 bf16 q, k; 1 E4M3 codes; 2 E2M1 codes (two per byte)
 hipError_t launch_window(const WinArgs& args, int qf, bool hybrid, hipStream_t stream);
 // Workgroups of one window-kernel launch over B x T x H with frames of L tokens.

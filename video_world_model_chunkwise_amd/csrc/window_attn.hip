@@ -268,7 +268,7 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<QF, SHORTL>& ld, const 
   const KeyMap& km = br.km;
   const int p_hi = br.p_hi;
   const uint8_t* kx = reinterpret_cast<const uint8_t*>(br.own_k ? a.k2 : a.k);
-  const uint8_t* kring = reinterpret_cast<const uint8_t*>(a.k_ring);
+  const uint8_t* kring = reinterpret_cast<const uint8_t*>(br.own_k && a.k_ring2 ? a.k_ring2 : a.k_ring);
   const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
   const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
   const int L = km.L;
@@ -321,7 +321,7 @@ __device__ __forceinline__ void win_block_addrs_al(WinLoads<QF, SHORTL>& ld, con
   constexpr int KROW = qk_row_bytes(QF);
   const KeyMap& km = br.km;
   const uint8_t* kx = reinterpret_cast<const uint8_t*>(br.own_k ? a.k2 : a.k);
-  const uint8_t* kring = reinterpret_cast<const uint8_t*>(a.k_ring);
+  const uint8_t* kring = reinterpret_cast<const uint8_t*>(br.own_k && a.k_ring2 ? a.k_ring2 : a.k_ring);
   const uint8_t* vx = reinterpret_cast<const uint8_t*>(a.v);
   const uint8_t* vring = reinterpret_cast<const uint8_t*>(a.v_ring);
   const uint32_t rs_k = (uint32_t)a.H * KROW, rs_v = (uint32_t)a.H * WD * 2;
