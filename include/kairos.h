@@ -76,6 +76,16 @@ typedef enum {
   KAIROS_FP4_E2M1 = 3          /* 4-bit windowed Q/K: OCP FP4 E2M1 codes, two per byte */
 } kairos_dtype;
 
+/* Quantisation blocks of FP8 / 4-bit windowed Q and K (64 tokens each).
+ *   KAIROS_QK_BLOCKS_TOKENS  consecutive 64-token blocks of the call (a block
+ *                            may straddle two frames when 64 does not divide L)
+ *   KAIROS_QK_BLOCKS_FRAMES  64-token blocks restarting at every frame (a
+ *                            frame's last block holds L mod 64 tokens when 64
+ *                            does not divide L); required for a streamed
+ *                            rollout with quantised Q/K, which then quantises
+ *                            exactly as one run over the whole sequence */
+typedef enum { KAIROS_QK_BLOCKS_TOKENS = 0, KAIROS_QK_BLOCKS_FRAMES = 1 } kairos_qk_blocks;
+
 /* Window form of the SWA / DSWA branches (Sec. 2.2.2, Eq. 7).
  *   KAIROS_WINDOW_CAUSAL    query i sees keys i - w < j <= i (w keys with itself)
  *   KAIROS_WINDOW_CENTERED  Eq. 7's centred band as printed: |j - i| <= floor(w / 2)
@@ -100,8 +110,9 @@ typedef struct {
  * (the last frame may be partial when ring_frames == 0).  window w >= 1 in
  * tokens; dilation >= 1.  frame_offset is the absolute index of the call's
  * first frame.  window_qk: KAIROS_BF16, or KAIROS_FP8_E4M3 / KAIROS_FP4_E2M1
- * to quantise the windowed branches' q and k per 64-token block (not with a
- * ring).
+ * to quantise the windowed branches' q and k per 64-token block, the blocks
+ * laid out as qk_blocks says (kairos_qk_blocks; with a ring, quantised Q/K
+ * need KAIROS_QK_BLOCKS_FRAMES, else KAIROS_ERR_UNSUPPORTED).
  * ring_frames R: 0 for a self-contained call (no keys before token 0);
  * otherwise the call continues a rollout: frames frame_offset-R ..
  * frame_offset-1 (those >= 0) are read from the ring, T must be a multiple of
@@ -118,7 +129,8 @@ typedef struct {
  * the gated delta rule.  Positions are absolute, so a key rotated in one call
  * is the same key in every later call: with a ring, the ring keeps the
  * rotated keys (see kairos_hlta_fwd).
- * reserved must be 0. */
+ * qk_blocks: kairos_qk_blocks (0, the former reserved field, keeps the
+ * call's token order). */
 typedef struct {
   kairos_gdn_desc g;
   int32_t L;
@@ -129,7 +141,7 @@ typedef struct {
   int32_t ring_frames;
   int32_t window_kind;         /* kairos_window_kind */
   float rope_base;             /* 0: no RoPE; else > 0, finite (10000 is RoFormer's) */
-  int32_t reserved;            /* must be 0 */
+  int32_t qk_blocks;           /* kairos_qk_blocks */
 } kairos_hlta_desc;
 
 /* Human-readable name of a status code (static storage). */
@@ -146,6 +158,17 @@ int kairos_hlta_workspace_size(const kairos_hlta_desc* desc, size_t* bytes);
 /* Ring frames a streamed (causal) call needs: dilation * ceil((window - 1) / L)
  * (frames whose keys a query can still see), written to *frames. */
 int kairos_hlta_ring_frames_required(const kairos_hlta_desc* desc, int32_t* frames);
+
+/* Bytes of the key ring and of the value ring of kairos_hlta_fwd for this
+ * descriptor (ring_frames R > 0).  Layout: the value ring is [B][R][L][H][d]
+ * bf16.  The key ring is P parts of k_part bytes each, P = 2 with RoPE and
+ * dilation > 1 (part 0 keys rotated at SWA positions, part 1 at DSWA
+ * positions), else 1; a part holds the key rows [B][R][L][H][row] (bf16, or
+ * E4M3 / E2M1 codes of row d or d/2 bytes) and, for quantised keys, their
+ * block scales [B][H][R][ceil(L/64)] fp32 at the next 256-byte boundary after
+ * the rows (k_part then ends at a 256-byte boundary too).  For bf16 keys
+ * without RoPE this is [B][R][L][H][d] bf16, as for the value ring. */
+int kairos_hlta_ring_size(const kairos_hlta_desc* desc, size_t* k_bytes, size_t* v_bytes);
 
 /* Gated delta rule forward (Sec. 2.2.1, Eq. 1-6 canonical form, step 4).
  *   q, k, v      [B][T][H][d]  io type; k L2-normalised per (token, head)
@@ -212,14 +235,14 @@ int kairos_context_destroy(kairos_context ctx);
 /* Hybrid layer forward: y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn
  * per head (Sec. 2.2, Fig. 5 pathways, run as parallel gated branches).
  *   gate_logits  [3][H] fp32 (device memory)
- *   k_ring, v_ring  [B][R][L][H][d] bf16, required iff ring_frames > 0; read
- *                for the frames before the call, then updated in stream order
- *                with the call's last min(R, F) frames.  With rope_base > 0 the
- *                key ring holds the windowed branches' rotated keys: when
- *                dilation > 1 it is [2][B][R][L][H][d], part 0 the keys
- *                rotated at SWA positions, part 1 at DSWA positions (one part
- *                when dilation == 1); a rollout keeps rope_base, L, window
- *                and dilation fixed across its calls
+ *   k_ring, v_ring  required iff ring_frames > 0, laid out and sized as
+ *                kairos_hlta_ring_size says ([B][R][L][H][d] bf16 each for
+ *                bf16 Q/K without RoPE); read for the frames before the call,
+ *                then updated in stream order with the call's last min(R, F)
+ *                frames.  The key ring holds the keys the windowed branches
+ *                read: with RoPE the rotated keys, with quantised Q/K their
+ *                codes and block scales; a rollout keeps L, window, dilation,
+ *                rope_base, window_qk and qk_blocks fixed across its calls
  *   out          [B][T][H][d] bf16; state_out as in kairos_gdn_fwd
  *   workspace    >= kairos_hlta_workspace_size bytes
  *   ctx          NULL, or a context of the current device (else

@@ -38,7 +38,7 @@ from .window import (windowed_attention, windowed_attention_rows, window_brutefo
 from .fp8 import e4m3_round, e4m3_encode, e4m3_decode, fp8_quantize_blocks, E4M3_MAX
 from .fp4 import (e2m1_round, e2m1_encode, e2m1_decode, fp4_pack, fp4_unpack, fp4_quantize_blocks,
                   E2M1_MAX)
-from .hlta import hlta, hlta_rows, sigmoid
+from .hlta import hlta, hlta_rows, sigmoid, quantize_frames
 from .prologue import l2_normalize, gdn_prologue
 from .rope import rope, rope_angles, branch_positions
 
@@ -49,6 +49,6 @@ __all__ = [
     "e4m3_round", "e4m3_encode", "e4m3_decode", "fp8_quantize_blocks", "E4M3_MAX",
     "e2m1_round", "e2m1_encode", "e2m1_decode", "fp4_pack", "fp4_unpack", "fp4_quantize_blocks",
     "E2M1_MAX",
-    "hlta", "hlta_rows", "sigmoid", "l2_normalize", "gdn_prologue",
+    "hlta", "hlta_rows", "sigmoid", "quantize_frames", "l2_normalize", "gdn_prologue",
     "rope", "rope_angles", "branch_positions",
 ]

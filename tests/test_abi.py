@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert K.version() == 200
+    assert K.version() == 201
     assert K.status_string(0) == "ok"
     assert "align" in K.status_string(ALIGN)
     assert K.status_string(12345) == "unknown status"
@@ -194,10 +194,15 @@ def test_hlta_validation():
     assert _hlta_call(K.hlta_desc(**base, ring_frames=3)) == SHAPE
     assert _hlta_call(K.hlta_desc(**base, ring_frames=4)) == NULL          # ring pointers missing
     assert _hlta_call(K.hlta_desc(**base, ring_frames=4, window_qk=K.FP8_E4M3)) == UNSUP
+    # quantised Q/K with a ring need quantisation blocks that restart at every frame
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, window_qk=K.FP8_E4M3,
+                                  qk_blocks=K.QK_BLOCKS_FRAMES)) == NULL
+    assert _hlta_call(K.hlta_desc(**base, ring_frames=4, window_qk=K.FP4_E2M1,
+                                  qk_blocks=K.QK_BLOCKS_FRAMES), k_ring=8 * G, v_ring=9 * G) == WS
     d2 = K.hlta_desc(**base)
     d2.window_kind = 2
     assert _hlta_call(d2) == SHAPE
-    # RoPE: base must be finite and >= 0; not with a ring; reserved must be 0
+    # RoPE: base must be finite and >= 0; qk_blocks must be 0 or 1
     assert _hlta_call(K.hlta_desc(**base, rope_base=-1.0)) == SHAPE
     assert _hlta_call(K.hlta_desc(**base, rope_base=float("nan"))) == SHAPE
     assert _hlta_call(K.hlta_desc(**base, rope_base=float("inf"))) == SHAPE
@@ -208,7 +213,7 @@ def test_hlta_validation():
                       v_ring=9 * G) == WS
     assert _hlta_call(K.hlta_desc(**base, rope_base=1e4)) == WS
     d3 = K.hlta_desc(**base)
-    d3.reserved = 1
+    d3.qk_blocks = 2
     assert _hlta_call(d3) == SHAPE
     # a centred window sees later frames: no ring
     assert _hlta_call(K.hlta_desc(**base, ring_frames=4, centered=True)) == UNSUP
@@ -316,3 +321,37 @@ def test_binding_rejects_bad_tensors_on_cpu():
         K.kairos_gdn_fwd(q, q.float(), q, a, a)
     with pytest.raises(ValueError):
         K.kairos_gdn_fwd(q, q, q, a[:, :4], a)
+
+
+def test_ring_sizes():
+    """kairos_hlta_ring_size: value ring [B][R][L][H][d] bf16; key ring parts
+    of rows (bf16 or codes) plus, for quantised keys, 256-aligned block scales
+    [B][H][R][ceil(L/64)] fp32."""
+    up = lambda x: (x + 255) // 256 * 256
+    B, L, H, d, R = 2, 1560, 3, 128, 4
+    toks = B * R * L * H
+    kw = dict(B=B, T=L, H=H, d=d, L=L, window=1560, dilation=4, ring_frames=R)
+    assert K.kairos_hlta_ring_size(K.hlta_desc(**kw)) == (toks * d * 2, toks * d * 2)
+    assert K.kairos_hlta_ring_size(K.hlta_desc(**kw, rope_base=1e4)) == (2 * toks * d * 2, toks * d * 2)
+    nbf = -(-L // 64)
+    part8 = up(up(toks * d) + B * H * R * nbf * 4)
+    fr = K.QK_BLOCKS_FRAMES
+    assert K.kairos_hlta_ring_size(K.hlta_desc(**kw, window_qk=K.FP8_E4M3, qk_blocks=fr)) == \
+        (part8, toks * d * 2)
+    part4 = up(up(toks * d // 2) + B * H * R * nbf * 4)
+    assert K.kairos_hlta_ring_size(K.hlta_desc(**kw, window_qk=K.FP4_E2M1, qk_blocks=fr,
+                                               rope_base=1e4)) == (2 * part4, toks * d * 2)
+
+
+@host_only
+def test_window_entry_points_refuse_frame_blocks_with_codes():
+    """The standalone window entry points take scales from the token-order
+    quantisers: frame-aligned blocks (and quantised rings) only in the layer."""
+    L = K.lib()
+    cv = lambda x: None if x is None else ctypes.c_void_p(x)
+    d = K.hlta_desc(1, 640, 2, 128, 320, 320, 2, window_qk=K.FP8_E4M3, qk_blocks=K.QK_BLOCKS_FRAMES)
+    assert L.kairos_window_fwd(ctypes.byref(d), 2, cv(G), cv(2 * G), cv(3 * G), cv(4 * G), cv(5 * G),
+                               None, None, cv(6 * G), None) == UNSUP
+    assert L.kairos_hlta_window_fwd(ctypes.byref(d), cv(G), cv(2 * G), cv(3 * G), cv(4 * G), cv(5 * G),
+                                    cv(6 * G), cv(7 * G), None, None, cv(8 * G), cv(9 * G), 1 << 30,
+                                    None) == UNSUP

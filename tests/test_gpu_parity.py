@@ -338,3 +338,57 @@ def test_streaming_equals_full_run(rope_base, dil):
                                L, w, dil, rope_base=rope_base or None)
     _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
     _assert_close(host(state), S_ref, "stream S")
+
+
+# ------------------------------------------------------------------ quantised windows per frame
+
+@pytest.mark.parametrize("fmt,L,F,w,dil,rope", [("fp8", 100, 6, 150, 2, 0.0), ("fp4", 100, 6, 150, 2, 0.0),
+                                                ("fp8", 40, 7, 90, 3, 0.0), ("fp8", 128, 4, 200, 2, 1e4)])
+def test_layer_frame_blocks_matches_oracle(fmt, L, F, w, dil, rope):
+    """Quantisation blocks that restart at every frame (64 does not divide L
+    here, or L < 64), in one call, against the oracle's "frames" reading."""
+    B, H = 1, 2
+    T = F * L
+    print(f"frame blocks {fmt} L{L} F{F} rope={rope}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=70 + L + F)
+    dv = inputs_to_dev(inp)
+    wq = K.FP8_E4M3 if fmt == "fp8" else K.FP4_E2M1
+    y, S = K.kairos_hlta_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dv["gates"], L, w, dil,
+                             window_qk=wq, qk_blocks=K.QK_BLOCKS_FRAMES, rope_base=rope)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, window_qk=fmt, qk_blocks="frames", rope_base=rope or None)
+    _assert_close(host(y), y_ref, "y")
+    _assert_close(host(S), S_ref, "S")
+
+
+@pytest.mark.parametrize("fmt,rope,dil,L", [("fp8", 0.0, 2, 96), ("fp4", 0.0, 2, 96), ("fp8", 1e4, 2, 96),
+                                            ("fp4", 1e4, 3, 50), ("fp8", 0.0, 1, 40)])
+def test_streaming_quantised_equals_full_run(fmt, rope, dil, L):
+    """A rollout with quantised Q/K fed one frame per call (the ring keeps the
+    keys' codes and block scales, rotated first with RoPE) equals one
+    full-length oracle run with per-frame quantisation blocks."""
+    B, F, H, w = 1, 9, 2, int(1.6 * L)
+    T = F * L
+    print(f"stream {fmt} rope={rope} dil={dil} L{L}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=80 + dil + L)
+    dv = inputs_to_dev(inp)
+    wq = K.FP8_E4M3 if fmt == "fp8" else K.FP4_E2M1
+    R = K.kairos_hlta_ring_frames_required(K.hlta_desc(B, L, H, 128, L, w, dil))
+    k_ring, v_ring = K.alloc_rings(B, L, H, 128, w, dil, R, wq, rope, K.QK_BLOCKS_FRAMES)
+    state = torch.zeros((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
+    ys = []
+    for f in range(F):
+        sl = slice(f * L, (f + 1) * L)
+        y, _ = K.kairos_hlta_fwd(dv["q"][:, sl].contiguous(), dv["k"][:, sl].contiguous(),
+                                 dv["v"][:, sl].contiguous(), dv["alpha"][:, sl].contiguous(),
+                                 dv["beta"][:, sl].contiguous(), dv["gates"], L, w, dil,
+                                 frame_offset=f, state_in=state, state_out=state, ring_frames=R,
+                                 k_ring=k_ring, v_ring=v_ring, rope_base=rope, window_qk=wq,
+                                 qk_blocks=K.QK_BLOCKS_FRAMES)
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, window_qk=fmt, qk_blocks="frames", rope_base=rope or None)
+    _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
+    _assert_close(host(state), S_ref, "stream S")

@@ -125,6 +125,41 @@ def test_workload3_streaming_sampled(rope_base):
     _check(host(state[:, hs]), S_ref, f"{w.name} final S ({len(hs)} heads)")
 
 
+@pytest.mark.parametrize("fmt,rope_base", [("fp8", 0.0), ("fp8", 1e4), ("fp4", 0.0)])
+def test_workload3_streaming_quantised_sampled(fmt, rope_base):
+    """The 61 x 1560 rollout with quantised windowed Q/K (per-frame 64-token
+    blocks; 1560 = 24 x 64 + 24), one call per frame, against one full-length
+    oracle run with the same blocks."""
+    w = WORKLOADS[3]
+    print(f"{w.name} {fmt} rope_base={rope_base}", flush=True)
+    inp = make_inputs(3)
+    d = inputs_to_dev(inp)
+    L, R = w.L, w.ring_frames
+    wq = K.FP8_E4M3 if fmt == "fp8" else K.FP4_E2M1
+    k_ring, v_ring = K.alloc_rings(w.B, L, w.H, w.d, w.window, w.dilation, R, wq, rope_base,
+                                   K.QK_BLOCKS_FRAMES)
+    state = torch.zeros((w.B, w.H, w.d, w.d), dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(d["v"])
+    for f in range(w.T // L):
+        sl = slice(f * L, (f + 1) * L)
+        K.kairos_hlta_fwd(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                          d["v"][:, sl].contiguous(), d["alpha"][:, sl].contiguous(),
+                          d["beta"][:, sl].contiguous(), d["gates"], L, w.window, w.dilation,
+                          frame_offset=f, state_in=state, state_out=state, ring_frames=R,
+                          k_ring=k_ring, v_ring=v_ring, out=y[:, sl], rope_base=rope_base,
+                          window_qk=wq, qk_blocks=K.QK_BLOCKS_FRAMES)
+    torch.cuda.synchronize()
+    hs = [0, 23]
+    rows = _rows(w)
+    sub = _sub(inp, [0], hs)
+    y_ref, S_ref = oracle.hlta_rows(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"],
+                                    sub["gates"], w.L, w.window, w.dilation, rows, window_qk=fmt,
+                                    rope_base=rope_base or None, qk_blocks="frames")
+    y_got = host(y[:, torch.as_tensor(rows, device=y.device)][:, :, hs])
+    _check(y_got, y_ref, f"{w.name} {fmt} y ({len(rows)} rows x {len(hs)} heads)")
+    _check(host(state[:, hs]), S_ref, f"{w.name} final S ({len(hs)} heads)")
+
+
 # ------------------------------------------------------------------ B4 H24 16 x 3600 fp8 layer
 
 @pytest.fixture(scope="module")

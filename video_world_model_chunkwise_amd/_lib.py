@@ -6,6 +6,7 @@ import os
 from ctypes import POINTER, byref, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+QK_BLOCKS_TOKENS, QK_BLOCKS_FRAMES = 0, 1
 WINDOW_CAUSAL, WINDOW_CENTERED = 0, 1
 PROLOGUE_NORMALIZE_Q, PROLOGUE_LITERAL_EQ6 = 1, 2
 
@@ -18,7 +19,7 @@ symbols = (
     "kairos_hlta_workspace_size", "kairos_hlta_ring_frames_required", "kairos_gdn_fwd",
     "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
     "kairos_gdn_prologue", "kairos_rope", "kairos_fp4_quantize", "kairos_context_create",
-    "kairos_context_destroy", "kairos_gdn_fwd_noalloc",
+    "kairos_context_destroy", "kairos_gdn_fwd_noalloc", "kairos_hlta_ring_size",
 )
 
 
@@ -36,7 +37,7 @@ class GdnDesc(ctypes.Structure):
 class HltaDesc(ctypes.Structure):
     _fields_ = [("g", GdnDesc), ("L", c_int32), ("window", c_int32), ("dilation", c_int32),
                 ("window_qk", c_int32), ("frame_offset", c_int64), ("ring_frames", c_int32),
-                ("window_kind", c_int32), ("rope_base", c_float), ("reserved", c_int32)]
+                ("window_kind", c_int32), ("rope_base", c_float), ("qk_blocks", c_int32)]
 
 
 _lib = None
@@ -57,6 +58,7 @@ def lib():
         L.kairos_gdn_workspace_size.argtypes = [POINTER(GdnDesc), POINTER(c_size_t)]
         L.kairos_hlta_workspace_size.argtypes = [POINTER(HltaDesc), POINTER(c_size_t)]
         L.kairos_hlta_ring_frames_required.argtypes = [POINTER(HltaDesc), POINTER(c_int32)]
+        L.kairos_hlta_ring_size.argtypes = [POINTER(HltaDesc), POINTER(c_size_t), POINTER(c_size_t)]
         L.kairos_gdn_fwd.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]
         L.kairos_gdn_fwd_noalloc.argtypes = [POINTER(GdnDesc)] + [c_void_p] * 8 + [c_void_p]
         L.kairos_window_fwd.argtypes = [POINTER(HltaDesc), c_int32] + [c_void_p] * 9
@@ -121,9 +123,10 @@ def gdn_desc(B, T, H, d, io=BF16, chunk=64) -> GdnDesc:
 
 
 def hlta_desc(B, T, H, d, L, window, dilation, frame_offset=0, ring_frames=0,
-              window_qk=BF16, io=BF16, centered=False, rope_base=0.0) -> HltaDesc:
+              window_qk=BF16, io=BF16, centered=False, rope_base=0.0,
+              qk_blocks=QK_BLOCKS_TOKENS) -> HltaDesc:
     return HltaDesc(gdn_desc(B, T, H, d, io), L, window, dilation, window_qk, frame_offset,
-                    ring_frames, WINDOW_CENTERED if centered else WINDOW_CAUSAL, rope_base, 0)
+                    ring_frames, WINDOW_CENTERED if centered else WINDOW_CAUSAL, rope_base, qk_blocks)
 
 
 # ------------------------------------------------------------------ torch marshalling
@@ -169,6 +172,13 @@ def kairos_hlta_workspace_size(desc: HltaDesc) -> int:
     n = c_size_t(0)
     _check(lib().kairos_hlta_workspace_size(byref(desc), byref(n)), "kairos_hlta_workspace_size")
     return n.value
+
+
+def kairos_hlta_ring_size(desc: HltaDesc):
+    """(key ring bytes, value ring bytes) of a streamed layer call."""
+    kb, vb = c_size_t(0), c_size_t(0)
+    _check(lib().kairos_hlta_ring_size(byref(desc), byref(kb), byref(vb)), "kairos_hlta_ring_size")
+    return kb.value, vb.value
 
 
 def kairos_hlta_ring_frames_required(desc: HltaDesc) -> int:
@@ -330,7 +340,7 @@ def kairos_window_fwd(q, k, v, L, window, dilation, frame_offset=0, ring_frames=
 def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, frame_offset=0,
                     state_in=None, ring_frames=0, k_ring=None, v_ring=None, window_qk=BF16,
                     out=None, state_out=None, keep_state=True, workspace=None, stream=None,
-                    centered=False, rope_base=0.0, ctx=None):
+                    centered=False, rope_base=0.0, ctx=None, qk_blocks=QK_BLOCKS_TOKENS):
     """Hybrid layer forward.  q, k, v: [B, T, H, 128] bf16; alpha, beta
     [B, T, H] fp32; gate_logits [3, H] fp32; ctx an optional Context (its
     side stream runs part of the call).  Returns (out, state_out)."""
@@ -344,17 +354,21 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
     _need(gate_logits, "gate_logits", torch.float32, (3, H), dev)
     if state_in is not None:
         _need(state_in, "state_in", torch.float32, (B, H, d, d), dev)
+    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, window_qk,
+                     centered=centered, rope_base=rope_base, qk_blocks=qk_blocks)
     if ring_frames:
-        kshape = ring_key_shape(B, ring_frames, L, H, d, dilation, rope_base)
-        _need(k_ring, "k_ring", torch.bfloat16, kshape, dev)
-        _need(v_ring, "v_ring", torch.bfloat16, (B, ring_frames, L, H, d), dev)
+        kb, vb = kairos_hlta_ring_size(desc)
+        for name, t, nb in (("k_ring", k_ring, kb), ("v_ring", v_ring, vb)):
+            if t is None or not t.is_contiguous() or t.device != dev:
+                raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+            if t.numel() * t.element_size() != nb:
+                raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, expected {nb} "
+                                 "(kairos_hlta_ring_size)")
     if out is None:
         out = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
     if state_out is None and keep_state:
         state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-    desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, window_qk,
-                     centered=centered, rope_base=rope_base)
     nws = kairos_hlta_workspace_size(desc)
     ws = workspace if workspace is not None else _workspace(nws, dev)
     if ws is not None and ws.numel() < nws:
@@ -368,9 +382,23 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
 
 
 def ring_key_shape(B, R, L, H, d, dilation, rope_base=0.0):
-    """Shape of a layer call's key ring: with RoPE and dilation > 1 it keeps
-    both windowed branches' rotated keys, [2, B, R, L, H, d]."""
+    """Shape of a bf16 layer call's key ring: with RoPE and dilation > 1 it
+    keeps both windowed branches' rotated keys, [2, B, R, L, H, d]."""
     return (2, B, R, L, H, d) if rope_base > 0 and dilation > 1 else (B, R, L, H, d)
+
+
+def alloc_rings(B, L, H, d, window, dilation, ring_frames, window_qk=BF16, rope_base=0.0,
+                qk_blocks=QK_BLOCKS_TOKENS, device="cuda:0"):
+    """Zeroed key and value rings of a streamed layer call (the key ring as
+    bytes, sized by kairos_hlta_ring_size)."""
+    torch = _torch()
+    desc = hlta_desc(B, L, H, d, L, window, dilation, 0, ring_frames, window_qk,
+                     rope_base=rope_base, qk_blocks=qk_blocks)
+    kb, vb = kairos_hlta_ring_size(desc)
+    k_ring = torch.zeros(kb, dtype=torch.uint8, device=device)
+    v_ring = torch.zeros((B, ring_frames, L, H, d), dtype=torch.bfloat16, device=device)
+    assert v_ring.numel() * 2 == vb
+    return k_ring, v_ring
 
 
 def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, frame_offset=0,

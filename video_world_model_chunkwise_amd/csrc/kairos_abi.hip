@@ -66,10 +66,39 @@ int qk_format(int window_qk) {
 }
 size_t qk_bytes(int qf, size_t n) { return qf == 2 ? n / 2 : qf == 1 ? n : 2 * n; }
 
+// Quantisation blocks per frame when they restart at every frame (0: the
+// call's token order), and scale entries per (b, h) of one quantised tensor.
+int blocks_per_frame(const kairos_hlta_desc* d) {
+  return qk_format(d->window_qk) != 0 && d->qk_blocks == KAIROS_QK_BLOCKS_FRAMES ? (d->L + 63) / 64 : 0;
+}
+size_t scale_blocks(const kairos_hlta_desc* d) {
+  const int nbf = blocks_per_frame(d);
+  return nbf > 0 ? (size_t)((d->g.T + d->L - 1) / d->L) * nbf : (size_t)(d->g.T + 63) / 64;
+}
+
 // Parts of a layer call's key ring: with RoPE and dilation > 1 the two
 // windowed branches rotate keys at different positions, and the ring keeps
 // each branch's rotated keys ([2][B][R][L][H][d]); otherwise one part.
 int ring_key_parts(const kairos_hlta_desc* d) { return d->rope_base > 0.f && d->dilation > 1 ? 2 : 1; }
+
+// Ring layout: V [B][R][L][H][d] bf16; keys in ring_key_parts parts, each the
+// key rows [B][R][L][H][row] (bf16, or codes) and, for quantised keys, their
+// block scales [B][H][R][nbf] fp32 after the rows (256-byte aligned).
+struct RingLayout {
+  size_t v_bytes, k_rows, k_scales, k_part, k_bytes;
+};
+RingLayout ring_layout(const kairos_hlta_desc* d) {
+  RingLayout r{};
+  const int qf = qk_format(d->window_qk);
+  const size_t toks = (size_t)d->g.B * d->ring_frames * d->L * d->g.H;
+  r.v_bytes = toks * d->g.dk * 2;
+  r.k_rows = qk_bytes(qf, toks * d->g.dk);
+  const size_t ns = qf != 0 ? (size_t)d->g.B * d->g.H * d->ring_frames * blocks_per_frame(d) * 4 : 0;
+  r.k_scales = ns > 0 ? align_up(r.k_rows) : 0;
+  r.k_part = ns > 0 ? align_up(r.k_scales + ns) : r.k_rows;
+  r.k_bytes = r.k_part * ring_key_parts(d);
+  return r;
+}
 
 int check_gdn_desc(const kairos_gdn_desc* d) {
   if (!d) return KAIROS_ERR_NULL;
@@ -106,10 +135,14 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
   if (d->window_kind != KAIROS_WINDOW_CAUSAL && d->window_kind != KAIROS_WINDOW_CENTERED)
     return KAIROS_ERR_SHAPE;
   if (d->window_kind == KAIROS_WINDOW_CENTERED && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
-  if (!(d->rope_base >= 0.f) || !(d->rope_base < 3.0e38f) || d->reserved != 0) return KAIROS_ERR_SHAPE;
+  if (!(d->rope_base >= 0.f) || !(d->rope_base < 3.0e38f)) return KAIROS_ERR_SHAPE;
+  if (d->qk_blocks != KAIROS_QK_BLOCKS_TOKENS && d->qk_blocks != KAIROS_QK_BLOCKS_FRAMES) return KAIROS_ERR_SHAPE;
   if (d->window_qk != KAIROS_BF16 && d->window_qk != KAIROS_FP8_E4M3 && d->window_qk != KAIROS_FP4_E2M1)
     return KAIROS_ERR_DTYPE;
-  if (d->window_qk != KAIROS_BF16 && d->ring_frames > 0) return KAIROS_ERR_UNSUPPORTED;
+  // a streamed rollout quantises exactly as one run over the whole sequence
+  // only if no quantisation block mixes two calls' tokens
+  if (d->window_qk != KAIROS_BF16 && d->ring_frames > 0 && d->qk_blocks != KAIROS_QK_BLOCKS_FRAMES)
+    return KAIROS_ERR_UNSUPPORTED;
   // group positions (frame / dil) * L + L and token indices must fit in int32
   const int64_t frames = (d->g.T + d->L - 1) / d->L;
   if ((d->frame_offset + frames + 1) * (int64_t)d->L >= ((int64_t)1 << 30)) return KAIROS_ERR_SHAPE;
@@ -141,11 +174,10 @@ size_t gdn_ws_bytes(const kairos_gdn_desc* d) {
 HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
   HltaWs w{};
   const size_t n = (size_t)d->g.B * d->g.T * d->g.H * d->g.dk;
-  const size_t nblk = (size_t)(d->g.T + 63) / 64;
   const int qf = qk_format(d->window_qk);
   const bool fp8 = qf != 0;
   const bool rope = d->rope_base > 0.f;
-  const size_t nsc = fp8 ? (size_t)d->g.B * d->g.H * nblk * 4 : 0;
+  const size_t nsc = fp8 ? (size_t)d->g.B * d->g.H * scale_blocks(d) * 4 : 0;
   size_t off = 0;
   w.gdn = off;
   off += align_up(gdn_ws_bytes(&d->g));
@@ -191,7 +223,8 @@ hipError_t rope_branch(const kairos_hlta_desc* d, int dil, const void* q, const 
   r.H = d->g.H;
   r.L = d->L;
   r.dil = dil;
-  r.nblk = (d->g.T + 63) / 64;
+  r.nblk = (int)scale_blocks(d);
+  r.nbf = blocks_per_frame(d);
   r.frame_offset = (long)d->frame_offset;
   return launch_rope(r, d->g.dk, (double)d->rope_base, qk_format(d->window_qk), s);
 }
@@ -232,7 +265,8 @@ void fill_win_args(WinArgs& a, const kairos_hlta_desc* d) {
   a.w = d->window;
   a.dil = d->dilation;
   a.R = d->ring_frames;
-  a.nblk = (d->g.T + 63) / 64;
+  a.nblk = (int)scale_blocks(d);
+  a.nbf = blocks_per_frame(d);
   a.centered = d->window_kind == KAIROS_WINDOW_CENTERED ? 1 : 0;
   a.frame_offset = (long)d->frame_offset;
 }
@@ -318,7 +352,7 @@ const char* kairos_status_string(int status) {
   }
 }
 
-int kairos_version(void) { return 200; }
+int kairos_version(void) { return 201; }
 
 int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
   if (!bytes) return KAIROS_ERR_NULL;
@@ -333,6 +367,16 @@ int kairos_hlta_workspace_size(const kairos_hlta_desc* desc, size_t* bytes) {
   const int st = check_hlta_desc(desc, true);
   if (st != KAIROS_OK) return st;
   *bytes = hlta_ws_layout(desc).total;
+  return KAIROS_OK;
+}
+
+int kairos_hlta_ring_size(const kairos_hlta_desc* desc, size_t* k_bytes, size_t* v_bytes) {
+  if (!k_bytes || !v_bytes) return KAIROS_ERR_NULL;
+  const int st = check_hlta_desc(desc, true);
+  if (st != KAIROS_OK) return st;
+  const RingLayout rl = ring_layout(desc);
+  *k_bytes = rl.k_bytes;
+  *v_bytes = rl.v_bytes;
   return KAIROS_OK;
 }
 
@@ -392,6 +436,9 @@ int kairos_window_fwd(const kairos_hlta_desc* desc, int32_t dilation, const void
   const int qf = qk_format(desc->window_qk);
   const bool fp8 = qf != 0;
   if (desc->rope_base != 0.f) return KAIROS_ERR_UNSUPPORTED;
+  // external scales come from the token-order quantisers; a ring of quantised
+  // keys exists only inside the layer call
+  if (fp8 && (desc->qk_blocks != KAIROS_QK_BLOCKS_TOKENS || desc->ring_frames > 0)) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!q || !k || !v || !out) return KAIROS_ERR_NULL;
   if (fp8 && (!q_scales || !k_scales)) return KAIROS_ERR_NULL;
@@ -431,6 +478,7 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
   const int qf = qk_format(desc->window_qk);
   const bool fp8 = qf != 0;
   if (desc->rope_base != 0.f) return KAIROS_ERR_UNSUPPORTED;
+  if (fp8 && (desc->qk_blocks != KAIROS_QK_BLOCKS_TOKENS || desc->ring_frames > 0)) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!q || !k || !v || !o_gdn || !gate_logits || !out) return KAIROS_ERR_NULL;
   if (fp8 && (!q_scales || !k_scales)) return KAIROS_ERR_NULL;
@@ -519,8 +567,8 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return KAIROS_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return KAIROS_ERR_ALIGN;
   const size_t n = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk;
-  const size_t nring = (size_t)desc->g.B * desc->ring_frames * desc->L * desc->g.H * desc->g.dk * 2;
-  const size_t nkring = nring * ring_key_parts(desc);
+  const RingLayout rl = ring_layout(desc);
+  const size_t nring = rl.v_bytes, nkring = rl.k_bytes;
   if (overlaps(k_ring, nkring, v_ring, nring) || overlaps(k_ring, nkring, out, 2 * n) ||
       overlaps(v_ring, nring, out, 2 * n) || overlaps(k_ring, nkring, k, 2 * n) ||
       overlaps(v_ring, nring, v, 2 * n) || overlaps(k_ring, nkring, q, 2 * n) ||
@@ -575,6 +623,7 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   a.v = (const uint16_t*)v;
   a.k_ring = (const uint16_t*)k_ring;
   a.v_ring = (const uint16_t*)v_ring;
+  if (desc->ring_frames > 0 && rl.k_scales > 0) a.ks_ring = (const float*)((const uint8_t*)k_ring + rl.k_scales);
   a.o_gdn = ovl ? nullptr : o_gdn;
   a.gates = gate_logits;
   a.ypart = (float*)(wsb + ws.ypart);
@@ -592,8 +641,10 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     if (rope) {
       e = rope_branch(desc, 1, q, k, q1, k1, qs1, ks1, so);
     } else {
-      e = launch_block_quant((const uint16_t*)q, (uint8_t*)q1, qs1, B, T, H, D, qf, so);
-      if (e == hipSuccess) e = launch_block_quant((const uint16_t*)k, (uint8_t*)k1, ks1, B, T, H, D, qf, so);
+      const int nbf = blocks_per_frame(desc);
+      e = launch_block_quant((const uint16_t*)q, (uint8_t*)q1, qs1, B, T, H, D, qf, so, desc->L, nbf);
+      if (e == hipSuccess)
+        e = launch_block_quant((const uint16_t*)k, (uint8_t*)k1, ks1, B, T, H, D, qf, so, desc->L, nbf);
     }
     if (e != hipSuccess) return KAIROS_ERR_HIP;
     a.q = q1;
@@ -612,7 +663,10 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     a.k2 = k2;
     a.q_scales2 = qs2;
     a.k_scales2 = ks2;
-    if (desc->ring_frames > 0) a.k_ring2 = (const uint16_t*)((const uint8_t*)k_ring + nring);
+    if (desc->ring_frames > 0) {
+      a.k_ring2 = (const uint16_t*)((const uint8_t*)k_ring + rl.k_part);
+      if (rl.k_scales > 0) a.ks_ring2 = (const float*)((const uint8_t*)k_ring + rl.k_part + rl.k_scales);
+    }
   }
   if (so != s && (hipEventRecord(sd->join, so) != hipSuccess || hipStreamWaitEvent(s, sd->join, 0) != hipSuccess))
     return KAIROS_ERR_HIP;
@@ -629,9 +683,16 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
     // make a rotated key valid in every later call)
     const int F = T / desc->L, R = desc->ring_frames;
     const long fo = (long)desc->frame_offset;
+    const int krow = (int)qk_bytes(qf, D);
     e = launch_ring_copy(v, v_ring, B, F, desc->L, H, 2 * D, fo, R, s);
-    if (e == hipSuccess) e = launch_ring_copy(a.k, k_ring, B, F, desc->L, H, 2 * D, fo, R, s);
-    if (e == hipSuccess && ws.has2) e = launch_ring_copy(a.k2, (uint8_t*)k_ring + nring, B, F, desc->L, H, 2 * D, fo, R, s);
+    for (int part = 0; part < ring_key_parts(desc) && e == hipSuccess; ++part) {
+      // part 0: the first branch's keys; part 1: the second branch's own keys
+      uint8_t* dst = (uint8_t*)k_ring + part * rl.k_part;
+      e = launch_ring_copy(part ? a.k2 : a.k, dst, B, F, desc->L, H, krow, fo, R, s);
+      if (e == hipSuccess && rl.k_scales > 0)
+        e = launch_ring_copy_scales(part ? a.k_scales2 : a.k_scales, (float*)(dst + rl.k_scales), B * H, F,
+                                    blocks_per_frame(desc), fo, R, s);
+    }
     if (e != hipSuccess) return KAIROS_ERR_HIP;
   }
   return KAIROS_OK;
@@ -699,6 +760,7 @@ int kairos_rope(const kairos_hlta_desc* desc, int32_t dilation, const void* x, v
   const int qf = qk_format(desc->window_qk);
   const bool fp8 = qf != 0;
   if (!fp8 && scales) return KAIROS_ERR_UNSUPPORTED;
+  if (fp8 && desc->qk_blocks != KAIROS_QK_BLOCKS_TOKENS) return KAIROS_ERR_UNSUPPORTED;
   if (desc->g.T == 0) return KAIROS_OK;
   if (!x || !out || (fp8 && !scales)) return KAIROS_ERR_NULL;
   if (!aligned16(x) || !aligned16(out) || ((uintptr_t)scales & 3u)) return KAIROS_ERR_ALIGN;

@@ -33,6 +33,13 @@ struct WinArgs {
   int B, T, H, L, F, QT;    // F frames in the call (last may be partial), QT query tiles per frame
   int w, dil, R, nblk;
   int centered;             // 0: causal window (i - w, i]; 1: centred |j - i| <= w / 2
+  // quantisation blocks of FP8 / FP4 Q and K: nbf == 0 -> 64-token blocks in
+  // the call's token order (scale of token t at t / 64); nbf > 0 -> blocks
+  // restart at every frame (scale of row m of call frame f at f * nbf + m / 64,
+  // and of a ring frame in slot s at s * nbf + m / 64 of ks_ring [B][H][R][nbf])
+  int nbf;
+  const float* ks_ring;     // key scales of the ring frames (quantised keys in a ring)
+  const float* ks_ring2;    // the same for the second branch's own keys
   long frame_offset;
 };
 
@@ -59,6 +66,8 @@ struct OperandArgs {
   void* out[2];
   float* scales[2];         // FP8 only: [B][H][nblk]
   int nt, B, T, H, L, dil, nblk;
+  int nbf;                  // 0: 64-token blocks in the call's token order; > 0: blocks restart
+                            // at every frame, nbf = ceil(L / 64) per frame (nblk = frames * nbf)
   long frame_offset;
 };
 struct RopeFreqs {
@@ -91,12 +100,15 @@ int gdn_segments(int B, int H, int T, int D);
 // Block quantiser: fmt 1 E4M3 (codes [B][T][H][D] bytes), 2 E2M1 (codes
 // [B][T][H][D/2] bytes); scales [B][H][ceil(T/64)]
 hipError_t launch_block_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
-                              int D, int fmt, hipStream_t stream);
+                              int D, int fmt, hipStream_t stream, int L = 1, int nbf = 0);
 // Ring update of a streamed call: copy the call's last min(R, F) frames of
 // src ([B][F * L][H][row_bytes]) into ring slots (frame_offset + f) mod R of
 // dst ([B][R][L][H][row_bytes]).
 hipError_t launch_ring_copy(const void* src, void* dst, int B, int F, int L, int H, int row_bytes,
                             long frame_offset, int R, hipStream_t stream);
+// The same for per-frame key scales: src [BH][F][nbf] fp32 -> dst [BH][R][nbf].
+hipError_t launch_ring_copy_scales(const float* src, float* dst, int BH, int F, int nbf, long frame_offset,
+                                   int R, hipStream_t stream);
 // qf: 0 bf16 q, k; 1 E4M3 codes; 2 E2M1 codes (two per byte)
 hipError_t launch_window(const WinArgs& args, int qf, bool hybrid, hipStream_t stream);
 // Workgroups of one window-kernel launch over B x T x H with frames of L tokens.

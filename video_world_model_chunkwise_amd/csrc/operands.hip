@@ -127,11 +127,22 @@ __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreq
   const int blk = blockIdx.x, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = 4 * blockIdx.y + wave;
+  // the block's first token and its number of tokens: 64 in token order, or
+  // (frame-aligned blocks) up to the end of the block's frame
+  int t0, tn;
+  if (a.nbf > 0) {
+    const int fb = blk / a.nbf, ib = blk % a.nbf;
+    t0 = fb * a.L + 64 * ib;
+    tn = min(64, min(a.L - 64 * ib, a.T - t0));
+  } else {
+    t0 = blk * 64;
+    tn = min(64, a.T - t0);
+  }
 
   if (ROPE) {
     for (int e = threadIdx.x; e < 64 * NP; e += 256) {
       const int tl = e / NP, i = e % NP;
-      const int t = min(blk * 64 + tl, a.T - 1);
+      const int t = t0 + min(tl, tn - 1);
       const long f = a.frame_offset + t / a.L;
       const long p = (f / a.dil) * a.L + t % a.L;
       const double ang = (double)p * fr.theta[i];
@@ -149,24 +160,24 @@ __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreq
     uint4 v[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int t = blk * 64 + i * TPI + tsub;
-      v[i] = t < a.T ? *reinterpret_cast<const uint4*>(a.x[n] + (((size_t)b * a.T + t) * a.H + h) * D + 8 * sub)
+      const int tl = i * TPI + tsub, t = t0 + tl;
+      v[i] = tl < tn ? *reinterpret_cast<const uint4*>(a.x[n] + (((size_t)b * a.T + t) * a.H + h) * D + 8 * sub)
                      : make_uint4(0u, 0u, 0u, 0u);
     }
     auto csrow = [&](int i) { return cs + (i * TPI + tsub) * CST + 4 * sub; };
     if (OUT == 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int t = blk * 64 + i * TPI + tsub;
+        const int tl = i * TPI + tsub, t = t0 + tl;
         float y[8];
         operand_values<D, ROPE>(v[i], ROPE ? csrow(i) : nullptr, y);
-        if (t < a.T)
+        if (tl < tn)
           *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out[n]) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * sub) =
               make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                          pack_bf16x2(y[6], y[7]));
       }
     } else {
-      float amax = 0.f;                      // rows past T are zero
+      float amax = 0.f;                      // rows past the block are zero
       if (ROPE) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -197,16 +208,16 @@ __global__ __launch_bounds__(256) void qk_operand_kernel(OperandArgs a, RopeFreq
       if (lane == 0) a.scales[n][((size_t)b * a.H + h) * a.nblk + blk] = s;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int t = blk * 64 + i * TPI + tsub;
+        const int tl = i * TPI + tsub, t = t0 + tl;
         float y[8];
         operand_values<D, ROPE>(v[i], ROPE ? csrow(i) : nullptr, y);
         if (OUT == 1) {
           const uint2 c = e4m3_encode8(y, s, r);
-          if (t < a.T)
+          if (tl < tn)
             *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.out[n]) + (((size_t)b * a.T + t) * a.H + h) * D + 8 * sub) = c;
         } else {
           const uint32_t c = e2m1_encode8(y, s, r);
-          if (t < a.T)
+          if (tl < tn)
             *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.out[n]) + ((((size_t)b * a.T + t) * a.H + h) * D + 8 * sub) / 2) = c;
         }
       }
@@ -236,7 +247,7 @@ hipError_t launch_operands(const OperandArgs& a, int D, const RopeFreqs& fr, hip
 }  // namespace
 
 hipError_t launch_block_quant(const uint16_t* x, uint8_t* codes, float* scales, int B, int T, int H,
-                              int D, int fmt, hipStream_t stream) {
+                              int D, int fmt, hipStream_t stream, int L, int nbf) {
   if (T <= 0) return hipSuccess;
   OperandArgs a{};
   a.x[0] = x;
@@ -246,9 +257,10 @@ hipError_t launch_block_quant(const uint16_t* x, uint8_t* codes, float* scales, 
   a.B = B;
   a.T = T;
   a.H = H;
-  a.L = 1;
+  a.L = L > 0 ? L : 1;
   a.dil = 1;
-  a.nblk = (T + 63) / 64;
+  a.nbf = nbf;
+  a.nblk = nbf > 0 ? ((T + a.L - 1) / a.L) * nbf : (T + 63) / 64;
   RopeFreqs fr{};
   return fmt == 2 ? launch_operands<false, 2>(a, D, fr, stream) : launch_operands<false, 1>(a, D, fr, stream);
 }

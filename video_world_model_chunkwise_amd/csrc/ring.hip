@@ -35,4 +35,28 @@ hipError_t launch_ring_copy(const void* src, void* dst, int B, int F, int L, int
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void ring_copy_scales_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                               int BH, int F, int f_first, int nbf, long frame_offset,
+                                                               int R) {
+  const long n = (long)BH * (F - f_first) * nbf;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    const long bh = i / ((long)(F - f_first) * nbf);
+    const int rest = (int)(i % ((long)(F - f_first) * nbf));
+    const int f = f_first + rest / nbf, j = rest % nbf;
+    const int slot = (int)((frame_offset + f) % R);
+    dst[(bh * R + slot) * nbf + j] = src[(bh * F + f) * nbf + j];
+  }
+}
+
+hipError_t launch_ring_copy_scales(const float* src, float* dst, int BH, int F, int nbf, long frame_offset,
+                                   int R, hipStream_t stream) {
+  const int n = F < R ? F : R;
+  if (n <= 0 || nbf <= 0) return hipSuccess;
+  const long total = (long)BH * n * nbf;
+  const long nb = (total + 255) / 256;
+  ring_copy_scales_kernel<<<(unsigned)(nb < 4096 ? nb : 4096), 256, 0, stream>>>(src, dst, BH, F, F - n, nbf,
+                                                                                 frame_offset, R);
+  return hipGetLastError();
+}
+
 }  // namespace kairos

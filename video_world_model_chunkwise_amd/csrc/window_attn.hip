@@ -140,6 +140,18 @@ __device__ __forceinline__ const uint8_t* frame_base(const KeyMap& km, const uin
   return ring + (((size_t)b * km.R + f % km.R) * km.L * (size_t)H + h) * (size_t)row_bytes;
 }
 
+// Key scales of the frame at sub-frame index n of the group, with blocks
+// restarting at every frame (nbf per frame): the call's scales, or for frames
+// before the call the ring's (slot f mod R).  kscale / kring_scale: this
+// branch's arrays; the result indexes by row / 64.
+__device__ __forceinline__ const float* frame_scales(const KeyMap& km, const float* kscale,
+                                                     const float* kring_scale, int b, int h, int H,
+                                                     int nblk, int nbf, int n) {
+  const int f = n * km.dil + km.res;                       // absolute frame
+  if (f >= km.frame_offset) return kscale + ((size_t)b * H + h) * nblk + (size_t)(f - km.frame_offset) * nbf;
+  return kring_scale + (((size_t)b * H + h) * km.R + f % km.R) * nbf;
+}
+
 // Key range of one branch for one query tile, in group-position space.
 struct BranchRange {
   KeyMap km;
@@ -302,10 +314,14 @@ __device__ __forceinline__ void win_block_addrs(WinLoads<QF, SHORTL>& ld, const 
       const uint8_t* base = SHORTL ? frame_base(km, vx, vring, 2 * WD, b, h, a.T, a.H, n) : (n == n0 ? v0 : v1);
       ld.src[j] = base + (size_t)mm * rs_v + col;
     } else {
-      // E4M3 calls have no ring: rows are tokens of the call
-      const int tok = (n * km.dil + km.res - km.frame_offset) * L + mm;
       const float* ksc = br.own_k ? a.k_scales2 : a.k_scales;
-      ld.src[j] = reinterpret_cast<const uint8_t*>(ksc + ((size_t)b * a.H + h) * a.nblk + tok / 64);
+      if (a.nbf > 0) {       // blocks restart at every frame; ring frames have their own scales
+        const float* ksr = br.own_k && a.ks_ring2 ? a.ks_ring2 : a.ks_ring;
+        ld.src[j] = reinterpret_cast<const uint8_t*>(frame_scales(km, ksc, ksr, b, h, a.H, a.nblk, a.nbf, n) + mm / 64);
+      } else {               // token-order blocks (no ring): rows are tokens of the call
+        const int tok = (n * km.dil + km.res - km.frame_offset) * L + mm;
+        ld.src[j] = reinterpret_cast<const uint8_t*>(ksc + ((size_t)b * a.H + h) * a.nblk + tok / 64);
+      }
     }
   }
 }
@@ -547,6 +563,8 @@ __device__ __forceinline__ bool win_block(const WinBuf& cb, const QueryCtx& qc, 
   return failed;
 }
 
+__device__ __forceinline__ bool more_blocks(int jj, int nb) { return jj + 1 < nb; }
+
 // One windowed branch over its key blocks: online softmax into O (unnormalised)
 // with running max m_run and lane-partial sum l_run.
 template <int QF, bool SHORTL>
@@ -562,15 +580,26 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   constexpr bool ALIGN = QF != QF_BF16 && !SHORTL;
   const int L = a.L;
   const KeyMap& km = br.km;
-  const float* kscale = (br.own_k ? a.k_scales2 : a.k_scales) + ((size_t)qc.b * a.H + qc.h) * a.nblk;
-  // token of the call at (sub-frame n, row m), and the end row of the block starting there
+  const float* kscale_all = br.own_k ? a.k_scales2 : a.k_scales;
+  const float* kring_scale = br.own_k && a.ks_ring2 ? a.ks_ring2 : a.ks_ring;
+  const float* kscale = kscale_all + ((size_t)qc.b * a.H + qc.h) * a.nblk;
+  const bool fblk = a.nbf > 0;        // quantisation blocks restart at every frame
+  // token of the call at (sub-frame n, row m), and the end row of the block
+  // starting there (blocks also end at quantisation-block boundaries)
   auto tok_of = [&](int n, int m) { return (n * km.dil + km.res - km.frame_offset) * L + m; };
-  auto blk_end = [&](int n, int m) { return ALIGN ? min(m + BK - (tok_of(n, m) & (BK - 1)), L) : m + BK; };
+  auto blk_end = [&](int n, int m) {
+    return ALIGN ? min(m + BK - ((fblk ? m : tok_of(n, m)) & (BK - 1)), L) : m + BK;
+  };
+  // key scale of the quantisation block holding (sub-frame n, row m)
+  auto scale_at = [&](int n, int m) {
+    return fblk ? frame_scales(km, kscale_all, kring_scale, qc.b, qc.h, a.H, a.nblk, a.nbf, n) + m / BK
+                : kscale + tok_of(n, m) / BK;
+  };
   int n0 = br.p_lo / L, m0 = br.p_lo - (br.p_lo / L) * L;
-  // current block: end row e0 and (ALIGN) token block tb0 with its key scale
+  // current block: end row e0 and (ALIGN) its key scale (tb0 points at it)
   int e0 = blk_end(n0, m0);
-  int tb0 = ALIGN ? tok_of(n0, m0) / BK : 0;
-  float ks0 = ALIGN ? kscale[tb0] : 1.f;
+  const float* tb0 = ALIGN ? scale_at(n0, m0) : nullptr;
+  float ks0 = ALIGN ? *tb0 : 1.f;
   int nb = br.nb;
   if (ALIGN) {
     nb = 0;
@@ -616,7 +645,8 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       // next block's (sub-frame, offset, end, token block) and its loads;
       // inside a frame an aligned block starts at the current end with the
       // next token block
-      int n1 = n0, m1 = e0, e1, tb1 = tb0;
+      int n1 = n0, m1 = e0, e1;
+      const float* tb1 = tb0;
       if (ALIGN) {
         if (e0 < L) {
           e1 = min(e0 + BK, L);
@@ -624,16 +654,15 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
         } else {
           n1 = n0 + 1;
           m1 = 0;
-          const int t = tok_of(n1, 0);
-          e1 = min(BK - (t & (BK - 1)), L);
-          tb1 = t / BK;
+          e1 = blk_end(n1, 0);
+          tb1 = more_blocks(jj, nb) ? scale_at(n1, 0) : tb0;
         }
       } else {
         while (m1 >= L) { m1 -= L; ++n1; }
         e1 = m1 + BK;
       }
       const bool more = jj + 1 < nb;
-      const float ks1 = ALIGN && more ? kscale[tb1] : 1.f;
+      const float ks1 = ALIGN && more ? *tb1 : 1.f;
       int dmax1 = 0;
       if (more) {
         if (ALIGN) {
@@ -779,7 +808,7 @@ __global__ __launch_bounds__(256, (win_wgs_per_cu<QF, SHORTL>())) void win_attn_
           q8f[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
       }
-      qscale = qscales[((size_t)b * a.H + h) * a.nblk + tq / 64];
+      qscale = qscales[((size_t)b * a.H + h) * a.nblk + (a.nbf > 0 ? (size_t)f * a.nbf + qc.mq / 64 : tq / 64)];
     }
     // log2(e) / sqrt(d) (x the query's block scale): scores in exp2 units
     qc.cq = 1.4426950408889634f * 0.08838834764831845f * qscale;
