@@ -129,3 +129,49 @@ def test_window_stage_poisoned_buffers_and_determinism():
     res = _runs(lambda: K.kairos_hlta_window_fwd(dv["q"], dv["k"], dv["v"], o_gdn, dv["gates"], L, w, dil,
                                                  out=out, workspace=ws), [ws, out])
     _assert_same([r[1:] for r in res], ["y"])
+
+
+@pytest.mark.parametrize("fmt,rope", [("bf16", 0.0), ("fp8", 1e4)])
+def test_streaming_resume_from_host(fmt, rope):
+    """Checkpoint and resume of a streamed rollout: after frame 4 the GDN state
+    and both rings (with FP8: key codes and block scales; with RoPE: both
+    branches' rotated keys) go to host memory, every device buffer is freed,
+    fresh buffers are filled from the host copies and the rollout continues.
+    Outputs and final state are bit-identical to an uninterrupted rollout:
+    state, rings and the absolute frame index are the rollout's whole state."""
+    B, F, L, H, w, dil = 1, 9, 96, 2, 150, 2
+    T = F * L
+    print(f"resume {fmt} rope={rope}", flush=True)
+    wq = K.FP8_E4M3 if fmt == "fp8" else K.BF16
+    qb = K.QK_BLOCKS_FRAMES if fmt == "fp8" else K.QK_BLOCKS_TOKENS
+    dv = inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=77))
+    R = K.kairos_hlta_ring_frames_required(K.hlta_desc(B, L, H, 128, L, w, dil))
+
+    def frame(f, state, kr, vr):
+        sl = slice(f * L, (f + 1) * L)
+        y, _ = K.kairos_hlta_fwd(dv["q"][:, sl].contiguous(), dv["k"][:, sl].contiguous(),
+                                 dv["v"][:, sl].contiguous(), dv["alpha"][:, sl].contiguous(),
+                                 dv["beta"][:, sl].contiguous(), dv["gates"], L, w, dil,
+                                 frame_offset=f, state_in=state, state_out=state, ring_frames=R,
+                                 k_ring=kr, v_ring=vr, rope_base=rope, window_qk=wq, qk_blocks=qb)
+        return y
+
+    kr, vr = K.alloc_rings(B, L, H, 128, w, dil, R, wq, rope, qb)
+    state = torch.zeros((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
+    ref = [frame(f, state, kr, vr).clone() for f in range(F)]
+    torch.cuda.synchronize()
+    ref_state = state.clone()
+
+    kr, vr = K.alloc_rings(B, L, H, 128, w, dil, R, wq, rope, qb)
+    state = torch.zeros((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
+    got = [frame(f, state, kr, vr).clone() for f in range(5)]
+    torch.cuda.synchronize()
+    saved = [t.to("cpu", copy=True) for t in (state, kr, vr)]     # host copies
+    del state, kr, vr
+    torch.cuda.empty_cache()
+    state, kr, vr = (t.to("cuda:0", copy=True) for t in saved)
+    got += [frame(f, state, kr, vr).clone() for f in range(5, F)]
+    torch.cuda.synchronize()
+    for f in range(F):
+        assert torch.equal(got[f], ref[f]), f"frame {f} differs after the resume"
+    assert torch.equal(state, ref_state)

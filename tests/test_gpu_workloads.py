@@ -202,3 +202,93 @@ def test_workload4_layer_fp8_sampled(w4):
     y_got = host(y[bs][:, torch.as_tensor(rows, device=y.device)][:, :, hs])
     _check(y_got, y_ref, f"{w.name} y ({len(rows)} rows x {len(bs)}x{len(hs)} heads)")
     _check(host(S[bs][:, hs]), S_ref, f"{w.name} S")
+
+
+# ------------------------------------------------------------------ dense full-size checks
+
+def _synthetic_o_gdn(w, seed):
+    """A seeded stand-in for the GDN branch output (an input of the window
+    stage): N(0, 1) rounded to bf16; bf16 bit patterns (host) and the device
+    tensor."""
+    from workloads import to_bf16_bits
+    bits = to_bf16_bits(np.random.default_rng(seed).standard_normal((w.B, w.T, w.H, w.d), dtype=np.float32))
+    return bits, dev_bf16(bits)
+
+
+def _widen(bits):
+    from workloads import bf16_bits_to_f32
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def test_workload2_window_stage_dense():
+    """All 24 heads, every query row of one whole frame of each DSWA residue
+    group (frames 8-11: 6240 rows), window stage of the 21 x 1560 layer
+    against the oracle."""
+    w = WORKLOADS[2]
+    inp = make_inputs(2)
+    d = inputs_to_dev(inp)
+    o_bits, o_dev = _synthetic_o_gdn(w, 202)
+    y = torch.full_like(d["v"], float("nan"))
+    K.kairos_hlta_window_fwd(d["q"], d["k"], d["v"], o_dev, d["gates"], w.L, w.window, w.dilation, out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y.float()).all()), "unwritten (NaN) outputs"
+    rows = np.arange(8 * w.L, 12 * w.L)
+    y_ref, _ = oracle.hlta_rows(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                                w.L, w.window, w.dilation, rows, o_gdn=_widen(o_bits))
+    y_got = host(y[:, torch.as_tensor(rows, device=y.device)])
+    _check(y_got, y_ref, f"{w.name} window stage, {len(rows)} rows x {w.H} heads")
+
+
+def test_workload4_window_stage_dense_fp8():
+    """FP8 window stage of the B4 H24 16 x 3600 layer with NaN-filled outputs:
+    every output finite, and all 24 heads of batch row 1 against the oracle on
+    the first and last 300 query rows of frames 8-11 (one frame of each DSWA
+    residue group; frame starts and each frame's ragged 16-row last tile)."""
+    w = WORKLOADS[4]
+    inp = make_inputs(4)
+    d = inputs_to_dev(inp)
+    o_bits, o_dev = _synthetic_o_gdn(w, 404)
+    cq, sq = K.kairos_fp8_quantize(d["q"])
+    ck, sk = K.kairos_fp8_quantize(d["k"])
+    y = torch.full_like(d["v"], float("nan"))
+    K.kairos_hlta_window_fwd(cq, ck, d["v"], o_dev, d["gates"], w.L, w.window, w.dilation, q_scales=sq,
+                             k_scales=sk, out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y.float()).all()), "unwritten (NaN) outputs"
+    del cq, ck, d
+    b = 1
+    Tp = 12 * w.L                                         # causal: later tokens are not needed
+    sub = {k: inp[k][[b]][:, :Tp] for k in ("q", "k", "v", "alpha", "beta")}
+    rows = np.concatenate([np.r_[f * w.L:f * w.L + 300, (f + 1) * w.L - 300:(f + 1) * w.L]
+                           for f in range(8, 12)])
+    y_ref, _ = oracle.hlta_rows(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"], inp["gates"],
+                                w.L, w.window, w.dilation, rows, window_qk="fp8",
+                                o_gdn=_widen(o_bits[[b]][:, :Tp]))
+    y_got = host(y[[b]][:, torch.as_tensor(rows, device=y.device)])
+    _check(y_got, y_ref, f"{w.name} fp8 window stage, {len(rows)} rows x {w.H} heads")
+
+
+def test_workload4_gdn_decay_closed_form_all_heads():
+    """Every (b, h) of the B4 H24 T57600 gated delta rule at full size, by the
+    beta = 0 closed form: S_t = gamma_t S_0 and o_t = gamma_t S_0 q_t with
+    gamma_t = prod_{s <= t} alpha_s (alpha near 1 so gamma stays O(1) over
+    57600 tokens).  Checks every head's and chunk's mapping of the prep and
+    scan kernels on all outputs of 8 chunks per head and every 7th token."""
+    w = WORKLOADS[4]
+    inp = make_inputs(4)
+    rng = np.random.default_rng(44)
+    alpha = (1.0 - 1e-5 * rng.uniform(0.5, 1.5, (w.B, w.T, w.H))).astype(np.float32)
+    beta = np.zeros((w.B, w.T, w.H), np.float32)
+    S0 = (0.1 * rng.standard_normal((w.B, w.H, w.d, w.d))).astype(np.float32)
+    d = inputs_to_dev(inp)
+    out, S = K.kairos_gdn_fwd(d["q"], d["k"], d["v"], dev_f32(alpha), dev_f32(beta), dev_f32(S0))
+    torch.cuda.synchronize()
+    gamma = np.cumprod(alpha.astype(np.float64), axis=1)                    # [B, T, H]
+    toks = np.unique(np.concatenate([np.arange(0, w.T, 7)] +
+                                    [np.arange(c * 64, c * 64 + 64) for c in (0, 1, 63, 64, 450, 451, 898, 899)]))
+    qs = inp["q"][:, toks].astype(np.float64).transpose(0, 2, 1, 3)          # [B, H, n, d]
+    o_ref = np.matmul(qs, S0.astype(np.float64).transpose(0, 1, 3, 2))       # (S0 q_t) per token
+    o_ref = o_ref.transpose(0, 2, 1, 3) * gamma[:, toks][..., None]          # [B, n, H, d]
+    _check(host(out[:, torch.as_tensor(toks, device=out.device)]), o_ref,
+           f"{w.name} beta=0 o ({len(toks)} tokens x {w.B * w.H} heads)")
+    _check(host(S), gamma[:, -1][:, :, None, None] * S0.astype(np.float64), f"{w.name} beta=0 S (all heads)")

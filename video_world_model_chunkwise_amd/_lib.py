@@ -11,7 +11,9 @@ WINDOW_CAUSAL, WINDOW_CENTERED = 0, 1
 PROLOGUE_NORMALIZE_Q, PROLOGUE_LITERAL_EQ6 = 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libkairos.so")
+# another build of this same library (the host-sanitized one the ABI tests
+# load) may be named in KAIROS_LIB; there is no other fallback
+lib_path = os.environ.get("KAIROS_LIB") or os.path.join(_HERE, "libkairos.so")
 
 # every symbol include/kairos.h declares
 symbols = (

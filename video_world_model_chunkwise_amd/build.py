@@ -49,8 +49,25 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+# host-only sanitizers (the device code is built as usual): AddressSanitizer
+# and UndefinedBehaviorSanitizer on the C ABI's validation and launch code
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime the sanitized library needs
+    preloaded (it must be the process's first ASan-aware library)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under /opt/rocm/lib/llvm")
+    return hits[-1]
+
+
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
     hipcc = _hipcc()
+    extra_flags = SANITIZE if sanitize else []
     with tempfile.TemporaryDirectory(prefix="kairos_build_") as tmp:
         objs = []
         jobs = []
@@ -58,16 +75,16 @@ def build(verbose: bool = False) -> str:
             for src in SOURCES:
                 obj = os.path.join(tmp, src.replace(".hip", ".o"))
                 objs.append(obj)
-                cmd = [hipcc, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+                cmd = [hipcc, *CFLAGS, *extra_flags, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
                 jobs.append(ex.submit(_run, cmd))
             for j in jobs:
-                out = j.result()
-                if verbose and out.strip():
-                    print(out)
-        tmp_lib = LIB + ".tmp"
-        _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib])
-        os.replace(tmp_lib, LIB)
-    return LIB
+                o = j.result()
+                if verbose and o.strip():
+                    print(o)
+        tmp_lib = out + ".tmp"
+        _run([hipcc, "-shared", f"--offload-arch={ARCH}", *extra_flags, *objs, "-o", tmp_lib])
+        os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":
