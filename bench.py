@@ -28,6 +28,12 @@ METRIC = "GDN / hybrid temporal-attention fwd tokens/s + % roofline, H=24 d=128,
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
+# transcendental (v_exp_f32) rate: quarter of the 16 fp32 lanes per clock of
+# a SIMD, 256 CU x 4 SIMD x 4 lanes x 2.4 GHz
+PEAK_EXP_PER_S = 256 * 4 * 4 * 2.4e9
+# one wave64 VALU instruction issues over 4 clocks (16 lanes per clock)
+VALU_ISSUE_CLK = 4
+SIMDS, CLOCK_HZ = 1024, 2.4e9
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
@@ -63,6 +69,18 @@ def window_pairs(T, L, w, dil, frame_offset=0, centered=False):
     return total
 
 
+def read_counter_summary(name):
+    """key: value lines of a committed counter summary under profiles/."""
+    out = {}
+    path = os.path.join(ROOT, "profiles", name)
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                out[key.strip()] = val.strip()
+    return out
+
+
 def src_sha(*names):
     h = hashlib.sha256()
     for n in names:
@@ -73,61 +91,101 @@ def src_sha(*names):
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(w):
-    """The oracle (untuned) on a bounded sample of the workload; tokens/s of
-    the whole layer extrapolated from per-token costs of its three parts."""
+def _oracle_costs(w, Tg, rows_n, Hs, seed_off):
+    """Oracle seconds per token of a layer workload's three parts (a token of
+    one batch row, all heads: the workload takes B T times that), from a
+    bounded sample: the gated delta rule over Tg tokens x all heads, the
+    block quantiser (FP8 workloads) and both windowed branches for rows_n
+    query rows of the last frame of a 2 dil + 1 frame prefix x Hs heads."""
     import numpy as np
     import oracle
     from workloads import make_custom
+    inp = make_custom(1, Tg, w.H, w.d, "bf16", seed=w.seed + seed_off)
+    t0 = time.perf_counter()
+    oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
+    c_gdn = (time.perf_counter() - t0) / Tg                       # per token (one batch row, all heads)
+    if not w.L:
+        return {"gdn": c_gdn}
+    F = 2 * w.dilation + 1
+    inp = make_custom(1, F * w.L, Hs, w.d, "bf16", seed=w.seed + seed_off + 1)
+    rows = np.arange((F - 1) * w.L, (F - 1) * w.L + rows_n)
+    q, k = inp["q"], inp["k"]
+    c_quant = 0.0
+    if w.window_qk == "fp8":
+        t0 = time.perf_counter()
+        _, _, q = oracle.fp8_quantize_blocks(q)
+        _, _, k = oracle.fp8_quantize_blocks(k)
+        c_quant = (time.perf_counter() - t0) / (F * w.L) * (w.H / Hs)
+    t0 = time.perf_counter()
+    oracle.windowed_attention_rows(q, k, inp["v"], rows, w.L, w.window, 1)
+    oracle.windowed_attention_rows(q, k, inp["v"], rows, w.L, w.window, w.dilation)
+    c_win = (time.perf_counter() - t0) / len(rows) * (w.H / Hs)
+    return {"gdn": c_gdn, "fp8_quant": c_quant, "windows": c_win}
+
+
+def cpu_baseline(w, WORKLOADS):
+    """The oracle (untuned) on bounded samples; tokens/s of the benchmark
+    workload's whole layer extrapolated from per-token costs of its three
+    parts, and the same figure for every workload."""
+    import oracle
+    from workloads import make_inputs
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         blas_threads = 1
     t_all = time.perf_counter()
-    # (1) gated delta rule: all H heads of one batch row, Tg tokens
-    Tg = 2048
-    inp = make_custom(1, Tg, w.H, w.d, "bf16", seed=w.seed + 7)
-    t0 = time.perf_counter()
-    oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
-    c_gdn = (time.perf_counter() - t0) / Tg                  # s per token (all heads)
+    Tg, rows_n, Hs = 2048, 384, 4
+    c = _oracle_costs(w, Tg, rows_n, Hs, 7)
+    per_token = sum(c.values())
     # the same loop on one BLAS thread, over a quarter of the tokens
     c_gdn_1 = None
     try:
         from threadpoolctl import threadpool_limits
+        from workloads import make_custom
         T1 = Tg // 4
+        inp = make_custom(1, T1, w.H, w.d, "bf16", seed=w.seed + 9)
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            oracle.gdn_recurrent(inp["q"][:, :T1], inp["k"][:, :T1], inp["v"][:, :T1],
-                                 inp["alpha"][:, :T1], inp["beta"][:, :T1])
+            oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
             c_gdn_1 = (time.perf_counter() - t0) / T1
     except Exception:
         pass
-    # (2) windowed branches: rows of the last frame of a 2*dil+1-frame prefix, Hs heads
-    Hs = 4
-    F = 2 * w.dilation + 1
-    inp = make_custom(1, F * w.L, Hs, w.d, "bf16", seed=w.seed + 8)
-    rows = np.arange((F - 1) * w.L, (F - 1) * w.L + 384)
-    q, k = inp["q"], inp["k"]
+    # every workload: workload 0 whole; the others by the sampled per-token costs
+    per_workload = {}
+    w0 = WORKLOADS[0]
+    inp = make_inputs(0)
     t0 = time.perf_counter()
-    if w.window_qk == "fp8":
-        _, _, q = oracle.fp8_quantize_blocks(q)
-        _, _, k = oracle.fp8_quantize_blocks(k)
-    c_quant = (time.perf_counter() - t0) / (F * w.L) * (w.H / Hs)   # s per token
-    t0 = time.perf_counter()
-    oracle.windowed_attention_rows(q, k, inp["v"], rows, w.L, w.window, 1)
-    oracle.windowed_attention_rows(q, k, inp["v"], rows, w.L, w.window, w.dilation)
-    c_win = (time.perf_counter() - t0) / len(rows) * (w.H / Hs)      # s per token (all heads)
-    per_token = c_gdn + c_quant + c_win
+    oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])
+    dt = time.perf_counter() - t0
+    per_workload[w0.name] = {"seconds": round(dt, 4), "tokens_per_s": round(w0.B * w0.T / dt, 1),
+                             "sample": "whole workload"}
+    for wi in (1, 2, 3):
+        ww = WORKLOADS[wi]
+        cw = _oracle_costs(ww, 512, 128, 2, 11 + wi)
+        pt = sum(cw.values())
+        per_workload[ww.name] = {"tokens_per_s": round(1.0 / pt, 1), "est_seconds": round(pt * ww.B * ww.T, 1),
+                                 "per_token_s": cw,
+                                 "sample": "GDN 512 tokens x all heads" + ("" if not ww.L else
+                                           "; windows 128 rows x 2 heads, scaled")}
+    per_workload[w.name] = {"tokens_per_s": round(1.0 / per_token, 1), "est_seconds": round(per_token * w.B * w.T, 1),
+                            "per_token_s": c, "sample": "the headline sample"}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {
         "value": 1.0 / per_token, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+        "threads": {"blas_threads": int(blas_threads), "logical_cpus": os.cpu_count(),
+                    "affinity_cpus": affinity},
         "sample": (f"numpy fp64 oracle: gated delta rule over {Tg} tokens x {w.H} heads; "
-                   f"E4M3 block quantiser over {F * w.L} tokens x {Hs} heads; SWA+DSWA for "
-                   f"{len(rows)} query rows (window {w.window}, dilation {w.dilation}) x {Hs} heads; "
-                   f"per-token costs summed and scaled to {w.H} heads"),
+                   f"E4M3 block quantiser over {(2 * w.dilation + 1) * w.L} tokens x {Hs} heads; SWA+DSWA for "
+                   f"{rows_n} query rows (window {w.window}, dilation {w.dilation}) x {Hs} heads; "
+                   f"per-token costs summed and scaled to {w.B} x {w.H} heads"),
         "seconds": round(time.perf_counter() - t_all, 2),
-        "per_token_s": {"gdn": c_gdn, "fp8_quant": c_quant, "windows": c_win},
+        "per_token_s": c,
         "gdn_tokens_per_s_1_thread": (round(1.0 / c_gdn_1, 1) if c_gdn_1 else None),
+        "per_workload": per_workload,
         "host": host_description(),
     }
 
@@ -146,6 +204,38 @@ def host_description():
 
 
 # ------------------------------------------------------------------ GPU timing helpers
+
+def time_stats(ms):
+    """avg / min / median / p10 / p90 of a list of times (nearest-rank
+    percentiles)."""
+    ms = sorted(ms)
+    n = len(ms)
+    pick = lambda p: ms[min(n - 1, max(0, int(math.ceil(p * n)) - 1))]
+    return {"avg_ms": sum(ms) / n, "min_ms": ms[0], "median_ms": pick(0.5), "p10_ms": pick(0.1),
+            "p90_ms": pick(0.9), "n": n}
+
+
+def versions(torch):
+    """Software and device the numbers were taken with."""
+    v = {"torch": torch.__version__, "hip_runtime": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            v["rocm"] = f.read().strip()
+    except OSError:
+        v["rocm"] = None
+    try:
+        with open("/sys/module/amdgpu/version") as f:
+            v["amdgpu_driver"] = f.read().strip()
+    except OSError:
+        v["amdgpu_driver"] = None
+    try:
+        p = torch.cuda.get_device_properties(0)
+        v["device"] = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+                       "compute_units": p.multi_processor_count, "memory_GB": round(p.total_memory / 1e9, 1)}
+    except Exception:
+        v["device"] = None
+    return v
+
 
 class StageTimer:
     """HIP events recorded on the current (launch) stream around each call."""
@@ -167,9 +257,18 @@ class StageTimer:
             fn()
             b.record()
         torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in ev)
-        self.acc[name] = {"avg_ms": sum(ms) / len(ms), "min_ms": ms[0], "median_ms": ms[len(ms) // 2]}
+        self.acc[name] = time_stats([a.elapsed_time(b) for a, b in ev])
         return self.acc[name]["avg_ms"]
+
+
+def gdn_segments_of(K, w):
+    """Segments of the time-split scan for a shape, read back from the GDN
+    workspace size (two D x D fp32 slots per (b, h) and segment when split)."""
+    up = lambda x: (x + 255) // 256 * 256
+    n = -(-w.T // 64)
+    base = up(w.B * w.H * n * 64 * 64 * 2) + up(w.B * w.H * n * 64 * 4)
+    extra = K.kairos_gdn_workspace_size(K.gdn_desc(w.B, w.T, w.H, w.d)) - base
+    return max(1, extra // (2 * w.B * w.H * w.d * w.d * 4))
 
 
 def layer_step_fn(K, d, w, bufs, fp8, ctx=None):
@@ -200,6 +299,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for memory counters)")
+    ap.add_argument("--gdn-workload", type=int, default=None,
+                    help="only time kairos_gdn_fwd on this workload index (prints its own JSON line)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -214,6 +315,9 @@ def main():
     K.lib()                                         # fail loudly if the library is missing
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if args.gdn_workload is not None:
+        gdn_only(K, torch, WORKLOADS[args.gdn_workload], make_device_inputs, args)
+        return
     w = WORKLOADS[4]                                # B4 H24 d128, 16 x 3600 tokens, FP8 windows
     fp8 = w.window_qk == "fp8"
     d = make_device_inputs(w, dev)
@@ -225,12 +329,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for a_ev, b_ev in evs:
+        a_ev.record()
         step()
+        b_ev.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / max(args.steps, 1)
+    step_stats = time_stats([a_ev.elapsed_time(b_ev) for a_ev, b_ev in evs]) if evs else None
     tokens = w.B * w.T
     value = tokens / (ms_per_step / 1e3)
     print(f"[bench] layer: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
@@ -340,16 +449,46 @@ def main():
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 cnt[key.strip()] = val.strip()
-    if cnt.get("win_attn_kernel.source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
+    win_fresh = cnt.get("win_attn_kernel.source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp")
+    if win_fresh:
         roofline["traffic"] = float(cnt["win_attn_kernel.traffic_bytes_per_launch"])
+    # the second ceiling of the window kernel: one exponential per (query, key)
+    # pair at the transcendental rate, and (from the committed SQ counters,
+    # while they match the kernel's source) the VALU and MFMA issue times
+    exps = pairs * w.B * w.H
+    roofline["exp_ceiling"] = {"exps_per_launch": exps, "peak_per_s": PEAK_EXP_PER_S,
+                               "bound_ms": round(exps / PEAK_EXP_PER_S * 1e3, 4),
+                               "frac": round(exps / PEAK_EXP_PER_S * 1e3 / t_win, 4)}
+    sq = read_counter_summary("hlta_fp8_B4H24F16L3600_sq_counters.txt")
+    if sq.get("win_attn_kernel.source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
+        v = float(sq["win_attn_kernel.SQ_INSTS_VALU"])
+        m = float(sq["win_attn_kernel.SQ_VALU_MFMA_BUSY_CYCLES"])
+        roofline["counters"] = {
+            "valu_insts_per_launch": v, "mfma_insts_per_launch": float(sq["win_attn_kernel.SQ_INSTS_MFMA"]),
+            "valu_issue_ms": round(v * VALU_ISSUE_CLK / SIMDS / CLOCK_HZ * 1e3, 4),
+            "mfma_busy_ms": round(m / SIMDS / CLOCK_HZ * 1e3, 4),
+            "source": "profiles/hlta_fp8_B4H24F16L3600_sq_counters.txt"}
     pro_fresh = cnt.get("gdn_prologue_kernel.source_sha") == src_sha("prologue.hip", "common.hpp",
                                                                     "launch.hpp")
 
     gdn_tok_heads = w.B * w.T * w.H
     gdn_bytes = gdn_tok_heads * GDN_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * w.d * w.d * 4
     gdn_flops = gdn_tok_heads * gdn_flops_per_token_head(w.d)
+    # the gated delta rule's own roofline (HBM-bound): its launch sequence
+    # (prep + scan) timed as one stage, algorithmic bytes over that time
+    gdn_ach = gdn_bytes / (t_gdn / 1e3) / 1e9
+    roofline_gdn = {"bound": "hbm", "achieved": round(gdn_ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gdn_ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "kernel": "gdn_prep_kernel + gdn_scan_kernel (one kairos_gdn_fwd)",
+                    "algorithmic_bytes_per_launch": gdn_bytes, "avg_launch_ms": round(t_gdn, 4),
+                    "median_ms": round(st.acc["gdn_chunk"]["median_ms"], 4)}
+    if cnt.get("gdn_scan_kernel.source_sha") == src_sha("gdn.hip", "common.hpp", "launch.hpp") \
+            and "gdn.traffic_bytes_per_launch" in cnt:
+        roofline_gdn["traffic"] = float(cnt["gdn.traffic_bytes_per_launch"])
     breakdown = {
         "stages_ms": {k: round(v["avg_ms"], 4) for k, v in st.acc.items()},
+        "stages_stats_ms": {k: {q: round(x, 4) for q, x in v.items() if q != "avg_ms"}
+                            for k, v in st.acc.items()},
         "gdn_branch": {
             "ms": round(t_gdn, 4), "tokens_per_s": round(tokens / (t_gdn / 1e3)),
             "alg_GB_per_s": round(gdn_bytes / (t_gdn / 1e3) / 1e9, 1),
@@ -404,7 +543,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline(w, WORKLOADS)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -414,9 +553,32 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d": w.d, "L": w.L,
                    "frames": w.T // w.L, "window": w.window, "dilation": w.dilation,
                    "window_qk": "fp8_e4m3" if fp8 else "bf16", "chunk": CHUNK},
-        "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown,
+        "roofline": roofline, "roofline_gdn": roofline_gdn, "cpu_baseline": cpu,
+        "step_ms": ({k: round(v, 4) for k, v in step_stats.items() if k != "n"} if step_stats else None),
+        "versions": versions(torch), "breakdown": breakdown,
     }
     print(json.dumps(line), flush=True)
+
+
+def gdn_only(K, torch, w, make_device_inputs, args):
+    """kairos_gdn_fwd alone on one workload: W untimed calls, then K calls
+    timed with events on the launch stream; one JSON line."""
+    d = make_device_inputs(w, torch.device("cuda:0"))
+    o = torch.empty_like(d["v"])
+    S = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(max(1, K.kairos_gdn_workspace_size(K.gdn_desc(w.B, w.T, w.H, w.d))), dtype=torch.uint8,
+                     device="cuda:0")
+    fn = lambda: K.kairos_gdn_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=o, state_out=S, workspace=ws)
+    for _ in range(args.warmup):
+        fn()
+    st = StageTimer(torch)
+    st.run("gdn", fn, max(args.steps, 1))
+    r = st.acc["gdn"]
+    gb = w.B * w.T * w.H * GDN_BYTES_PER_TOKEN_HEAD + 2 * w.B * w.H * w.d * w.d * 4
+    print(json.dumps({"gdn_workload": w.name, "steps": args.steps, **{k: round(v, 4) for k, v in r.items()},
+                      "alg_bytes": gb, "alg_GB_per_s": round(gb / (r["avg_ms"] / 1e3) / 1e9, 1),
+                      "hbm_frac": round(gb / (r["avg_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "scan_segments": gdn_segments_of(K, w)}), flush=True)
 
 
 def workload_breakdown(K, torch, WORKLOADS, make_device_inputs, reps, ctx):
@@ -444,9 +606,11 @@ def workload_breakdown(K, torch, WORKLOADS, make_device_inputs, reps, ctx):
     t = st.run("gdn_B1H24T32760", fn, reps)
     th = w2.B * w2.T * w2.H
     gb = th * GDN_BYTES_PER_TOKEN_HEAD + 2 * w2.B * w2.H * w2.d * w2.d * 4
-    out["gdn_B1H24T32760"] = {"ms": round(t, 4), "tokens_per_s": round(w2.B * w2.T / (t / 1e3)),
+    out["gdn_B1H24T32760"] = {"ms": round(t, 4), "median_ms": round(st.acc["gdn_B1H24T32760"]["median_ms"], 4),
+                              "tokens_per_s": round(w2.B * w2.T / (t / 1e3)),
                               "alg_GB_per_s": round(gb / (t / 1e3) / 1e9, 1),
-                              "hbm_frac": round(gb / (t / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+                              "hbm_frac": round(gb / (t / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "scan_segments": gdn_segments_of(K, w2)}
     del o, S
     bufs = alloc_layer(K, torch, w2, d, False)
     fn = layer_step_fn(K, d, w2, bufs, False, ctx)
