@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY (see the package header).
 
-Source: the Kairos project page (TL;DR / Q3) names FP8 and INT4 attention
+Source: the Kairos project page (Sec. 2, Q2) names FP8 and INT4 attention
 quantisation without details.
 
 Readings:

@@ -1,7 +1,7 @@
 """FP8 E4M3 quantisation of the windowed branches' Q and K.
 
 Source: the Kairos project page (zhaifeiyue.github.io, "Kairos: A Native
-World Model Stack for Physical AI", TL;DR and Q3) names FP8/INT4 attention
+World Model Stack for Physical AI", Sec. 1 TL;DR and Sec. 2 Q2) names FP8/INT4 attention
 quantisation without details; the workload fixes e4m3 with one absmax scale
 per 64-token block.
 

@@ -1,7 +1,7 @@
 // Operands of the windowed branches: the FP8 E4M3 and the 4-bit (FP4 E2M1)
 // block quantisers of Q and K, RoPE of Q and K, and RoPE fused with either.
 //
-// Quantisation (Kairos project page, TL;DR / Q3: FP8 attention quantisation;
+// Quantisation (Kairos project page, Sec. 2 Q2: FP8/INT4 attention quantisation;
 // block size and scale rule as in the 64-token-block absmax workload): per
 // (b, h, 64 consecutive tokens, all d): s = amax / 448 in fp32 (1 when
 // amax == 0); code = E4M3(x / s) of the correctly rounded fp32 quotient,

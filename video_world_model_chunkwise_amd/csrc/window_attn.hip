@@ -45,8 +45,9 @@
 // maximum as it stands and check only their sum; the block maximum is taken
 // (and the block formed again) only when that sum exceeds 2^32.
 //
-// Two workgroups share a CU (two waves per SIMD; three with 4-bit Q/K), so
-// one wave's softmax arithmetic overlaps another's matrix products.  To fit, the hybrid
+// Quantised Q/K in frames of at least one block run three workgroups per CU
+// (three waves per SIMD), bf16 Q/K and shorter frames two, so that one wave's
+// softmax arithmetic overlaps another's matrix products.  To fit, the hybrid
 // kernel parks the finished first branch (gated, normalised, fp32) in a
 // workspace row per query and adds it back in the epilogue.
 #include "common.hpp"
@@ -491,8 +492,11 @@ __device__ __forceinline__ float win_probs(const f32x16 (&S)[2], float cq, float
 // One key block of a branch: scores from buffer cb, online softmax, O update.
 // With spec, the probabilities are first formed against the running maximum
 // as it stands, without the block maximum: a lane whose block sum stays at or
-// below SPEC_LIMIT has every probability at or below it, which bounds O and l
-// as the lazy rescale does.  Only if some lane of the wave exceeds it (its
+// below SPEC_LIMIT has every probability at or below it.  Over nb blocks the
+// two lanes of a query then hold l <= nb * 2^33 and |O| <= l * max|v|, so fp32
+// holds them while nb * max|v| stays below about 2^94 (about 2^113 when every
+// probability is at most 2^RESCALE_SLACK, as after the maximum path).  Only
+// if some lane of the wave exceeds it (its
 // maximum rose by more than log2(SPEC_LIMIT) - 6, or the lane has seen no key
 // yet) are the scores formed again and the block takes the maximum and
 // rescale path; after that every lane's probabilities are at most
