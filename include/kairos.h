@@ -22,7 +22,9 @@
  *   alpha, beta        [B][T][H]         fp32, the gate values themselves
  *   state_in/out       [B][H][dv][dk]    fp32 (the memory S in R^{dv x dk})
  *   gate_logits        [3][H]            fp32, rows (swa, dswa, gdn); sigmoid applied inside
- *   k_ring, v_ring     [B][R][L][H][d]   bf16, slot s holds absolute frame f with f mod R == s
+ *   v_ring             [B][R][L][H][d]   bf16, slot s holds absolute frame f with f mod R == s
+ *   k_ring             the same for bf16 keys without RoPE; otherwise the layout
+ *                      kairos_hlta_ring_size states (rotated keys, codes + scales)
  *   fp8 codes          [B][T][H][d]      uint8 OCP E4M3; scales [B][H][ceil(T/64)] fp32
  * The gated delta rule is the canonical form
  *   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t,

@@ -285,14 +285,6 @@ bool side_usable(const kairos_context_t* c, hipStream_t s) {
   return ss == hipStreamCaptureStatusActive && cs == hipStreamCaptureStatusActive && cid == sid;
 }
 
-// Whether a layer call runs its GDN branch beside the window kernel (the
-// window epilogue then leaves the windowed sum in fp32 and a combine kernel
-// adds the gated GDN output), rather than before it: only when both grids
-// fit on the device at once (two workgroups per compute unit), i.e. when the
-// window kernel alone would leave compute units idle, as for one streamed
-// frame.  On larger calls the extra fp32 round trip and the scan's share of
-// the compute units cost more than the overlap saves (measured: one 1560-
-// token frame at H 24 -10%; 21 frames +10%; the B4 16 x 3600 FP8 layer +4%).
 // Device address of the current device's copy of the scratch array,
 // resolved on the first no-alloc call on that device.
 int noalloc_scratch(void** p) {
@@ -314,6 +306,14 @@ int gdn_fwd_launch(const kairos_gdn_desc* desc, const void* q, const void* k, co
                    const float* alpha, const float* beta, const float* state_in, void* out,
                    float* state_out, void* workspace, hipStream_t s);
 
+// Whether a layer call runs its GDN branch beside the window kernel (the
+// window epilogue then leaves the windowed sum in fp32 and a combine kernel
+// adds the gated GDN output), rather than before it: only when both grids
+// fit on the device at once (two workgroups per compute unit), i.e. when the
+// window kernel alone would leave compute units idle, as for one streamed
+// frame.  On larger calls the extra fp32 round trip and the scan's share of
+// the compute units cost more than the overlap saves (measured: one 1560-
+// token frame at H 24 -10%; 21 frames +10%; the B4 16 x 3600 FP8 layer +4%).
 bool overlap_gdn(const kairos_hlta_desc* d, const kairos_context_t* c) {
   if (!c || c->cus <= 0 || d->g.dk != 128) return false;
   const long win = window_workgroups(d->g.B, d->g.T, d->g.H, d->L);
