@@ -32,7 +32,7 @@ def _pair(B, T, H, seed, with_state):
 
 
 def test_noalloc_matches_workspace_call_twice():
-    _pair(2, 4096, 16, 811, False)        # 34.1 MB of the 64 MiB array, scan split in 3 segments
+    _pair(2, 4096, 16, 811, False)        # 29.9 MB of the 64 MiB array, scan split in 3 segments
     _pair(1, 1000, 4, 812, True)          # smaller, ragged last chunk, state carried in
 
 

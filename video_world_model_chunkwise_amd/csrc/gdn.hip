@@ -28,6 +28,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace kairos {
 
 // ---------------------------------------------------------------- fp32 path
@@ -868,7 +870,8 @@ __device__ __forceinline__ void scan_loader(const ScanCtx<D, NW>& x, const ScanB
 // nseg_launch segments (from segment 0), each as `tiles` row tiles of 16 NW
 // rows.  Tiles below D / (16 NW) advance rows of the state S; tiles above
 // advance rows of the segment's transition M (the same recurrence with v = 0,
-// started from the identity), so that S_end = S_start M + S_end(from zero).
+// started from the identity), so that S_end = S_start M + S_end(from zero);
+// segment 0 has no transition tiles.
 //   start state of segment j (state rows): init_seg[bh][j] when init_seg is
 //     given, else state_in for j = 0 (NULL: zero), else zero;
 //   end state: the last segment of the sequence -> state_out (NULL: dropped);
@@ -895,6 +898,12 @@ struct GdnScanArgs {
 // Workgroup: NW compute waves (16 rows of S each) and NW loader waves that
 // stream the next chunk into the other LDS buffer (each SIMD runs one of
 // each).  The double-buffered LDS tiles allow one workgroup per CU.
+// Workgroups per (b, h) of a scan launch over nseg segments of `tiles` row
+// tiles each, nt of them state tiles: the first segment has no transition tiles.
+__host__ __device__ constexpr int scan_tiles_per_bh(int nseg, int tiles, int nt) {
+  return nseg * tiles - (tiles - nt);
+}
+
 template <int D, int NW, bool OUT>
 __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(const GdnScanArgs a) {
   using G = ScanGeom<D, NW>;
@@ -913,15 +922,18 @@ __global__ __launch_bounds__(128 * NW) void gdn_scan_kernel(const GdnScanArgs a)
   const ScanBuf B1{K1, Q1, V1, T1, g1, gam1, w1, b1};
 
   // (b, h) outermost, then segment, then row tile: the tiles of one segment
-  // are adjacent and share an XCD (and its L2) for the common K, Q, T reads
+  // are adjacent and share an XCD (and its L2) for the common K, Q, T reads.
+  // The first segment starts from a given state, so it has state tiles only
+  // (no transition tiles are launched for it: idle workgroups would share
+  // compute units with working ones).
   const int lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int per_bh = a.nseg_launch * a.tiles;
+  const int per_bh = scan_tiles_per_bh(a.nseg_launch, a.tiles, NT);
   const int bh = lid / per_bh;
   if (bh >= a.B * a.H) return;
-  const int j = (lid % per_bh) / a.tiles;
-  const int tile = lid % a.tiles;
+  const int local = lid % per_bh;
+  const int j = local < NT ? 0 : 1 + (local - NT) / a.tiles;
+  const int tile = local < NT ? local : (local - NT) % a.tiles;
   const bool trans = tile >= NT;
-  if (trans && j == 0) return;        // the first segment starts from a given state
   const int b = bh / a.H, h = bh % a.H;
   const int c0 = j * a.seg_chunks;
   const int nch = max(0, min(a.seg_chunks, a.nchunks - c0));
@@ -1096,27 +1108,40 @@ int gdn_chunk_waves(int B, int H, int D) {
 // plain scan occupies few compute units for the whole sequence; splitting the
 // sequence into P segments runs P - 1 of them from known starts (zero state
 // and identity transition, without outputs) in a first pass, combines the
-// segment maps, and then all P with their true start states and outputs:
-// about twice the work on a sequential depth of two segments.  P is picked
-// from the shape alone (a 256-compute-unit budget; workgroups of 64 rows, two
-// per unit in the first pass, whose kernel needs no Q, P or O tiles, one in
-// the second), so that workspace sizes do not depend on the device.
+// segment maps, and then all P with their true start states and outputs.
+// P minimises a cost model of the two passes and the combine, from the shape
+// alone (so that workspace sizes do not depend on the device): a pass of w
+// workgroups on 256 compute units runs ceil(w / 256) rounds (a compute unit
+// holding two workgroups runs each at about half speed), each round L chunks
+// long at a per-chunk time that is the larger of a latency term and a term
+// growing with the round's workgroups (memory traffic).  Constants in
+// microseconds, fitted to kairos_gdn_fwd times on MI355X over B H in
+// {2 .. 64}, T in {4096 .. 65536} and P in {1 .. 16}: the model's choice is
+// within 0.5% of the fastest P on every measured shape.
 int gdn_segments(int B, int H, int T, int D) {
   const long bh = (long)B * H;
   const long n = (T + CH - 1) / CH;
   if (n < 64 || D % 64 != 0) return 1;
-  const long cus = 256, nt = D / 64;
-  auto rounds = [](long w, long slots) { return (w + slots - 1) / slots; };
-  long best = rounds(bh * nt, cus) * n;
+  const long nt = D / 64;                              // state-row workgroups per (b, h)
+  constexpr long kCus = 256;
+  constexpr double kLat1 = 0.896, kPerWg1 = 3.93e-3;   // first pass (no outputs)
+  constexpr double kLat2 = 1.92, kPerWg2 = 8.65e-3;    // second pass, plain scan
+  constexpr double kCombineStep = 5.44;
+  auto pass = [](long w, long L, double lat, double per_wg) {
+    const long full = w / kCus, rest = w % kCus;
+    double t = (double)full * std::max(lat, kCus * per_wg);
+    if (rest > 0) t += std::max(lat, (double)rest * per_wg);
+    return t * (double)L;
+  };
+  double best = pass(bh * nt, n, kLat2, kPerWg2);
   int best_p = 1;
-  for (int P = 2; P <= 8; ++P) {
+  for (int P = 2; P <= 16; ++P) {
     const long L = (n + P - 1) / P;
     if ((P - 1) * L >= n) continue;                    // empty last segment
-    const long w1 = bh * (nt + 2 * nt * (P - 2));      // first pass: segment 0, then S and M rows
-    const long w2 = bh * nt * P;                       // second pass
-    const long cost = rounds(w1, 2 * cus) * L + rounds(w2, cus) * L + P;   // + launches, combine
-    if (cost < best) {
-      best = cost;
+    const double t = pass(bh * nt * (2 * P - 3), L, kLat1, kPerWg1) + pass(bh * nt * P, L, kLat2, kPerWg2) +
+                     kCombineStep * (P - 2) * (1.0 + (double)(bh * (D / 16)) / kCus);
+    if (t < best) {
+      best = t;
       best_p = P;
     }
   }
@@ -1147,7 +1172,7 @@ size_t gdn_chunk_workspace(int B, int T, int H, int D) { return gdn_ws_layout(B,
 
 template <int D, int NW, bool OUT>
 static hipError_t launch_scan(const GdnScanArgs& a, hipStream_t stream) {
-  const long nblk = (long)a.B * a.H * a.nseg_launch * a.tiles;
+  const long nblk = (long)a.B * a.H * scan_tiles_per_bh(a.nseg_launch, a.tiles, D / (16 * NW));
   if (nblk > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (nblk == 0) return hipSuccess;
   gdn_scan_kernel<D, NW, OUT><<<(unsigned)nblk, 128 * NW, 0, stream>>>(a);
