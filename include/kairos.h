@@ -68,7 +68,9 @@ typedef enum {
   KAIROS_ERR_ALIAS = -5,       /* an output overlaps an input it may not overlap  */
   KAIROS_ERR_UNSUPPORTED = -6, /* valid in principle, not implemented             */
   KAIROS_ERR_WORKSPACE = -7,   /* workspace missing or too small                  */
-  KAIROS_ERR_HIP = -8          /* a HIP launch or query failed                    */
+  KAIROS_ERR_HIP = -8,        /* a HIP launch or query failed                    */
+  KAIROS_ERR_RANGE = -9       /* input values outside their range (reported by the
+                                 binding's debug check, kairos_gdn_check_gates)   */
 } kairos_status;
 
 typedef enum {
@@ -188,6 +190,23 @@ int kairos_gdn_fwd(const kairos_gdn_desc* desc, const void* q, const void* k, co
                    const float* alpha, const float* beta, const float* state_in,
                    void* out, float* state_out, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/* Debug check of the gates (Sec. 2.2.1: alpha and beta are sigmoids, Eq. 1
+ * and Eq. 4; Sec. 2.3.2, Remark 2, Eq. 18: the long-horizon bound needs a
+ * contractive update, which holds for alpha <= 1 and, with unit keys,
+ * 0 <= beta <= 1; the kernels take log2 alpha, so alpha must be > 0).
+ * Counts the (b, t, h) with alpha outside (0, 1] or beta outside
+ * [0, beta_max] (NaN counts as outside) into *count.
+ *   alpha, beta  [B][T][H] fp32, 16-byte aligned (may be NULL when T == 0)
+ *   beta_max     1 for the canonical form; larger for the printed Eq. 6 form
+ *                of kairos_gdn_prologue, whose beta / alpha may exceed 1
+ *   count        one device uint32, 4-byte aligned, overwritten (not added to)
+ * Enqueued on `stream` like every other call: the count is valid once the
+ * stream reaches that point (the caller reads it).  Nothing else is touched.
+ * Errors: KAIROS_ERR_NULL, _SHAPE (B, H < 1, T < 0, B*T*H above 2^40, NaN or
+ * negative beta_max), _ALIGN, _ALIAS (count inside alpha or beta), _HIP. */
+int kairos_gdn_check_gates(const float* alpha, const float* beta, int32_t B, int32_t T, int32_t H,
+                           float beta_max, uint32_t* count, void* stream);
 
 /* kairos_gdn_fwd for callers that cannot allocate device memory (code under
  * graph capture, tight serving loops, harnesses that forbid allocation): the

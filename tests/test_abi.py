@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert K.version() == 201
+    assert K.version() == 202
     assert K.status_string(0) == "ok"
     assert "align" in K.status_string(ALIGN)
     assert K.status_string(12345) == "unknown status"
@@ -245,6 +245,24 @@ def test_window_and_quantiser_validation():
     assert L.kairos_fp8_quantize(cv(0x1008), cv(0x2000), cv(0x3000), 1, 64, 2, 128, None) == ALIGN
     assert L.kairos_fp8_quantize(cv(0x1000), cv(0x1000), cv(0x9000000), 1, 64, 2, 128, None) == ALIAS
     assert L.kairos_fp8_quantize(None, None, None, 1, 0, 2, 128, None) == OK   # empty: nothing to do
+
+
+@host_only
+def test_gate_check_validation():
+    L = K.lib()
+    cv, f = ctypes.c_void_p, ctypes.c_float
+    a, b, c = 0x10000, 0x20000, 0x30000
+    n4 = 2 * 100 * 3 * 4
+    call = lambda a_=a, b_=b, B=2, T=100, H=3, bmax=1.0, c_=c: L.kairos_gdn_check_gates(
+        cv(a_) if a_ else None, cv(b_) if b_ else None, B, T, H, f(bmax), cv(c_) if c_ else None, None)
+    assert call(c_=0) == NULL
+    assert call(a_=0) == NULL and call(b_=0) == NULL
+    assert call(B=0) == SHAPE and call(H=0) == SHAPE and call(T=-1) == SHAPE
+    assert call(B=1 << 20, T=1 << 20, H=2) == SHAPE                  # more than 2^40 gate pairs
+    assert call(bmax=-1.0) == SHAPE and call(bmax=float("nan")) == SHAPE
+    assert call(a_=a + 8) == ALIGN and call(c_=c + 2) == ALIGN
+    assert call(c_=a + 16) == ALIAS and call(c_=b + n4 - 4) == ALIAS
+    assert K.status_string(K.KAIROS_ERR_RANGE) == "input values out of range"
 
 
 @host_only

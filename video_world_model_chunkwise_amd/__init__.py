@@ -17,5 +17,5 @@ from ._lib import (  # noqa: F401
     WINDOW_CAUSAL, WINDOW_CENTERED,
     kairos_gdn_prologue, kairos_rope, kairos_gdn_fwd, kairos_gdn_fwd_noalloc, kairos_hlta_fwd, kairos_hlta_window_fwd, kairos_window_fwd, kairos_fp8_quantize, kairos_fp4_quantize,
     kairos_gdn_workspace_size, kairos_hlta_workspace_size, kairos_hlta_ring_frames_required,
-    gdn_desc, hlta_desc, ring_key_shape,
+    gdn_desc, hlta_desc, ring_key_shape, kairos_gdn_check_gates, KAIROS_ERR_RANGE,
 )

@@ -22,7 +22,9 @@ symbols = (
     "kairos_window_fwd", "kairos_hlta_fwd", "kairos_fp8_quantize", "kairos_hlta_window_fwd",
     "kairos_gdn_prologue", "kairos_rope", "kairos_fp4_quantize", "kairos_context_create",
     "kairos_context_destroy", "kairos_gdn_fwd_noalloc", "kairos_hlta_ring_size",
+    "kairos_gdn_check_gates",
 )
+KAIROS_ERR_RANGE = -9
 
 
 class KairosError(RuntimeError):
@@ -74,6 +76,8 @@ def lib():
         L.kairos_fp8_quantize.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                           c_int32, c_void_p]
         L.kairos_fp4_quantize.argtypes = L.kairos_fp8_quantize.argtypes
+        L.kairos_gdn_check_gates.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float,
+                                             c_void_p, c_void_p]
         for name in symbols:
             getattr(L, name).restype = c_int if name != "kairos_status_string" else c_char_p
         _lib = L
@@ -190,6 +194,41 @@ def kairos_hlta_ring_frames_required(desc: HltaDesc) -> int:
     return n.value
 
 
+def _debug() -> bool:
+    """KAIROS_DEBUG set (and not 0): the GDN and layer calls first check
+    their gates with kairos_gdn_check_gates (synchronising) and raise
+    KairosError(KAIROS_ERR_RANGE) if any is out of range."""
+    return os.environ.get("KAIROS_DEBUG", "0") not in ("", "0")
+
+
+def kairos_gdn_check_gates(alpha, beta, beta_max=1.0, count=None, stream=None) -> int:
+    """Number of (b, t, h) with alpha [B, T, H] outside (0, 1] or beta outside
+    [0, beta_max] (NaN counts as outside).  Synchronises the stream to read
+    the count; `count` (one int32 on the device) is allocated when not given."""
+    torch = _torch()
+    B, T, H = alpha.shape
+    dev = alpha.device
+    _need(alpha, "alpha", torch.float32, (B, T, H), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=dev)
+    st = lib().kairos_gdn_check_gates(_ptr(alpha), _ptr(beta), B, T, H, c_float(beta_max), _ptr(count),
+                                      _stream(stream))
+    _check(st, "kairos_gdn_check_gates")
+    if stream is None or isinstance(stream, int):
+        torch.cuda.synchronize(dev)
+    else:
+        stream.synchronize()
+    return int(count.item()) & 0xFFFFFFFF
+
+
+def _debug_gates(alpha, beta, stream, where):
+    n = kairos_gdn_check_gates(alpha, beta, stream=stream)
+    if n:
+        raise KairosError(KAIROS_ERR_RANGE, f"{where} ({n} of {alpha.numel()} gate pairs outside alpha in (0, 1], "
+                                            "beta in [0, 1]; KAIROS_DEBUG)")
+
+
 def _workspace(nbytes, device):
     torch = _torch()
     if nbytes == 0:
@@ -221,6 +260,8 @@ def kairos_gdn_fwd(q, k, v, alpha, beta, state_in=None, out=None, state_out=None
         _need(state_out, "state_out", torch.float32, (B, H, d, d), dev)
     desc = gdn_desc(B, T, H, d, io)
     nws = kairos_gdn_workspace_size(desc)
+    if _debug():
+        _debug_gates(alpha, beta, stream, "kairos_gdn_fwd")
     ws = workspace if workspace is not None else _workspace(nws, dev)
     st = lib().kairos_gdn_fwd(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                               _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(ws), nws,
@@ -372,6 +413,8 @@ def kairos_hlta_fwd(q, k, v, alpha, beta, gate_logits, L, window, dilation, fram
     if state_out is None and keep_state:
         state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     nws = kairos_hlta_workspace_size(desc)
+    if _debug():
+        _debug_gates(alpha, beta, stream, "kairos_hlta_fwd")
     ws = workspace if workspace is not None else _workspace(nws, dev)
     if ws is not None and ws.numel() < nws:
         raise ValueError(f"workspace too small: {ws.numel()} < {nws}")

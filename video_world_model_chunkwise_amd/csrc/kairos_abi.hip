@@ -348,11 +348,12 @@ const char* kairos_status_string(int status) {
     case KAIROS_ERR_UNSUPPORTED: return "unsupported combination";
     case KAIROS_ERR_WORKSPACE: return "workspace missing or too small";
     case KAIROS_ERR_HIP: return "HIP runtime error";
+    case KAIROS_ERR_RANGE: return "input values out of range";
     default: return "unknown status";
   }
 }
 
-int kairos_version(void) { return 201; }
+int kairos_version(void) { return 202; }
 
 int kairos_gdn_workspace_size(const kairos_gdn_desc* desc, size_t* bytes) {
   if (!bytes) return KAIROS_ERR_NULL;
@@ -807,6 +808,17 @@ int block_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B,
 }
 
 }  // namespace
+
+int kairos_gdn_check_gates(const float* alpha, const float* beta, int32_t B, int32_t T, int32_t H,
+                           float beta_max, uint32_t* count, void* stream) {
+  if (B < 1 || H < 1 || T < 0 || !(beta_max >= 0.f)) return KAIROS_ERR_SHAPE;
+  const int64_t n = (int64_t)B * T * H;
+  if (n > kMaxElems) return KAIROS_ERR_SHAPE;
+  if (!count || (n > 0 && (!alpha || !beta))) return KAIROS_ERR_NULL;
+  if (((uintptr_t)count & 3u) != 0 || !aligned16(alpha) || !aligned16(beta)) return KAIROS_ERR_ALIGN;
+  if (overlaps(count, 4, alpha, (size_t)n * 4) || overlaps(count, 4, beta, (size_t)n * 4)) return KAIROS_ERR_ALIAS;
+  return hip_status(launch_gate_check(alpha, beta, (long)n, beta_max, count, (hipStream_t)stream));
+}
 
 int kairos_fp8_quantize(const void* x_bf16, uint8_t* codes, float* scales, int32_t B, int32_t T,
                         int32_t H, int32_t d, void* stream) {
