@@ -6,8 +6,8 @@
 // rests on the update being a contraction, which holds for alpha <= 1 and,
 // with unit keys, 0 <= beta <= 1; the kernels also take log2 alpha, which
 // needs alpha > 0.
-#include "common.hpp"
-#include "launch.hpp"
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #include <algorithm>
 

@@ -29,6 +29,12 @@ struct kairos_context_t {
 
 namespace kairos {
 
+// Count of the n gate pairs with alpha outside (0, 1] or beta outside
+// [0, beta_max] (NaN counts as outside) into *count, overwritten
+// (csrc/gates_check.hip).
+hipError_t launch_gate_check(const float* alpha, const float* beta, long n, float beta_max, uint32_t* count,
+                             hipStream_t stream);
+
 // Scratch array of kairos_gdn_fwd_noalloc, the workspace of callers that
 // cannot allocate device memory.  Each device the library runs on holds its
 // own copy until the process ends.  Host code never uses the array's name as

@@ -109,10 +109,6 @@ hipError_t launch_ring_copy(const void* src, void* dst, int B, int F, int L, int
 // The same for per-frame key scales: src [BH][F][nbf] fp32 -> dst [BH][R][nbf].
 hipError_t launch_ring_copy_scales(const float* src, float* dst, int BH, int F, int nbf, long frame_offset,
                                    int R, hipStream_t stream);
-// Count of the n gate pairs with alpha outside (0, 1] or beta outside
-// [0, beta_max] (NaN counts as outside) into *count (overwritten).
-hipError_t launch_gate_check(const float* alpha, const float* beta, long n, float beta_max, uint32_t* count,
-                             hipStream_t stream);
 // qf: 0 bf16 q, k; 1 E4M3 codes; 2 E2M1 codes (two per byte)
 hipError_t launch_window(const WinArgs& args, int qf, bool hybrid, hipStream_t stream);
 // Workgroups of one window-kernel launch over B x T x H with frames of L tokens.
