@@ -392,3 +392,59 @@ def test_streaming_quantised_equals_full_run(fmt, rope, dil, L):
                                L, w, dil, window_qk=fmt, qk_blocks="frames", rope_base=rope or None)
     _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
     _assert_close(host(state), S_ref, "stream S")
+
+
+# ------------------------------------------------------------------ more streaming and frame-block cases
+
+@pytest.mark.parametrize("fmt,rope,dil", [("bf16", 1e4, 2), ("fp8", 1e4, 2), ("fp4", 0.0, 3)])
+def test_streaming_batched_equals_full_run(fmt, rope, dil):
+    """Two batch rows through the ring (the ring's and the scales' batch
+    strides), fed one frame per call, against one full-length oracle run."""
+    B, F, L, H = 2, 7, 96, 2
+    w = int(1.6 * L)
+    T = F * L
+    print(f"stream batched {fmt} rope={rope} dil={dil}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=91 + dil)
+    dv = inputs_to_dev(inp)
+    wq = {"bf16": K.BF16, "fp8": K.FP8_E4M3, "fp4": K.FP4_E2M1}[fmt]
+    qb = K.QK_BLOCKS_FRAMES if fmt != "bf16" else K.QK_BLOCKS_TOKENS
+    R = K.kairos_hlta_ring_frames_required(K.hlta_desc(B, L, H, 128, L, w, dil))
+    k_ring, v_ring = K.alloc_rings(B, L, H, 128, w, dil, R, wq, rope, qb)
+    state = torch.zeros((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
+    ys = []
+    for f in range(F):
+        sl = slice(f * L, (f + 1) * L)
+        y, _ = K.kairos_hlta_fwd(dv["q"][:, sl].contiguous(), dv["k"][:, sl].contiguous(),
+                                 dv["v"][:, sl].contiguous(), dv["alpha"][:, sl].contiguous(),
+                                 dv["beta"][:, sl].contiguous(), dv["gates"], L, w, dil,
+                                 frame_offset=f, state_in=state, state_out=state, ring_frames=R,
+                                 k_ring=k_ring, v_ring=v_ring, rope_base=rope, window_qk=wq, qk_blocks=qb)
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, window_qk=fmt, qk_blocks="frames" if fmt != "bf16" else "tokens",
+                               rope_base=rope or None)
+    _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
+    _assert_close(host(state), S_ref, "stream S")
+
+
+@pytest.mark.parametrize("fmt,L,F,extra,w,dil,centered", [
+    ("fp8", 100, 5, 37, 150, 2, False),     # partial last frame: its blocks end with it
+    ("fp4", 40, 6, 23, 90, 3, False),       # frames shorter than a block, partial last frame
+    ("fp8", 128, 4, 0, 200, 3, True),       # centred windows on frame-aligned blocks
+    ("fp8", 100, 5, 61, 160, 2, True),
+])
+def test_layer_frame_blocks_partial_and_centred(fmt, L, F, extra, w, dil, centered):
+    B, H = 1, 2
+    T = F * L + extra
+    print(f"frame blocks {fmt} L{L} T{T} centred={centered}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=130 + L + extra)
+    dv = inputs_to_dev(inp)
+    wq = K.FP8_E4M3 if fmt == "fp8" else K.FP4_E2M1
+    y, S = K.kairos_hlta_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dv["gates"], L, w, dil,
+                             window_qk=wq, qk_blocks=K.QK_BLOCKS_FRAMES, centered=centered)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, window_qk=fmt, qk_blocks="frames", centered=centered)
+    _assert_close(host(y), y_ref, "y")
+    _assert_close(host(S), S_ref, "S")
