@@ -448,3 +448,38 @@ def test_layer_frame_blocks_partial_and_centred(fmt, L, F, extra, w, dil, center
                                L, w, dil, window_qk=fmt, qk_blocks="frames", centered=centered)
     _assert_close(host(y), y_ref, "y")
     _assert_close(host(S), S_ref, "S")
+
+
+@pytest.mark.parametrize("fmt,rope", [("fp8", 1e4), ("bf16", 0.0)])
+def test_streaming_with_context_equals_full_run(fmt, rope):
+    """A rollout whose frame calls take the overlapped schedule of a context
+    (the GDN branch on the side stream beside the window kernel, the
+    pre-passes and the combine on the caller's stream), with the ring, against
+    one full-length oracle run."""
+    B, F, L, H, w, dil = 1, 7, 96, 2, 150, 2
+    T = F * L
+    print(f"stream ctx {fmt} rope={rope}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=97)
+    dv = inputs_to_dev(inp)
+    wq = K.FP8_E4M3 if fmt == "fp8" else K.BF16
+    qb = K.QK_BLOCKS_FRAMES if fmt == "fp8" else K.QK_BLOCKS_TOKENS
+    R = K.kairos_hlta_ring_frames_required(K.hlta_desc(B, L, H, 128, L, w, dil))
+    k_ring, v_ring = K.alloc_rings(B, L, H, 128, w, dil, R, wq, rope, qb)
+    state = torch.zeros((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
+    ys = []
+    with K.Context() as ctx:
+        for f in range(F):
+            sl = slice(f * L, (f + 1) * L)
+            y, _ = K.kairos_hlta_fwd(dv["q"][:, sl].contiguous(), dv["k"][:, sl].contiguous(),
+                                     dv["v"][:, sl].contiguous(), dv["alpha"][:, sl].contiguous(),
+                                     dv["beta"][:, sl].contiguous(), dv["gates"], L, w, dil,
+                                     frame_offset=f, state_in=state, state_out=state, ring_frames=R,
+                                     k_ring=k_ring, v_ring=v_ring, rope_base=rope, window_qk=wq,
+                                     qk_blocks=qb, ctx=ctx)
+            ys.append(y)
+        torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, window_qk=fmt, qk_blocks="frames" if fmt == "fp8" else "tokens",
+                               rope_base=rope or None)
+    _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
+    _assert_close(host(state), S_ref, "stream S")
