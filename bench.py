@@ -28,11 +28,14 @@ METRIC = "GDN / hybrid temporal-attention fwd tokens/s + % roofline, H=24 d=128,
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
-# transcendental (v_exp_f32) rate: quarter of the 16 fp32 lanes per clock of
-# a SIMD, 256 CU x 4 SIMD x 4 lanes x 2.4 GHz
-PEAK_EXP_PER_S = 256 * 4 * 4 * 2.4e9
-# one wave64 VALU instruction issues over 4 clocks (16 lanes per clock)
-VALU_ISSUE_CLK = 4
+# SIMD time of one wave64 VALU instruction: 2 clocks for fp32 arithmetic (the
+# published 157.3 TFLOP/s fp32 vector peak is 32 FMA lanes per clock per SIMD);
+# 8 clocks for a transcendental (v_exp_f32), measured on gfx950 with two or
+# more waves per SIMD issuing independent instructions
+VALU_ISSUE_CLK = 2
+TRANS_ISSUE_CLK = 8
+# exponentials per second: 256 CU x 4 SIMD x 64 lanes / 8 clocks x 2.4 GHz
+PEAK_EXP_PER_S = 256 * 4 * (64 / TRANS_ISSUE_CLK) * 2.4e9
 SIMDS, CLOCK_HZ = 1024, 2.4e9
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
@@ -462,10 +465,12 @@ def main():
     sq = read_counter_summary("hlta_fp8_B4H24F16L3600_sq_counters.txt")
     if sq.get("win_attn_kernel.source_sha") == src_sha("window_attn.hip", "common.hpp", "launch.hpp"):
         v = float(sq["win_attn_kernel.SQ_INSTS_VALU"])
+        tr = float(sq["win_attn_kernel.SQ_INSTS_VALU_TRANS_F32"])
         m = float(sq["win_attn_kernel.SQ_VALU_MFMA_BUSY_CYCLES"])
         roofline["counters"] = {
-            "valu_insts_per_launch": v, "mfma_insts_per_launch": float(sq["win_attn_kernel.SQ_INSTS_MFMA"]),
-            "valu_issue_ms": round(v * VALU_ISSUE_CLK / SIMDS / CLOCK_HZ * 1e3, 4),
+            "valu_insts_per_launch": v, "trans_insts_per_launch": tr,
+            "mfma_insts_per_launch": float(sq["win_attn_kernel.SQ_INSTS_MFMA"]),
+            "valu_issue_ms": round(((v - tr) * VALU_ISSUE_CLK + tr * TRANS_ISSUE_CLK) / SIMDS / CLOCK_HZ * 1e3, 4),
             "mfma_busy_ms": round(m / SIMDS / CLOCK_HZ * 1e3, 4),
             "source": "profiles/hlta_fp8_B4H24F16L3600_sq_counters.txt"}
     pro_fresh = cnt.get("gdn_prologue_kernel.source_sha") == src_sha("prologue.hip", "common.hpp",
