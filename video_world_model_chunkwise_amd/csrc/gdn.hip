@@ -115,7 +115,7 @@ __global__ __launch_bounds__(D) void gdn_f32_kernel(const float* __restrict__ q,
 
 constexpr int CH = 64;          // chunk length
 constexpr int TS = CH + 8;      // row stride of the bf16 T tile in the prep kernel
-constexpr int AS = CH + 4;      // row stride of the fp32 A tile
+constexpr int ADS = 20;         // row stride of an fp32 diagonal block of A in the prep kernel
 
 __device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xFFFFu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
@@ -157,12 +157,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 //   A   = strictlower(b_t 2^{g_t - g_i} k_t.k_i)
 //   T   = (I + A)^{-1}                   (written out, bf16, unit lower triangular)
 // One wave per chunk: the 64 x D key tile stays in registers (it is both
-// operands of the Gram product), A goes to LDS in fp32.  T by blocks of 16:
-// diagonal blocks by forward substitution, then the 16x16 off-diagonal block
-// of each 32x32 half, then the lower-left 32x32 block T_LL = -T_H A_HL T_L
-// (block inverse of a lower triangular matrix).
+// operands of the Gram product).  T by blocks of 16: diagonal blocks by
+// forward substitution, then the 16x16 off-diagonal block of each 32x32
+// half, then the lower-left 32x32 block T_LL = -T_H A_HL T_L (block inverse
+// of a lower triangular matrix).  Only the forward substitution needs A in
+// fp32, so only A's four diagonal blocks go to LDS in fp32; its off-diagonal
+// blocks are matrix-product operands (bf16) and sit in the T tile at the
+// places their T blocks take later, each read before its T block is written.
+// The smaller LDS footprint lets more waves run per CU.
 struct PrepSmem {
-  float Af[CH][AS];
+  float Ad[4][16][ADS];
   uint16_t Tb[CH][TS];
   float g2[CH];
   float bet[CH];
@@ -217,8 +221,9 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
   for (int i = lane; i < CH * TS / 8; i += 64) reinterpret_cast<uint4*>(&sm.Tb[0][0])[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  // A = strictlower(b 2^{dg} K K^T), fp32.  Lane (l16, g) of tile (ti, tj)
-  // holds rows 16 ti + 4g + r (r = 0..3) of column 16 tj + l16.
+  // A = strictlower(b 2^{dg} K K^T): diagonal tiles in fp32, the others in
+  // bf16 in the T tile.  Lane (l16, g) of tile (ti, tj) holds rows
+  // 16 ti + 4g + r (r = 0..3) of column 16 tj + l16.
   float4 grow[4], brow[4];
   float gcol[4];
 #pragma unroll
@@ -241,7 +246,8 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * ti + 4 * g + r;
       const float val = br[r] * __builtin_amdgcn_exp2f(gr[r] - gcol[tj]) * acc[r];
-      sm.Af[row][col] = (ti > tj || col < row) ? val : 0.f;
+      if (ti == tj) sm.Ad[ti][4 * g + r][l16] = col < row ? val : 0.f;
+      else sm.Tb[row][col] = bf16_bits(val);
     }
   }
   __syncthreads();
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
     for (int t = 1; t < 16; ++t)
 #pragma unroll
       for (int q = 0; q < (t + 3) / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(&sm.Af[16 * blk + t][16 * blk + 4 * q]);
+        const float4 v = *reinterpret_cast<const float4*>(&sm.Ad[blk][t][4 * q]);
         a[t][4 * q] = v.x; a[t][4 * q + 1] = v.y; a[t][4 * q + 2] = v.z; a[t][4 * q + 3] = v.w;
       }
     float x[16];
@@ -278,8 +284,8 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int h0 = 2 * half, h1 = 2 * half + 1;
-    const float4 av = *reinterpret_cast<const float4*>(&sm.Af[16 * h1 + l16][16 * h0 + 4 * g]);
-    const bf16x8 a = to_bf16x8(av.x, av.y, av.z, av.w, 0.f, 0.f, 0.f, 0.f);
+    const uint2 av = *reinterpret_cast<const uint2*>(&sm.Tb[16 * h1 + l16][16 * h0 + 4 * g]);   // A_{h1,h0}
+    const bf16x8 a = as_bf16x8(av, make_uint2(0, 0));
     const uint2 lo = lds_read_tr(&sm.Tb[16 * h0 + 4 * g + l16 / 4][16 * h0 + 4 * (l16 % 4)]);
     const f32x4 z = mfma16x16x32(a, as_bf16x8(lo, make_uint2(0, 0)), zero4());
     const uint2 tlo = *reinterpret_cast<const uint2*>(&sm.Tb[16 * h1 + l16][16 * h1 + 4 * g]);
@@ -302,9 +308,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const uint16_t* __restrict
     f32x4 z[2];
 #pragma unroll
     for (int zi = 0; zi < 2; ++zi) {
-      const float4 a0 = *reinterpret_cast<const float4*>(&sm.Af[32 + 16 * zi + l16][8 * g]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&sm.Af[32 + 16 * zi + l16][8 * g + 4]);
-      const bf16x8 a = to_bf16x8(a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w);
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Tb[32 + 16 * zi + l16][8 * g]));   // A_HL
       z[zi] = mfma16x16x32(a, as_bf16x8(b0, b1), zero4());
     }
     const bf16x8 zb = regs_operand(z[0], z[1]);
