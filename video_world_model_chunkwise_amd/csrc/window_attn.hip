@@ -637,6 +637,13 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   // maximum keeps rising, and a failed attempt costs most of a block.
   bool spec = false;
   int nfail = 0;
+  // Aligned blocks: the number of blocks after the current one that form a
+  // run of interior blocks, each full, valid, past the first block inside
+  // every window of the wave (so inside them all, with a speculative attempt
+  // allowed), and followed by a full, valid block of the same frame.  Such a
+  // block steps its load addresses by one block and needs neither the
+  // classification nor the mask; the general step sets the count.
+  int run = 0;
   for (int jb = 0; jb < nb; jb += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -644,60 +651,85 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
       if (jj >= nb) break;
       const WinBuf& cb = half ? B1 : B0;
       const WinBuf& nbuf = half ? B0 : B1;
-      const int pb = ALIGN ? n0 * L + m0 : br.p_lo + BK * jj;
-      const int size = ALIGN ? e0 - m0 : BK;
-      // next block's (sub-frame, offset, end, token block) and its loads;
-      // inside a frame an aligned block starts at the current end with the
-      // next token block
-      int n1 = n0, m1 = e0, e1;
-      const float* tb1 = tb0;
-      if (ALIGN) {
-        if (e0 < L) {
-          e1 = min(e0 + BK, L);
-          tb1 = tb0 + 1;
-        } else {
-          n1 = n0 + 1;
-          m1 = 0;
-          e1 = blk_end(n1, 0);
-          tb1 = more_blocks(jj, nb) ? scale_at(n1, 0) : tb0;
-        }
+      int pb, size, n1, m1, e1, dmax1 = 0;
+      const float* tb1;
+      bool more, full, touch;
+      if (ALIGN && run > 0) {
+        --run;
+        pb = n0 * L + m0;
+        size = BK;
+        n1 = n0;
+        m1 = e0;
+        e1 = e0 + BK;
+        tb1 = tb0 + 1;
+        dmax1 = BK - 1;
+        more = true;
+        full = true;
+        touch = true;
+        ld.kb += (size_t)BK * a.H * qk_row_bytes(QF);
+        ld.vb += (size_t)BK * a.H * WD * 2;
+        win_issue_al<QF, SHORTL>(ld, nbuf, qc.wave);
       } else {
-        while (m1 >= L) { m1 -= L; ++n1; }
-        e1 = m1 + BK;
-      }
-      const bool more = jj + 1 < nb;
-      const float ks1 = ALIGN && more ? *tb1 : 1.f;
-      int dmax1 = 0;
-      if (more) {
+        pb = ALIGN ? n0 * L + m0 : br.p_lo + BK * jj;
+        size = ALIGN ? e0 - m0 : BK;
+        // next block's (sub-frame, offset, end, token block) and its loads;
+        // inside a frame an aligned block starts at the current end with the
+        // next token block
+        n1 = n0;
+        m1 = e0;
+        tb1 = tb0;
         if (ALIGN) {
-          // a full next block in the same frame is this block's rows 64 on
-          dmax1 = min(e1 - m1, br.p_hi - (n1 * L + m1) + 1) - 1;
-          if (dmax0 == BK - 1 && dmax1 == BK - 1 && n1 == n0) {
-            ld.kb += (size_t)BK * a.H * qk_row_bytes(QF);
-            ld.vb += (size_t)BK * a.H * WD * 2;
+          if (e0 < L) {
+            e1 = min(e0 + BK, L);
+            tb1 = tb0 + 1;
           } else {
-            win_block_addrs_al<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1, m1, dmax1);
+            n1 = n0 + 1;
+            m1 = 0;
+            e1 = blk_end(n1, 0);
+            tb1 = more_blocks(jj, nb) ? scale_at(n1, 0) : tb0;
           }
-          win_issue_al<QF, SHORTL>(ld, nbuf, qc.wave);
         } else {
-          // inside one frame, unclamped, the next block's rows are this block's
-          // rows 64 positions on
-          const bool step = !SHORTL && m0 + BK <= L && n1 == n0 && m1 + BK <= L && pb + 2 * BK - 1 <= br.p_hi;
-          if (step) {
-#pragma unroll
-            for (int j = 0; j < WinGeom<QF, SHORTL>::NJ; ++j) ld.src[j] += ld.inc[j];
-          } else {
-            win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1 * L + m1, n1, m1);
-          }
-          win_issue<QF, SHORTL>(ld, nbuf, qc.wave);
+          while (m1 >= L) { m1 -= L; ++n1; }
+          e1 = m1 + BK;
         }
+        more = jj + 1 < nb;
+        if (more) {
+          if (ALIGN) {
+            // a full next block in the same frame is this block's rows 64 on
+            dmax1 = min(e1 - m1, br.p_hi - (n1 * L + m1) + 1) - 1;
+            if (dmax0 == BK - 1 && dmax1 == BK - 1 && n1 == n0) {
+              ld.kb += (size_t)BK * a.H * qk_row_bytes(QF);
+              ld.vb += (size_t)BK * a.H * WD * 2;
+            } else {
+              win_block_addrs_al<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1, m1, dmax1);
+            }
+            win_issue_al<QF, SHORTL>(ld, nbuf, qc.wave);
+            // the run that starts with the next block (pc: its position)
+            const int pc = n1 * L + m1;
+            if (qc.active && e1 - m1 == BK && dmax1 == BK - 1 && m1 + 2 * BK <= L && pc + 2 * BK - 1 <= br.p_hi &&
+                pc > full_lo && pc + BK - 1 <= full_hi)
+              run = 1 + min(min(L - m1 - 2 * BK, br.p_hi - pc - (2 * BK - 1)), full_hi - pc - (BK - 1)) / BK;
+          } else {
+            // inside one frame, unclamped, the next block's rows are this block's
+            // rows 64 positions on
+            const bool step = !SHORTL && m0 + BK <= L && n1 == n0 && m1 + BK <= L && pb + 2 * BK - 1 <= br.p_hi;
+            if (step) {
+#pragma unroll
+              for (int j = 0; j < WinGeom<QF, SHORTL>::NJ; ++j) ld.src[j] += ld.inc[j];
+            } else {
+              win_block_addrs<QF, SHORTL>(ld, a, br, qc.b, qc.h, qc.wave, n1 * L + m1, n1, m1);
+            }
+            win_issue<QF, SHORTL>(ld, nbuf, qc.wave);
+          }
+        }
+        full = size == BK && pb >= full_lo && pb + BK - 1 <= full_hi;
+        // a wave whose rows all lie past the frame's end (the last, partial
+        // query tile), or whose windows all miss this block, only loads its
+        // share of the block and keeps the barriers: a block masked for every
+        // lane adds nothing to O, l or the running maximum
+        touch = pb + size - 1 >= need_lo && pb <= need_hi;
       }
-      const bool full = size == BK && pb >= full_lo && pb + BK - 1 <= full_hi;
-      // a wave whose rows all lie past the frame's end (the last, partial
-      // query tile), or whose windows all miss this block, only loads its
-      // share of the block and keeps the barriers: a block masked for every
-      // lane adds nothing to O, l or the running maximum
-      const bool touch = pb + size - 1 >= need_lo && pb <= need_hi;
+      const float ks1 = ALIGN && more ? *tb1 : 1.f;
       if (qc.active && touch) {
         const bool failed = win_block<QF, ALIGN>(cb, qc, hi, wl, pb, size, ks0, full, spec && pb > full_lo,
                                                  qf, q8f, O, m_run, l_run);
