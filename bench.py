@@ -43,7 +43,11 @@ PEAK_FP4_TFLOPS = 10100.0
 # QK^T at the 4-bit peak, P V at the bf16 peak (equal flops): time-weighted peak
 PEAK_FP4_BLEND_TFLOPS = 2.0 / (1.0 / PEAK_FP4_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 
-# algorithmic work per unit (derivation in the design doc)
+# algorithmic work per unit: the bytes one token of one head must move through
+# HBM at least once (q, k, v read and o written in bf16, alpha and beta in
+# fp32), and the flops of the chunkwise form per token (one chunk-head: the
+# five C x C x d products of the Gram, output and solve operands, the three
+# C x d x d state products, and the C^3 / 3 of the triangular inverse)
 GDN_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 2 + 2 * 4      # q, k, v, o bf16 + alpha, beta fp32
 CHUNK = 64
 
@@ -307,8 +311,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the multi-GPU sharding of the path is "
-              "described in DESIGN.md and not implemented (use --gpus 1).", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU; sharding the path across GPUs is not "
+              "implemented (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
