@@ -76,6 +76,27 @@ def window_pairs(T, L, w, dil, frame_offset=0, centered=False):
     return total
 
 
+def shared_frame_pairs(T, L, w, centered=False):
+    """(query, key) pairs of a query's own frame inside its window: within a
+    frame the SWA and DSWA positions differ by a constant, so both branches
+    hold exactly these pairs, with the same scores when they score the same
+    q and k; they are computed once.  Every pair the two windows share when
+    w <= (dil - 1) L + 1 (causal) or floor(w / 2) < L (centred)."""
+    total = 0
+    for f in range(-(-T // L)):
+        n = min(L, T - f * L)
+        total += window_pairs(n, n, w, 1, 0, centered)
+    return total
+
+
+def hybrid_pairs(T, L, w, dil, centered=False, shared=True):
+    """Distinct (query, key) pairs of the two windowed branches of the hybrid
+    layer (SWA + DSWA, less the own-frame pairs they share when both score the
+    same q and k, i.e. without RoPE)."""
+    pairs = window_pairs(T, L, w, 1, 0, centered) + window_pairs(T, L, w, dil, 0, centered)
+    return pairs - (shared_frame_pairs(T, L, w, centered) if shared and dil > 1 else 0)
+
+
 def read_counter_summary(name):
     """key: value lines of a committed counter summary under profiles/."""
     out = {}
@@ -360,7 +381,7 @@ def main():
     sq = torch.empty((w.B, w.H, nb), dtype=torch.float32, device=dev)
     sk = torch.empty_like(sq)
     o_gdn = torch.empty_like(d["v"])
-    yws = torch.empty(4 * d["v"].numel(), dtype=torch.uint8, device=dev)
+    yws = torch.empty(4 * (d["v"].numel() + d["v"].numel() // w.d), dtype=torch.uint8, device=dev)
     S = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
     t_quant = st.run("fp8_quant_q", lambda: K.kairos_fp8_quantize(d["q"], codes_q, sq), reps)
     st.run("fp8_quant_k", lambda: K.kairos_fp8_quantize(d["k"], codes_k, sk), reps)
@@ -431,10 +452,11 @@ def main():
                  "gdn_prologue_qk_literal": rows * (6 * w.d * 2 + 16)}
     del p_k, p_q, p_v, p_a, p_b, za, zb
 
-    pairs = window_pairs(w.T, w.L, w.window, 1) + window_pairs(w.T, w.L, w.window, w.dilation)
+    # distinct pairs: the own-frame pairs that SWA and DSWA share count once
+    pairs = hybrid_pairs(w.T, w.L, w.window, w.dilation)
+    pairs_branches = window_pairs(w.T, w.L, w.window, 1) + window_pairs(w.T, w.L, w.window, w.dilation)
     win_flops = pairs * 4 * w.d * w.B * w.H          # QK^T 2d + PV 2d per (query, key) pair
-    pairs_c = window_pairs(w.T, w.L, w.window, 1, centered=True) + \
-        window_pairs(w.T, w.L, w.window, 6, centered=True)
+    pairs_c = hybrid_pairs(w.T, w.L, w.window, 6, centered=True)
     win_flops_c = pairs_c * 4 * w.d * w.B * w.H
     if fp8:
         # QK^T at the fp8 peak, PV at the bf16 peak: time-weighted (blended) peak
@@ -506,7 +528,7 @@ def main():
             "bf16_mfma_frac": round(gdn_flops / (t_gdn / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
         "window_stage": {"ms": round(t_win, 4), "alg_TFLOP_per_s": round(achieved, 1),
-                         "pairs_per_bh": pairs},
+                         "pairs_per_bh": pairs, "pairs_per_bh_both_branches": pairs_branches},
         "cold_vs_warm": {"layer_warm_ms": round(t_layer_warm, 4), "layer_cold_ms": round(t_layer_cold, 4),
                          "gdn_branch_warm_ms": round(t_gdn, 4), "gdn_branch_cold_ms": round(t_gdn_cold, 4),
                          "flush": "512 MB fill before each timed launch (Infinity Cache 256 MB)"},
@@ -625,7 +647,7 @@ def workload_breakdown(K, torch, WORKLOADS, make_device_inputs, reps, ctx):
     fn = layer_step_fn(K, d, w2, bufs, False, ctx)
     fn()
     t = st.run("layer_bf16_B1H24F21L1560", fn, reps)
-    pairs = window_pairs(w2.T, w2.L, w2.window, 1) + window_pairs(w2.T, w2.L, w2.window, w2.dilation)
+    pairs = hybrid_pairs(w2.T, w2.L, w2.window, w2.dilation)
     fl = pairs * 4 * w2.d * w2.B * w2.H + w2.B * w2.T * w2.H * gdn_flops_per_token_head(w2.d)
     out["layer_bf16_B1H24F21L1560"] = {"ms": round(t, 4), "tokens_per_s": round(w2.B * w2.T / (t / 1e3)),
                                        "alg_TFLOP_per_s": round(fl / (t / 1e3) / 1e12, 1),

@@ -293,8 +293,8 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
  *   v          bf16 [B][T][H][128];  o_gdn bf16 [B][T][H][128]
  *   gate_logits [3][H] fp32;  k_ring / v_ring as in kairos_hlta_fwd (read only)
  *   out        bf16 [B][T][H][128], y = sig(z_swa) o_swa + sig(z_dswa) o_dswa + sig(z_gdn) o_gdn
- *   workspace  >= 4*B*T*H*128 bytes, 256-byte aligned (fp32 partial result of
- *              the first branch, one row per query)
+ *   workspace  >= 4*B*T*H*129 bytes, 256-byte aligned (fp32 partial results:
+ *              a row of 128 per query, then one log-sum-exp per query)
  * kairos_hlta_fwd = [kairos_fp8_quantize x2] + kairos_gdn_fwd + this call
  * [+ the ring update]; the stages are exposed for timing and composition.
  * Both branches share q and k, so desc->rope_base must be 0 here (with RoPE

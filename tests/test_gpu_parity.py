@@ -295,7 +295,7 @@ def test_hlta_window_stage_wide_scores(qf):
     inp["q_bits"] = to_bf16_bits(inp["q"])
     dv = inputs_to_dev(inp)
     o_gdn = torch.zeros_like(dv["v"])
-    ws = torch.empty(4 * B * T * H * 128, dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(4 * B * T * H * 129, dtype=torch.uint8, device="cuda:0")
     if qf == "bf16":
         y = K.kairos_hlta_window_fwd(dv["q"], dv["k"], dv["v"], o_gdn, dv["gates"], L, w, dil, workspace=ws)
     else:

@@ -124,7 +124,7 @@ def test_window_stage_poisoned_buffers_and_determinism():
     T = F * L
     dv = inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=602))
     o_gdn = dv["v"].flip(1).contiguous()                  # any bf16 tensor of the shape
-    ws = torch.empty(4 * B * T * H * 128, dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(4 * B * T * H * 129, dtype=torch.uint8, device="cuda:0")
     out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda:0")
     res = _runs(lambda: K.kairos_hlta_window_fwd(dv["q"], dv["k"], dv["v"], o_gdn, dv["gates"], L, w, dil,
                                                  out=out, workspace=ws), [ws, out])

@@ -474,7 +474,7 @@ def kairos_hlta_window_fwd(q, k, v, o_gdn, gate_logits, L, window, dilation, fra
     _need(out, "out", torch.bfloat16, (B, T, H, d), dev)
     desc = hlta_desc(B, T, H, d, L, window, dilation, frame_offset, ring_frames, fmt,
                      centered=centered)
-    nws = 4 * B * T * H * d
+    nws = 4 * B * T * H * (d + 1)
     ws = workspace if workspace is not None else _workspace(nws, dev)
     if ws.numel() < nws:
         raise ValueError(f"workspace too small: {ws.numel()} < {nws}")

@@ -162,11 +162,12 @@ int check_hlta_desc(const kairos_hlta_desc* d, bool layer) {
   return KAIROS_OK;
 }
 
-// Layer workspace: GDN chunk data, o_gdn, the parked first branch, and the
-// windowed operands of each branch (E4M3 codes + scales, or with RoPE the
+// Layer workspace: GDN chunk data, o_gdn, the parked partial result of the
+// window kernel (a row per query) and its log-sum-exp (one per query), and
+// the windowed operands of each branch (E4M3 codes + scales, or with RoPE the
 // rotated q, k; the second set only when RoPE gives DSWA its own operands).
 struct HltaWs {
-  size_t gdn, o_gdn, ypart;
+  size_t gdn, o_gdn, ypart, ylse;
   size_t q1, k1, qs1, ks1;   // first-branch operands (codes / rotated bf16), scales (codes)
   size_t q2, k2, qs2, ks2;   // second-branch operands (RoPE with dilation > 1)
   bool has1, has2;
@@ -191,6 +192,8 @@ HltaWs hlta_ws_layout(const kairos_hlta_desc* d) {
   off += align_up(n * 2);
   w.ypart = off;
   off += align_up(n * 4);
+  w.ylse = off;
+  off += align_up(n / d->g.dk * 4);
   w.has1 = fp8 || rope;
   w.has2 = rope && d->dilation > 1;
   for (int set = 0; set < 2; ++set) {
@@ -481,7 +484,8 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
                            size_t workspace_bytes, void* stream) {
   int st = check_hlta_desc(desc, true);
   if (st != KAIROS_OK) return st;
-  const size_t nws = (size_t)desc->g.B * desc->g.T * desc->g.H * desc->g.dk * 4;
+  // the parked partial result (a row per query) and its log-sum-exp (one per query)
+  const size_t nws = (size_t)desc->g.B * desc->g.T * desc->g.H * (desc->g.dk + 1) * 4;
   const int qf = qk_format(desc->window_qk);
   const bool fp8 = qf != 0;
   if (desc->rope_base != 0.f) return KAIROS_ERR_UNSUPPORTED;
@@ -510,6 +514,7 @@ int kairos_hlta_window_fwd(const kairos_hlta_desc* desc, const void* q, const vo
   WinArgs a;
   fill_win_args(a, desc);
   a.ypart = (float*)workspace;
+  a.ylse = (float*)((uint8_t*)workspace + n * 4);
   a.q = q;
   a.k = k;
   a.v = (const uint16_t*)v;
@@ -634,6 +639,7 @@ int kairos_hlta_fwd(const kairos_hlta_desc* desc, const void* q, const void* k, 
   a.o_gdn = ovl ? nullptr : o_gdn;
   a.gates = gate_logits;
   a.ypart = (float*)(wsb + ws.ypart);
+  a.ylse = (float*)(wsb + ws.ylse);
   a.out = (uint16_t*)out;
   const int qf = qk_format(desc->window_qk);
   const bool fp8 = qf != 0;

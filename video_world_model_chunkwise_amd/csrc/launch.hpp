@@ -29,6 +29,7 @@ struct WinArgs {
                             // launch_hlta_combine adds the gated GDN branch
   const float* gates;       // logits [3][H] (hybrid only)
   float* ypart;             // fp32 [B][T][H][128] scratch for the first branch (hybrid only)
+  float* ylse;              // fp32 [B][T][H] scratch: log-sum-exp of a parked partial result (hybrid only)
   uint16_t* out;            // bf16 [B][T][H][128]
   int B, T, H, L, F, QT;    // F frames in the call (last may be partial), QT query tiles per frame
   int w, dil, R, nblk;

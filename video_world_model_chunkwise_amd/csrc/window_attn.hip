@@ -623,13 +623,17 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
   }
   win_wait_vmem();
   lds_barrier();
+  // Windows are cut at the range's last position p_hi: a range may be part of
+  // a branch's key range (the keys of the frames before the query's frame),
+  // and a block of consecutive positions may then reach past it.  For a whole
+  // range p_hi is already the largest window end of the workgroup.
   const int pq = br.pq0 + qc.mq;                         // this lane's query position
-  const int hi = min(pq + br.fwd, br.p_last);            // its window's last key position
-  const int wl = hi - (pq - br.back) + 1;                // and the window's length
+  const int hi = min(min(pq + br.fwd, br.p_last), br.p_hi);   // its window's last key position
+  const int wl = max(hi - (pq - br.back) + 1, 0);        // and the window's length (0: no key)
   const int full_lo = br.pq0 + qc.mw_hi - br.back;       // blocks inside every window of the wave
-  const int full_hi = min(br.pq0 + qc.mw_lo + br.fwd, br.p_last);
+  const int full_hi = min(min(br.pq0 + qc.mw_lo + br.fwd, br.p_last), br.p_hi);
   const int need_lo = br.pq0 + qc.mw_lo - br.back;       // keys inside some window of the wave
-  const int need_hi = min(br.pq0 + qc.mw_hi + br.fwd, br.p_last);
+  const int need_hi = min(min(br.pq0 + qc.mw_hi + br.fwd, br.p_last), br.p_hi);
   // A block is formed against the running maximum alone only if every lane's
   // window began before it (each lane has a key, hence a finite maximum), the
   // wave's previous block did not fail such an attempt, and fewer than
@@ -857,10 +861,90 @@ __global__ __launch_bounds__(256, (win_wgs_per_cu<QF, SHORTL>())) void win_attn_
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
 
+  float fac;
+  if (HYBRID && a.dil > 1 && !a.q2) {
+    // ---- SWA and DSWA with the query's own frame shared.  Inside one frame
+    // the two branches' positions differ by a constant, so a window of either
+    // (causal or centred) holds the same keys of that frame, with the same
+    // scores (both branches score the same q and k): those keys are computed
+    // once.  With the other frames split off (SWA: the neighbouring frames;
+    // DSWA: the neighbouring frames of the residue group), each branch is the
+    // softmax over two disjoint key sets, merged exactly from each set's
+    // result o and log-sum-exp (log2 units) lse = m + log2(l):
+    //   o = (2^{lse1 - M} o1 + 2^{lse2 - M} o2) / (2^{lse1 - M} + 2^{lse2 - M}),
+    //   M = max(lse1, lse2).
+    // Each part is a run of whole key blocks over a range of positions:
+    // before the frame [p_lo, pq0 - 1], the frame [pq0, pq0 + L - 1], after
+    // it (centred windows) [pq0 + L, p_hi].
+    float* lse_row = a.ylse + ((size_t)b * a.T + tq) * a.H + h;
+    float* yp = a.ypart + rowoff;
+    // Each part's range is recomputed (a few scalar operations) rather than
+    // kept live; each part is its own copy of the branch loop, which keeps the
+    // loops free of register spills.
+    auto part = [&](int dil, int which) {
+      BranchRange r = branch_range(a, dil, f, m0, m_last_wg);
+      const int lo = which == 0 ? r.p_lo : which == 1 ? r.pq0 : r.pq0 + a.L;
+      const int hi = which == 0 ? r.pq0 - 1 : which == 1 ? r.pq0 + a.L - 1 : r.p_hi;
+      r.p_lo = max(r.p_lo, lo);
+      r.p_hi = min(r.p_hi, hi);
+      if (r.p_hi < r.p_lo) return;
+      r.nb = (r.p_hi - r.p_lo + BK) / BK;
+      run_branch<QF, SHORTL>(a, B0, B1, r, qc, qf, q8f, ld, O, m_run, l_run);
+    };
+    // (1) SWA keys of the other frames -> normalised o and lse, parked
+    part(1, 0);
+    if (a.centered) part(1, 2);
+    {
+      const float ls = sum_with_partner(l_run);
+      const float rl = ls > 0.f ? 1.f / ls : 0.f;
+      if (q_valid) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<float4*>(yp + 32 * dt + 8 * rq + 4 * g) =
+                make_float4(rl * O[dt][4 * rq], rl * O[dt][4 * rq + 1], rl * O[dt][4 * rq + 2],
+                            rl * O[dt][4 * rq + 3]);
+        if (g == 0) *lse_row = ls > 0.f ? m_run + __log2f(ls) : -1e30f;
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
+    m_run = -1e30f;
+    l_run = 0.f;
+    // (2) the query's own frame, for both branches (never empty: it holds the query)
+    part(1, 1);
+    // (3) sig(z_swa) o_swa, merged from (1) and (2) in place in the parked row;
+    //     (2) stays in registers
+    {
+      const float lc = sum_with_partner(l_run);
+      const float lse_c = m_run + __log2f(lc);
+      if (q_valid) {
+        const float lse_s = *lse_row;
+        const float mx = fmaxf(lse_s, lse_c);
+        const float ws = __builtin_amdgcn_exp2f(lse_s - mx), wc = __builtin_amdgcn_exp2f(lse_c - mx);
+        const float gs = 1.f / ((1.f + __expf(-a.gates[h])) * (ws + wc));
+        const float fs = gs * ws, fc = gs * wc / lc;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            float4* p4 = reinterpret_cast<float4*>(yp + 32 * dt + 8 * rq + 4 * g);
+            const float4 o1 = *p4;
+            *p4 = make_float4(fs * o1.x + fc * O[dt][4 * rq], fs * o1.y + fc * O[dt][4 * rq + 1],
+                              fs * o1.z + fc * O[dt][4 * rq + 2], fs * o1.w + fc * O[dt][4 * rq + 3]);
+          }
+      }
+    }
+    // (4) DSWA keys of the group's other frames, continuing from (2)
+    part(a.dil, 0);
+    if (a.centered) part(a.dil, 2);
+    fac = 1.f / (sum_with_partner(l_run)) / (1.f + __expf(-a.gates[a.H + h]));
+  } else {
   // ---- first branch: SWA (or the single requested branch)
   const BranchRange b0 = branch_range(a, HYBRID ? 1 : a.dil, f, m0, m_last_wg);
   run_branch<QF, SHORTL>(a, B0, B1, b0, qc, qf, q8f, ld, O, m_run, l_run);
-  float fac = 1.f / (sum_with_partner(l_run));
+  fac = 1.f / (sum_with_partner(l_run));
   if (HYBRID) {
     fac *= 1.f / (1.f + __expf(-a.gates[h]));
     // park sig(z_swa) o_swa (fp32) in this query's workspace row
@@ -886,6 +970,7 @@ __global__ __launch_bounds__(256, (win_wgs_per_cu<QF, SHORTL>())) void win_attn_
     }
     run_branch<QF, SHORTL>(a, B0, B1, b1, qc, qf, q8f, ld, O, m_run, l_run);
     fac = 1.f / (sum_with_partner(l_run)) / (1.f + __expf(-a.gates[a.H + h]));
+  }
   }
 
   // ---- epilogue: (+ parked first branch + gated GDN branch) -> bf16 output row
