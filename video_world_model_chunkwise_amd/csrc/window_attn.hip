@@ -760,7 +760,9 @@ __device__ __forceinline__ void run_branch(const WinArgs& a, const WinBuf& B0, c
 template <int QF, bool SHORTL>
 constexpr int win_wgs_per_cu() { return QF != QF_BF16 && !SHORTL ? 3 : 2; }
 
-template <int QF, bool HYBRID, bool SHORTL>
+// SHARE (hybrid only): the two windowed branches score the same q and k and
+// the DSWA dilation exceeds 1, so the query's own frame is computed once.
+template <int QF, bool HYBRID, bool SHORTL, bool SHARE>
 __global__ __launch_bounds__(256, (win_wgs_per_cu<QF, SHORTL>())) void win_attn_kernel(WinArgs a) {
   using G = WinGeom<QF, SHORTL>;
   constexpr bool FP8 = G::FP8;
@@ -862,7 +864,7 @@ __global__ __launch_bounds__(256, (win_wgs_per_cu<QF, SHORTL>())) void win_attn_
   for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
 
   float fac;
-  if (HYBRID && a.dil > 1 && !a.q2) {
+  if constexpr (SHARE) {
     // ---- SWA and DSWA with the query's own frame shared.  Inside one frame
     // the two branches' positions differ by a constant, so a window of either
     // (causal or centred) holds the same keys of that frame, with the same
@@ -1054,14 +1056,20 @@ hipError_t launch_window(const WinArgs& args_in, int qf, bool hybrid, hipStream_
   if (qf < QF_BF16 || qf > QF_FP4) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
   const bool shortl = a.L < BK;
-#define KAIROS_WIN_LAUNCH(QQ, HY, SL) win_attn_kernel<QQ, HY, SL><<<grid, 256, 0, stream>>>(a)
+  // the own frame is shared when both branches score the same q and k
+  const bool share = hybrid && a.dil > 1 && !a.q2;
+#define KAIROS_WIN_LAUNCH(QQ, HY, SL, SH) win_attn_kernel<QQ, HY, SL, SH><<<grid, 256, 0, stream>>>(a)
+#define KAIROS_WIN_SL(QQ, SL)                                                              \
+  if (share) KAIROS_WIN_LAUNCH(QQ, true, SL, true);                                        \
+  else if (hybrid) KAIROS_WIN_LAUNCH(QQ, true, SL, false);                                 \
+  else KAIROS_WIN_LAUNCH(QQ, false, SL, false);
 #define KAIROS_WIN_QF(QQ)                                                                  \
-  if (shortl) { if (hybrid) KAIROS_WIN_LAUNCH(QQ, true, true); else KAIROS_WIN_LAUNCH(QQ, false, true); } \
-  else { if (hybrid) KAIROS_WIN_LAUNCH(QQ, true, false); else KAIROS_WIN_LAUNCH(QQ, false, false); }
+  if (shortl) { KAIROS_WIN_SL(QQ, true) } else { KAIROS_WIN_SL(QQ, false) }
   if (qf == QF_FP4) { KAIROS_WIN_QF(QF_FP4) }
   else if (qf == QF_FP8) { KAIROS_WIN_QF(QF_FP8) }
   else { KAIROS_WIN_QF(QF_BF16) }
 #undef KAIROS_WIN_QF
+#undef KAIROS_WIN_SL
 #undef KAIROS_WIN_LAUNCH
   return hipGetLastError();
 }
