@@ -450,6 +450,34 @@ def test_layer_frame_blocks_partial_and_centred(fmt, L, F, extra, w, dil, center
     _assert_close(host(S), S_ref, "S")
 
 
+@pytest.mark.parametrize("fmt,blocks,L,F,w,dil,fo,centered", [
+    ("bf16", "tokens", 100, 5, 40, 2, 0, False),   # window shorter than a frame
+    ("fp8", "tokens", 150, 6, 30, 4, 1, False),
+    ("fp8", "frames", 128, 4, 50, 3, 0, True),
+    ("fp4", "frames", 96, 5, 20, 2, 2, True),
+    ("fp8", "frames", 100, 4, 1, 2, 0, False),     # each query sees only itself
+])
+def test_hlta_window_shorter_than_frame(fmt, blocks, L, F, w, dil, fo, centered):
+    """Both windowed branches with a window shorter than a frame: deep in a
+    frame neither branch reaches another frame, so only the frame's own keys
+    are scored, and the two branches' key sets within the frame coincide."""
+    B, H = 1, 2
+    T = F * L
+    print(f"short window {fmt}/{blocks} L{L} F{F} w{w} dil{dil} fo{fo} centred={centered}", flush=True)
+    inp = make_custom(B, T, H, 128, "bf16", seed=900 + L + w)
+    dv = inputs_to_dev(inp)
+    wq = {"bf16": K.BF16, "fp8": K.FP8_E4M3, "fp4": K.FP4_E2M1}[fmt]
+    qb = K.QK_BLOCKS_FRAMES if blocks == "frames" else K.QK_BLOCKS_TOKENS
+    y, S = K.kairos_hlta_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dv["gates"], L, w, dil,
+                             frame_offset=fo, window_qk=wq, qk_blocks=qb, centered=centered)
+    torch.cuda.synchronize()
+    y_ref, S_ref = oracle.hlta(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["gates"],
+                               L, w, dil, frame_offset=fo, window_qk=fmt, qk_blocks=blocks,
+                               centered=centered)
+    _assert_close(host(y), y_ref, "y")
+    _assert_close(host(S), S_ref, "S")
+
+
 @pytest.mark.parametrize("fmt,rope", [("fp8", 1e4), ("bf16", 0.0)])
 def test_streaming_with_context_equals_full_run(fmt, rope):
     """A rollout whose frame calls take the overlapped schedule of a context
