@@ -493,11 +493,17 @@ def main():
         v = float(sq["win_attn_kernel.SQ_INSTS_VALU"])
         tr = float(sq["win_attn_kernel.SQ_INSTS_VALU_TRANS_F32"])
         m = float(sq["win_attn_kernel.SQ_VALU_MFMA_BUSY_CYCLES"])
+        # the shader clock the kernel actually ran at (GPU busy cycles over the
+        # dispatch's duration in the counter pass): busy cycles become time at
+        # that clock, and the published peak assumes the 2.4 GHz maximum
+        clk = float(sq.get("win_attn_kernel.shader_clock_hz", CLOCK_HZ))
         roofline["counters"] = {
             "valu_insts_per_launch": v, "trans_insts_per_launch": tr,
             "mfma_insts_per_launch": float(sq["win_attn_kernel.SQ_INSTS_MFMA"]),
-            "valu_issue_ms": round(((v - tr) * VALU_ISSUE_CLK + tr * TRANS_ISSUE_CLK) / SIMDS / CLOCK_HZ * 1e3, 4),
-            "mfma_busy_ms": round(m / SIMDS / CLOCK_HZ * 1e3, 4),
+            "shader_clock_ghz": round(clk / 1e9, 3),
+            "valu_issue_ms": round(((v - tr) * VALU_ISSUE_CLK + tr * TRANS_ISSUE_CLK) / SIMDS / clk * 1e3, 4),
+            "mfma_busy_ms": round(m / SIMDS / clk * 1e3, 4),
+            "frac_of_peak_at_shader_clock": round(roofline["frac"] * CLOCK_HZ / clk, 4),
             "source": "profiles/hlta_fp8_B4H24F16L3600_sq_counters.txt"}
     pro_fresh = cnt.get("gdn_prologue_kernel.source_sha") == src_sha("prologue.hip", "common.hpp",
                                                                     "launch.hpp")
