@@ -49,7 +49,12 @@
 // (three waves per SIMD), bf16 Q/K and shorter frames two, so that one wave's
 // softmax arithmetic overlaps another's matrix products.  To fit, the hybrid
 // kernel parks the finished first branch (gated, normalised, fp32) in a
-// workspace row per query and adds it back in the epilogue.
+// workspace row per query and adds it back in the epilogue.  When both
+// branches score the same q and k (no RoPE) and the dilation exceeds 1, the
+// query's own frame is scored once for both: SWA's other frames are parked
+// with their log-sum-exp, the own frame's softmax state is merged into that
+// row and then carried on over DSWA's other frames (a softmax over disjoint
+// key sets is the log-sum-exp weighted mix of the per-set results).
 #include "common.hpp"
 #include "launch.hpp"
 
