@@ -163,7 +163,7 @@ def cpu_baseline(w, WORKLOADS):
     except Exception:
         blas_threads = 1
     t_all = time.perf_counter()
-    Tg, rows_n, Hs = 2048, 384, 4
+    Tg, rows_n, Hs = 8192, 1536, 4
     c = _oracle_costs(w, Tg, rows_n, Hs, 7)
     per_token = sum(c.values())
     # the same loop on one BLAS thread, over a quarter of the tokens
