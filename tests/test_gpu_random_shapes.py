@@ -7,7 +7,10 @@ frame quantisation blocks; RoPE or none) and whether a context runs part of
 the call on its side stream, and compares y and the final GDN state with the
 CPU oracle.  The rollout cases feed a random sequence through the ring in
 calls of one to three frames and compare with one full-length oracle run.
-Tolerances as in the other parity tests.
+The gated delta rule cases draw fp32 or bf16 inputs, the head dimension,
+ragged lengths (long ones with few heads, where the scan splits over time)
+and an incoming state.  Tolerances as in the other parity tests (fp32
+gated delta rule: 1e-4).
 """
 import numpy as np
 import pytest
@@ -25,11 +28,11 @@ TOL_MAX, TOL_MEAN = 2e-2, 5e-3
 FMT = {"bf16": K.BF16, "fp8": K.FP8_E4M3, "fp4": K.FP4_E2M1}
 
 
-def _assert_close(got, ref, what):
+def _assert_close(got, ref, what, tmax=TOL_MAX, tmean=TOL_MEAN):
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     rmax, rmean = rel_errors(got, ref)
     print(f"{what}: rel_max={rmax:.3e} rel_mean={rmean:.3e}", flush=True)
-    assert rmax <= TOL_MAX and rmean <= TOL_MEAN, f"{what}: rel_max {rmax:.3e} rel_mean {rmean:.3e}"
+    assert rmax <= tmax and rmean <= tmean, f"{what}: rel_max {rmax:.3e} rel_mean {rmean:.3e}"
 
 
 def _layer_cases(n=16, seed=20261203):
@@ -64,8 +67,23 @@ def _stream_cases(n=6, seed=20261204):
     return cases
 
 
+def _gdn_cases(n=10, seed=20261205):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        io = str(rng.choice(["f32", "bf16"]))
+        d = int(rng.choice([32, 64, 128] if io == "f32" else [64, 128]))
+        long_seq = i % 3 == 0                    # few heads, long sequence: the split scan
+        B, H = (1, int(rng.integers(1, 3))) if long_seq else (int(rng.integers(1, 4)), int(rng.integers(1, 6)))
+        T = int(rng.integers(2000, 6001)) if long_seq else int(rng.choice([int(rng.integers(0, 1500)), 64 * int(rng.integers(1, 20))]))
+        cases.append(dict(io=io, d=d, B=B, H=H, T=T, state=bool(rng.random() < 0.5),
+                          alpha=str(rng.choice(["softplus", "uniform"])), seed=int(rng.integers(0, 1 << 30))))
+    return cases
+
+
 LAYER_CASES = _layer_cases()
 STREAM_CASES = _stream_cases()
+GDN_CASES = _gdn_cases()
 
 
 @pytest.mark.parametrize("i", range(len(LAYER_CASES)))
@@ -122,3 +140,23 @@ def test_random_rollout_matches_full_run(i):
                                rope_base=c["rope"] or None)
     _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "rollout y")
     _assert_close(host(state), S_ref, "rollout S")
+
+
+@pytest.mark.parametrize("i", range(len(GDN_CASES)))
+def test_random_gdn_matches_oracle(i):
+    c = GDN_CASES[i]
+    print(f"random gdn {i}: {c}", flush=True)
+    B, T, H, d = c["B"], c["T"], c["H"], c["d"]
+    inp = make_custom(B, T, H, d, c["io"], seed=c["seed"], alpha_kind=c["alpha"])
+    dv = inputs_to_dev(inp, c["io"])
+    s0 = None
+    if c["state"]:
+        s0 = np.random.default_rng(c["seed"] + 1).standard_normal((B, H, d, d)).astype(np.float32) * 0.1
+    out, S = K.kairos_gdn_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"],
+                              state_in=None if s0 is None else torch.from_numpy(s0).to("cuda:0"))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.gdn_recurrent(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], state_in=s0)
+    tol = (1e-4, 1e-4) if c["io"] == "f32" else (TOL_MAX, TOL_MEAN)
+    if T > 0:
+        _assert_close(host(out), o_ref, "o", *tol)
+    _assert_close(host(S), S_ref, "S", *tol)
