@@ -393,3 +393,41 @@ def test_bf16_rounding_is_nearest_even():
     got = bf16_bits_to_f32(to_bf16_bits(x))
     want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(got, want)
+
+
+from hypothesis import given, settings, strategies as st
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(T=st.integers(1, 36), L=st.integers(1, 12), w=st.integers(1, 30), dil=st.integers(1, 4),
+       fo=st.integers(0, 5), centered=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_window_blocked_equals_bruteforce_property(T, L, w, dil, fo, centered, seed):
+    """The blocked window oracle against the scalar key-set definition on
+    arbitrary tiny shapes: partial last frames, windows shorter or longer than
+    a frame, dilations, frame offsets, causal and centred."""
+    rng = np.random.default_rng(seed)
+    q, k, v, _, _ = _rand_inputs(rng, 1, T, 2, 4)
+    np.testing.assert_allclose(windowed_attention(q, k, v, L, w, dil, fo, centered=centered),
+                               window_bruteforce(q, k, v, L, w, dil, fo, centered=centered),
+                               rtol=1e-11, atol=1e-12)
+
+
+@settings(max_examples=40, deadline=None, derandomize=True)
+@given(T=st.integers(0, 100), d=st.sampled_from([2, 4, 8]), C=st.integers(1, 70), split=st.floats(0, 1),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_gdn_chunked_and_state_passing_property(T, d, C, split, seed):
+    """On arbitrary tiny shapes: the chunkwise form with any chunk length
+    equals the token recurrence, and running the sequence in two pieces with
+    the state carried across equals one run."""
+    rng = np.random.default_rng(seed)
+    q, k, v, a, b = _rand_inputs(rng, 1, T, 2, d)
+    S0 = rng.standard_normal((1, 2, d, d))
+    o1, S1 = gdn_recurrent(q, k, v, a, b, S0)
+    o2, S2 = gdn_chunked(q, k, v, a, b, S0, chunk=C)
+    np.testing.assert_allclose(o2, o1, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(S2, S1, rtol=1e-9, atol=1e-11)
+    s = int(round(split * T))
+    oa, Sa = gdn_recurrent(q[:, :s], k[:, :s], v[:, :s], a[:, :s], b[:, :s], S0)
+    ob, Sb = gdn_recurrent(q[:, s:], k[:, s:], v[:, s:], a[:, s:], b[:, s:], Sa)
+    np.testing.assert_allclose(np.concatenate([oa, ob], axis=1), o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Sb, S1, rtol=1e-12, atol=1e-13)
