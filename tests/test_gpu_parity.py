@@ -511,3 +511,36 @@ def test_streaming_with_context_equals_full_run(fmt, rope):
                                rope_base=rope or None)
     _assert_close(np.concatenate([host(y) for y in ys], axis=1), y_ref, "stream y")
     _assert_close(host(state), S_ref, "stream S")
+
+
+@pytest.mark.parametrize("fmt,B,F,extra,L,H,w,dil,centered,use_ctx", [
+    ("fp8", 1, 5, 37, 100, 2, 150, 2, False, False),
+    ("fp8", 2, 4, 0, 128, 3, 200, 3, False, False),
+    ("fp4", 1, 6, 23, 96, 2, 130, 2, True, False),
+    ("fp8", 1, 3, 0, 64, 1, 64, 1, False, False),
+    ("fp8", 1, 8, 0, 1024, 8, 1000, 4, False, True),    # operand pre-passes beside the scan
+    ("fp4", 1, 8, 0, 1024, 8, 1000, 4, False, True),
+])
+def test_layer_equals_its_parts_bitwise(fmt, B, F, extra, L, H, w, dil, centered, use_ctx):
+    """A quantised layer call equals, bit for bit, the chain of its public
+    parts: the gated delta rule, the standalone quantisers of q and k (64-token
+    blocks) and the windowed stage fed with their outputs."""
+    T = F * L + extra
+    print(f"layer vs parts {fmt} B{B} T{T} L{L} H{H} w{w} dil{dil} centred={centered} ctx={use_ctx}", flush=True)
+    dv = inputs_to_dev(make_custom(B, T, H, 128, "bf16", seed=700 + T + H))
+    wq = K.FP8_E4M3 if fmt == "fp8" else K.FP4_E2M1
+    ctx = K.Context() if use_ctx else None
+    y, S = K.kairos_hlta_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"], dv["gates"], L, w, dil,
+                             window_qk=wq, centered=centered, ctx=ctx)
+    o_gdn, S2 = K.kairos_gdn_fwd(dv["q"], dv["k"], dv["v"], dv["alpha"], dv["beta"])
+    quant = K.kairos_fp8_quantize if fmt == "fp8" else K.kairos_fp4_quantize
+    cq, sq = quant(dv["q"])
+    ck, sk = quant(dv["k"])
+    y2 = K.kairos_hlta_window_fwd(cq, ck, dv["v"], o_gdn, dv["gates"], L, w, dil, q_scales=sq, k_scales=sk,
+                                  centered=centered, window_qk=wq)
+    torch.cuda.synchronize()
+    if ctx is not None:
+        ctx.close()
+    assert torch.equal(S, S2), "final state differs from the gated delta rule alone"
+    same = (y.view(torch.int16) == y2.view(torch.int16))
+    assert bool(same.all()), f"{int((~same).sum())} of {same.numel()} outputs differ from the chained parts"
